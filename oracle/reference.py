@@ -1,0 +1,276 @@
+"""fp64 CPU oracle for the Prefilling-dLLM chunk-sparse attention path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in
+``oracle/``.  The product path (``diffusion_long_context_amd``) never imports
+it and shares no code with it; the two meet only through the seeded input
+arrays of the ``synth`` module.
+
+Every function computes the *plain definition* of one step, in float64, with
+no blocking, fusion or reordering beyond what the definition states.  numpy's
+``@`` (matrix product), ``exp``, ``max`` and ``sum`` serve as library
+primitives.  Sources are the technical summary pages of "Prefilling-dLLM:
+Predictive Prefilling for Long-Context Inference in Diffusion Language
+Models" (gist.science, paper 2606.10537); section names refer to that
+summary:
+
+* Methodology, "1. Chunked prefill and KV cache": the prefix is cut into N
+  chunks of C tokens, each gets a BOS token prepended, and each chunk is run
+  with bidirectional attention restricted to itself; the top-K chunks by a
+  given score s are selected.
+* Methodology, "2. Two-level sparsity": only the K selected chunks take part
+  in decode attention, and inside each of them only the B tokens with the
+  largest cumulative bidirectional attention weight from the query tokens are
+  kept.
+* Methodology, "3. Decoding with static KV reuse": the cached chunk KV stays
+  fixed across denoising steps; only the query / response rows' KV is
+  recomputed, and the decode rows attend to both.
+* "Attention kernel optimization": the decode attention may be split along
+  the KV dimension into independent parts that are merged by a log-sum-exp
+  reduction (``lse_merge`` below is that merge, used to pin split
+  invariance).
+
+Readings where the pages are silent (each is listed with its support in the
+design notes):
+  * BOS (row 0 of a chunk slot) is always kept and attended; top-B ranks the
+    C content rows 1..C only, so a selected chunk contributes B + 1 rows.
+  * The scoring window's softmax is normalised over the chunk's own R = C + 1
+    keys only, and a key's score is the plain sum of its softmax weight over
+    all query heads and all window rows.
+  * No mask anywhere (bidirectional); positions are already applied to Q, K.
+  * Query head h reads KV head floor(h / G), G = h_q / h_kv (grouped query
+    attention with G consecutive query heads per KV head).
+  * Selection order: larger score first, ties to the lower index, -0 == +0,
+    NaN after every number; the kept indices are returned in ascending order.
+  * lse is the natural logarithm of the softmax normaliser (with max).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# input decoding
+# --------------------------------------------------------------------------
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Exact float64 value of a float32 array or of bf16 bit patterns (uint16).
+
+    A bfloat16 number is the top half of a float32, so shifting its 16 bits
+    into the high half of a 32-bit word gives the same value as a float32,
+    which widens exactly to float64.
+    """
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if x.dtype in (np.float32, np.float64):
+        return x.astype(np.float64)
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+def kv_head_of(h: int, group: int) -> int:
+    """KV head read by query head h when ``group`` query heads share a KV head."""
+    return h // group
+
+
+def softmax_rows(z: np.ndarray):
+    """Row-wise softmax in two passes: subtract the row max, exponentiate,
+    divide by the row sum.  Returns (p, m, l) with m the row max and l the sum
+    of exp(z - m), so that the row's log-normaliser is m + ln l."""
+    m = np.max(z, axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    l = np.sum(e, axis=-1, keepdims=True)
+    return e / l, m[..., 0], l[..., 0]
+
+
+# --------------------------------------------------------------------------
+# prefill side: chunk-local attention and per-key scoring
+# --------------------------------------------------------------------------
+def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win,
+                        scale, chunks: Optional[Sequence[int]] = None):
+    """Chunk-local bidirectional attention plus per-key cumulative weight.
+
+    Methodology 1 (each chunk, BOS first, attends only to itself) and
+    Methodology 2 (intra-chunk sparsity ranks a chunk's tokens by their
+    cumulative bidirectional attention weight from the query tokens).
+
+    pool_k, pool_v : [n_slots][R][h_kv][d]; chunk c lives in slot chunk_slot[c]
+    q_chunk        : [n_chunks][R][h_q][d]   the chunk's own queries
+    q_win          : [n_win][W][h_q][d]      chunk c is scored by window
+                                             c // chunks_per_win
+    Returns (o_chunk [len(chunks)][R][h_q][d], key_score [len(chunks)][R]),
+    both float64, for ``chunks`` (default: all chunks, in order).
+
+    o_chunk[c, r, h]  = sum_j softmax_j(scale <Qc[c,r,h], K[slot,j,g]>) V[slot,j,g]
+    key_score[c, j]   = sum_h sum_w softmax_j(scale <Qw[w,h], K[slot,j,g]>)
+    with g = kv_head_of(h, G) and j over the chunk's R rows.
+    """
+    n_chunks = q_chunk.shape[0]
+    _, r_rows, h_kv, _ = pool_k.shape
+    h_q = q_chunk.shape[2]
+    group = h_q // h_kv
+    if chunks is None:
+        chunks = range(n_chunks)
+    chunks = list(chunks)
+    d = pool_k.shape[3]
+    o = np.zeros((len(chunks), r_rows, h_q, d))
+    score = np.zeros((len(chunks), r_rows))
+    for n, c in enumerate(chunks):
+        slot = int(chunk_slot[c])
+        kk = as_f64(pool_k[slot])          # [R][h_kv][d]
+        vv = as_f64(pool_v[slot])
+        qc = as_f64(q_chunk[c])            # [R][h_q][d]
+        qw = as_f64(q_win[c // chunks_per_win])   # [W][h_q][d]
+        for h in range(h_q):
+            g = kv_head_of(h, group)
+            k_g, v_g = kk[:, g, :], vv[:, g, :]
+            p, _, _ = softmax_rows(scale * (qc[:, h, :] @ k_g.T))      # [R][R]
+            o[n, :, h, :] = p @ v_g
+            pw, _, _ = softmax_rows(scale * (qw[:, h, :] @ k_g.T))     # [W][R]
+            score[n] += pw.sum(axis=0)
+    return o, score
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+def _rank_key(value: float, index: int):
+    """Sort key of the selection order: larger first, NaN last, then index."""
+    if math.isnan(value):
+        return (1, 0.0, index)
+    return (0, -value, index)
+
+
+def _top(values: np.ndarray, candidates: Sequence[int], count: int) -> List[int]:
+    order = sorted(candidates, key=lambda j: _rank_key(float(values[j]), j))
+    return sorted(order[:count])
+
+
+def select_topb(key_score: np.ndarray, b: int) -> np.ndarray:
+    """Top-B content rows of every chunk (Methodology 2, intra-chunk sparsity).
+
+    key_score : [n_chunks][R] (float32 as the GPU holds it, or float64)
+    Returns keep_rows [n_chunks][b] int32: the b best rows among 1..R-1 (row 0
+    is the BOS anchor, always kept and not a candidate), ascending.
+    """
+    n_chunks, r_rows = key_score.shape
+    out = np.empty((n_chunks, b), dtype=np.int32)
+    for c in range(n_chunks):
+        out[c] = _top(key_score[c], range(1, r_rows), b)
+    return out
+
+
+def select_topk(chunk_score: np.ndarray, k_per_seq: Sequence[int], k_max: int) -> np.ndarray:
+    """Top-K chunks of every sequence by the given score s (Methodology 1,
+    selection; Methodology 2, inter-chunk sparsity).
+
+    chunk_score : [n_seq][N];  k_per_seq[s] = K_s <= k_max
+    Returns sel_chunk [n_seq][k_max] int32: the K_s best chunk ids in
+    ascending order, then -1 padding.
+    """
+    n_seq, n = chunk_score.shape
+    out = np.full((n_seq, k_max), -1, dtype=np.int32)
+    for s in range(n_seq):
+        ks = int(k_per_seq[s])
+        out[s, :ks] = _top(chunk_score[s], range(n), ks)
+    return out
+
+
+# --------------------------------------------------------------------------
+# decode: attention over the kept chunk rows plus the response rows
+# --------------------------------------------------------------------------
+def attended_pool_rows(chunk_slot, sel_chunk, keep_rows, k_s: int, seq: int,
+                       n_chunks_per_seq: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(slot, row) of every cached row sequence ``seq`` attends to, in chunk
+    order: for each selected chunk, BOS row 0 then its kept rows."""
+    slots, rows = [], []
+    for k in range(k_s):
+        c = seq * n_chunks_per_seq + int(sel_chunk[seq][k])
+        slot = int(chunk_slot[c])
+        for r in [0] + [int(x) for x in keep_rows[c]]:
+            slots.append(slot)
+            rows.append(r)
+    return np.asarray(slots, dtype=np.int64), np.asarray(rows, dtype=np.int64)
+
+
+def attended_kv(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_s, seq,
+                n_chunks_per_seq, k_resp, v_resp):
+    """Dense [N_kv][h_kv][d] float64 keys and values attended by ``seq``:
+    the kept pool rows (static cache, Methodology 3) followed by the L_d
+    recomputed response rows."""
+    slots, rows = attended_pool_rows(chunk_slot, sel_chunk, keep_rows, k_s, seq,
+                                     n_chunks_per_seq)
+    kp = as_f64(pool_k[slots, rows]) if len(slots) else np.zeros((0,) + pool_k.shape[2:])
+    vp = as_f64(pool_v[slots, rows]) if len(slots) else np.zeros((0,) + pool_v.shape[2:])
+    kk = np.concatenate([kp, as_f64(k_resp[seq])], axis=0)
+    vv = np.concatenate([vp, as_f64(v_resp[seq])], axis=0)
+    return kk, vv
+
+
+def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq,
+                      q, k_resp, v_resp, scale, heads: Optional[Sequence[int]] = None):
+    """Decode-step attention of the L_d window rows (Methodology 2 and 3).
+
+    For sequence s, token i and query head h, the attended set A_s is every
+    selected chunk's BOS row and kept rows plus the L_d response rows; the
+    output is the softmax-weighted mean of their values:
+        z_a = scale <q[s,i,h], k_a[g]>,  o = sum_a softmax(z)_a v_a[g],
+        lse = ln sum_a exp(z_a).
+    Returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d]) float64; heads not
+    in ``heads`` (default: all) are left as NaN.
+    """
+    n_seq, l_d, h_q, d = q.shape
+    h_kv = k_resp.shape[2]
+    group = h_q // h_kv
+    n_per_seq = len(chunk_slot) // n_seq
+    heads = range(h_q) if heads is None else heads
+    o = np.full((n_seq, l_d, h_q, d), np.nan)
+    lse = np.full((n_seq, h_q, l_d), np.nan)
+    for s in range(n_seq):
+        kk, vv = attended_kv(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows,
+                             int(k_per_seq[s]), s, n_per_seq, k_resp, v_resp)
+        qs = as_f64(q[s])
+        for h in heads:
+            g = kv_head_of(h, group)
+            p, m, l = softmax_rows(scale * (qs[:, h, :] @ kk[:, g, :].T))
+            o[s, :, h, :] = p @ vv[:, g, :]
+            lse[s, h, :] = m + np.log(l)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# split-KV with log-sum-exp merge (used to pin split invariance)
+# --------------------------------------------------------------------------
+def lse_merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge per-part attention results ("Attention kernel optimization").
+
+    o_parts [S][..., d] are per-part normalised outputs and lse_parts [S][...]
+    their log-normalisers (an empty part has lse = -inf and any o).  With
+    M = max_s lse_s:  lse = M + ln sum_s exp(lse_s - M),
+    o = sum_s exp(lse_s - lse) o_s.
+    """
+    m = np.max(lse_parts, axis=0)
+    w = np.exp(lse_parts - m[None])                    # -inf parts weigh 0
+    total = np.sum(w, axis=0)
+    lse = m + np.log(total)
+    wn = w / total[None]
+    o = np.sum(np.where(wn[..., None] > 0, wn[..., None] * o_parts, 0.0), axis=0)
+    return o, lse
+
+
+def attention_over_parts(q_rows: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                         scale: float, parts: Sequence[np.ndarray]):
+    """Attention of q_rows [M][d] over k_rows/v_rows [N][d] computed on each
+    part (an index array into the N rows) separately, then LSE-merged."""
+    m_rows, d = q_rows.shape
+    o_parts = np.zeros((len(parts), m_rows, d))
+    lse_parts = np.full((len(parts), m_rows), -np.inf)
+    for i, idx in enumerate(parts):
+        if len(idx) == 0:
+            continue
+        p, m, l = softmax_rows(scale * (q_rows @ k_rows[idx].T))
+        o_parts[i] = p @ v_rows[idx]
+        lse_parts[i] = m + np.log(l)
+    return lse_merge(o_parts, lse_parts)
