@@ -1,0 +1,241 @@
+"""ctypes binding of libpdllm (include/pdllm.h) for torch tensors.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch provides device memory (outputs and workspaces are allocated
+with ``torch.empty``) and the stream (the current HIP stream).  If the
+library has not been built, importing this module raises ``ImportError``:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpdllm.so")
+
+F32, BF16 = 0, 1
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("stride_slot", ctypes.c_int64), ("stride_row", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64), ("n_slots", ctypes.c_int32),
+                ("slot_rows", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class PageTable(ctypes.Structure):
+    _fields_ = [("chunk_slot", ctypes.c_void_p), ("sel_chunk", ctypes.c_void_p),
+                ("keep_rows", ctypes.c_void_p), ("k_per_seq", ctypes.c_void_p),
+                ("n_chunks_per_seq", ctypes.c_int32), ("k_max", ctypes.c_int32),
+                ("b", ctypes.c_int32)]
+
+
+EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_select_topB",
+           "pdllm_select_topK", "pdllm_decode_plan", "pdllm_split_attn_decode_workspace",
+           "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m diffusion_long_context_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    P = ctypes.POINTER
+    lib.pdllm_abi_version.restype = ctypes.c_int
+    lib.pdllm_last_error.restype = ctypes.c_char_p
+    lib.pdllm_prefill_score_workspace.restype = sz
+    lib.pdllm_prefill_score_workspace.argtypes = [i32, i32, i32]
+    lib.pdllm_chunk_prefill_score.restype = ctypes.c_int
+    lib.pdllm_chunk_prefill_score.argtypes = [P(Pool), vp, i32, vp, i32, vp, i32, i32, f32, vp, vp,
+                                              vp, sz, vp]
+    lib.pdllm_select_topB.restype = ctypes.c_int
+    lib.pdllm_select_topB.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.pdllm_select_topK.restype = ctypes.c_int
+    lib.pdllm_select_topK.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    lib.pdllm_decode_plan.restype = ctypes.c_int
+    lib.pdllm_decode_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+                                      P(i64)]
+    lib.pdllm_split_attn_decode_workspace.restype = sz
+    lib.pdllm_split_attn_decode_workspace.argtypes = [P(Pool), P(PageTable), i32, i32, i32, i32]
+    lib.pdllm_split_attn_decode.restype = ctypes.c_int
+    lib.pdllm_split_attn_decode.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32,
+                                            i32, vp, vp, vp, sz, vp]
+    return lib
+
+
+lib = _load()
+ABI_VERSION = 1
+if lib.pdllm_abi_version() != ABI_VERSION:
+    raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
+
+
+class PdllmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib.pdllm_last_error().decode(errors="replace")
+        super().__init__(f"{what} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise PdllmError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dense(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_pool(pool_k: torch.Tensor, pool_v: torch.Tensor) -> Pool:
+    """Describe [n_slots][slot_rows][h_kv][d] K/V tensors (any strides with d
+    contiguous; K and V must share strides)."""
+    if pool_k.shape != pool_v.shape or pool_k.stride() != pool_v.stride():
+        raise ValueError("pool k and v must have the same shape and strides")
+    if pool_k.dtype not in _DTYPE or pool_v.dtype != pool_k.dtype:
+        raise ValueError("pool dtype must be float32 or bfloat16 (both the same)")
+    if pool_k.dim() != 4 or pool_k.stride(3) != 1:
+        raise ValueError("pool tensors must be 4-D with the head dim contiguous")
+    n_slots, rows, h_kv, d = pool_k.shape
+    return Pool(pool_k.data_ptr(), pool_v.data_ptr(), pool_k.stride(0), pool_k.stride(1),
+                pool_k.stride(2), n_slots, rows, h_kv, d, _DTYPE[pool_k.dtype])
+
+
+def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win, scale,
+                        o_chunk=None, key_score=None, workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """pdllm_chunk_prefill_score.  q_chunk [n_chunks][R][h_q][d], q_win
+    [n_win][W][h_q][d]; returns (o_chunk, key_score [n_chunks][R] float32)."""
+    pool = make_pool(pool_k, pool_v)
+    _dense(chunk_slot, "chunk_slot", torch.int32)
+    _dense(q_chunk, "q_chunk", pool_k.dtype)
+    _dense(q_win, "q_win", pool_k.dtype)
+    n_chunks, rows, h_q, d = q_chunk.shape
+    if rows != pool.slot_rows or d != pool.d or q_win.shape[2:] != (h_q, d):
+        raise ValueError("q_chunk / q_win shapes do not match the pool")
+    w = q_win.shape[1]
+    if chunks_per_win < 1 or q_win.shape[0] * chunks_per_win < n_chunks:
+        raise ValueError("q_win must hold ceil(n_chunks / chunks_per_win) windows")
+    if chunk_slot.numel() < n_chunks:
+        raise ValueError("chunk_slot must hold n_chunks entries")
+    dev = q_chunk.device
+    if o_chunk is None:
+        o_chunk = torch.empty_like(q_chunk)
+    if key_score is None:
+        key_score = torch.empty((n_chunks, rows), dtype=torch.float32, device=dev)
+    need = lib.pdllm_prefill_score_workspace(n_chunks, pool.h_kv, rows)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib.pdllm_chunk_prefill_score(ctypes.byref(pool), chunk_slot.data_ptr(), n_chunks,
+                                         q_chunk.data_ptr(), h_q, q_win.data_ptr(), w, chunks_per_win,
+                                         float(scale), o_chunk.data_ptr(), key_score.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), _stream(dev)),
+           "pdllm_chunk_prefill_score")
+    return o_chunk, key_score
+
+
+def select_topb(key_score: torch.Tensor, b: int, keep_rows=None) -> torch.Tensor:
+    """pdllm_select_topB: key_score [n_chunks][R] float32 -> [n_chunks][b] int32."""
+    _dense(key_score, "key_score", torch.float32)
+    n_chunks, rows = key_score.shape
+    if keep_rows is None:
+        keep_rows = torch.empty((n_chunks, b), dtype=torch.int32, device=key_score.device)
+    _check(lib.pdllm_select_topB(key_score.data_ptr(), n_chunks, rows, b, keep_rows.data_ptr(),
+                                 _stream(key_score.device)), "pdllm_select_topB")
+    return keep_rows
+
+
+def select_topk(chunk_score: torch.Tensor, k_per_seq: Sequence[int], k_max: int,
+                sel_chunk=None) -> torch.Tensor:
+    """pdllm_select_topK: chunk_score [n_seq][N] float32 -> [n_seq][k_max] int32."""
+    _dense(chunk_score, "chunk_score", torch.float32)
+    n_seq, n = chunk_score.shape
+    ks = (ctypes.c_int32 * max(n_seq, 1))(*[int(x) for x in k_per_seq])
+    if sel_chunk is None:
+        sel_chunk = torch.empty((n_seq, k_max), dtype=torch.int32, device=chunk_score.device)
+    _check(lib.pdllm_select_topK(chunk_score.data_ptr(), n_seq, n, ks, k_max, sel_chunk.data_ptr(),
+                                 _stream(chunk_score.device)), "pdllm_select_topK")
+    return sel_chunk
+
+
+def decode_plan(k_per_seq, b, l_d, h_q, h_kv, d, dtype, num_splits=0, n_cu=256):
+    """pdllm_decode_plan (host only): returns (splits, tiles_per_split, workspace_bytes)."""
+    n_seq = len(k_per_seq)
+    ks = (ctypes.c_int32 * n_seq)(*[int(x) for x in k_per_seq])
+    splits = (ctypes.c_int32 * n_seq)()
+    tps = (ctypes.c_int32 * n_seq)()
+    ws = ctypes.c_int64(0)
+    _check(lib.pdllm_decode_plan(ks, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, n_cu, splits,
+                                 tps, ctypes.byref(ws)), "pdllm_decode_plan")
+    return list(splits), list(tps), ws.value
+
+
+class Decode:
+    """A prepared pdllm_split_attn_decode call: the structs, host K_s array,
+    outputs and workspace are built once so repeated calls (timing loops,
+    denoising steps) only cross the boundary."""
+
+    def __init__(self, pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
+                 v_resp, scale, num_splits=0, want_lse=True, out=None):
+        self.pool = make_pool(pool_k, pool_v)
+        for t, name in ((chunk_slot, "chunk_slot"), (sel_chunk, "sel_chunk"), (keep_rows, "keep_rows")):
+            _dense(t, name, torch.int32)
+        _dense(q, "q", pool_k.dtype)
+        _dense(k_resp, "k_resp", pool_k.dtype)
+        _dense(v_resp, "v_resp", pool_k.dtype)
+        n_seq, l_d, h_q, d = q.shape
+        if d != self.pool.d or k_resp.shape != (n_seq, l_d, self.pool.h_kv, d) or v_resp.shape != k_resp.shape:
+            raise ValueError("q / k_resp / v_resp shapes do not match the pool")
+        if sel_chunk.dim() != 2 or sel_chunk.shape[0] != n_seq:
+            raise ValueError("sel_chunk must be [n_seq][k_max]")
+        if keep_rows.dim() != 2 or chunk_slot.numel() % n_seq or keep_rows.shape[0] != chunk_slot.numel():
+            raise ValueError("keep_rows must be [n_seq * N][b] and chunk_slot [n_seq * N]")
+        self._keep = (chunk_slot, sel_chunk, keep_rows, q, k_resp, v_resp, pool_k, pool_v)
+        self.ks = (ctypes.c_int32 * n_seq)(*[int(x) for x in k_per_seq])
+        self.pt = PageTable(chunk_slot.data_ptr(), sel_chunk.data_ptr(), keep_rows.data_ptr(),
+                            ctypes.cast(self.ks, ctypes.c_void_p), chunk_slot.numel() // n_seq,
+                            sel_chunk.shape[1], keep_rows.shape[1])
+        self.n_seq, self.l_d, self.h_q = n_seq, l_d, h_q
+        self.scale = float(scale)
+        self.num_splits = int(num_splits)
+        dev = q.device
+        self.device = dev
+        self.o = out if out is not None else torch.empty_like(q)
+        self.lse = torch.empty((n_seq, h_q, l_d), dtype=torch.float32, device=dev) if want_lse else None
+        need = lib.pdllm_split_attn_decode_workspace(ctypes.byref(self.pool), ctypes.byref(self.pt),
+                                                     n_seq, l_d, h_q, self.num_splits)
+        self.workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream: Optional[int] = None):
+        st = lib.pdllm_split_attn_decode(
+            ctypes.byref(self.pool), ctypes.byref(self.pt), self._keep[3].data_ptr(),
+            self._keep[4].data_ptr(), self._keep[5].data_ptr(), self.n_seq, self.l_d, self.h_q,
+            self.scale, self.num_splits, self.o.data_ptr(), _ptr(self.lse), self.workspace.data_ptr(),
+            self.workspace.numel(), _stream(self.device) if stream is None else stream)
+        _check(st, "pdllm_split_attn_decode")
+        return self.o, self.lse
+
+
+def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
+                      v_resp, scale, num_splits=0, want_lse=True):
+    """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None)."""
+    return Decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp, v_resp,
+                  scale, num_splits, want_lse)()

@@ -1,0 +1,60 @@
+// Device-side helpers of the gfx950 kernels: vector types, MFMA wrappers,
+// bf16 conversion, wave reductions and the XCD-aware workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pdllm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16) on one wavefront.
+// Lane l supplies A row (l % 16) and B column (l % 16), each with the eight
+// k values of lane group l / 16; it receives D column (l % 16), rows
+// 4 (l / 16) .. 4 (l / 16) + 3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// float -> bf16 bits, round to nearest even (quiet NaN kept a NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+// Workgroup ids are dispatched round-robin over the 8 XCDs (id % 8).  Remap
+// them so that each XCD receives one contiguous range of logical work items;
+// neighbouring items share K/V tiles, which then stay in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd, rem = n % kXcd;
+  const int x = bid % kXcd, k = bid / kXcd;
+  return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+}  // namespace pdllm

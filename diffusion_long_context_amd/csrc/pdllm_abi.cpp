@@ -1,0 +1,372 @@
+// C ABI of libpdllm (declared in include/pdllm.h): argument validation on the
+// host, split planning, and kernel launches on the caller's stream.  Nothing
+// here allocates device memory or synchronises with the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/pdllm.h"
+#include "pdllm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pdllm_status fail(pdllm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pdllm_status ok() {
+  g_last_error.clear();
+  return PDLLM_OK;
+}
+
+pdllm_status hip_status(int err, const char* what) {
+  if (err == (int)hipSuccess) return PDLLM_OK;
+  return fail(PDLLM_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == PDLLM_BF16 ? 2 : 4; }
+
+bool d_supported(int dtype, int d) {
+  if (dtype == PDLLM_BF16) return d == 64 || d == 128;
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+pdllm_status check_pool(const pdllm_pool* pool) {
+  if (pool == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "pool is NULL");
+  if (pool->k == nullptr || pool->v == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "pool k/v is NULL");
+  if (pool->dtype != PDLLM_F32 && pool->dtype != PDLLM_BF16)
+    return fail(PDLLM_ERR_INVALID_ARG, "pool dtype %d is not PDLLM_F32 or PDLLM_BF16", pool->dtype);
+  if (pool->n_slots < 1 || pool->slot_rows < 1 || pool->h_kv < 1 || pool->d < 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "pool sizes must be >= 1 (n_slots %d, slot_rows %d, h_kv %d, d %d)",
+                pool->n_slots, pool->slot_rows, pool->h_kv, pool->d);
+  if (!d_supported(pool->dtype, pool->d))
+    return fail(PDLLM_ERR_UNSUPPORTED, "head dim %d is not supported for %s", pool->d,
+                pool->dtype == PDLLM_BF16 ? "bf16 (64, 128)" : "f32 (16, 32, 64, 128)");
+  const int64_t vec = pool->dtype == PDLLM_BF16 ? 8 : 4;
+  if (pool->stride_head < pool->d || pool->stride_row < (int64_t)pool->h_kv * pool->d ||
+      pool->stride_slot < (int64_t)pool->slot_rows * pool->stride_row)
+    return fail(PDLLM_ERR_INVALID_ARG, "pool strides overlap (slot %lld, row %lld, head %lld)",
+                (long long)pool->stride_slot, (long long)pool->stride_row, (long long)pool->stride_head);
+  if (pool->stride_head % vec || pool->stride_row % vec || pool->stride_slot % vec)
+    return fail(PDLLM_ERR_INVALID_ARG, "pool strides must be multiples of %lld elements", (long long)vec);
+  if (!aligned16(pool->k) || !aligned16(pool->v))
+    return fail(PDLLM_ERR_INVALID_ARG, "pool k/v must be 16-byte aligned");
+  return PDLLM_OK;
+}
+
+pdllm_status check_tensor(const void* p, const char* name) {
+  if (p == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(PDLLM_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return PDLLM_OK;
+}
+
+pdllm::DecodeArgs base_decode_args(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                   const void* q, const void* k_resp, const void* v_resp,
+                                   int l_d, int h_q, float scale, void* o, float* lse) {
+  pdllm::DecodeArgs a{};
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.ps_slot = pool->stride_slot;
+  a.ps_row = pool->stride_row;
+  a.ps_head = pool->stride_head;
+  a.chunk_slot = pt->chunk_slot;
+  a.sel_chunk = pt->sel_chunk;
+  a.keep_rows = pt->keep_rows;
+  a.q = q;
+  a.k_resp = k_resp;
+  a.v_resp = v_resp;
+  a.o = o;
+  a.lse = lse;
+  a.n_chunks_per_seq = pt->n_chunks_per_seq;
+  a.k_max = pt->k_max;
+  a.b = pt->b;
+  a.l_d = l_d;
+  a.h_q = h_q;
+  a.h_kv = pool->h_kv;
+  a.group = h_q / pool->h_kv;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq,
+                          int32_t l_d, int32_t h_q, int32_t num_splits) {
+  pdllm_status st = check_pool(pool);
+  if (st != PDLLM_OK) return st;
+  if (pt == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "page table is NULL");
+  if (n_seq < 1 || l_d < 1 || h_q < 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "n_seq, l_d and h_q must be >= 1 (got %d, %d, %d)", n_seq, l_d, h_q);
+  if (h_q % pool->h_kv != 0)
+    return fail(PDLLM_ERR_INVALID_ARG, "h_q %d is not a multiple of h_kv %d", h_q, pool->h_kv);
+  if (num_splits < 0) return fail(PDLLM_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (pt->n_chunks_per_seq < 1) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks_per_seq must be >= 1");
+  if (pt->k_max < 0 || pt->k_max > pt->n_chunks_per_seq)
+    return fail(PDLLM_ERR_INVALID_ARG, "k_max %d outside [0, n_chunks_per_seq %d]", pt->k_max,
+                pt->n_chunks_per_seq);
+  if (pt->b < 0 || pt->b > pool->slot_rows - 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "b %d outside [0, slot_rows - 1 = %d]", pt->b, pool->slot_rows - 1);
+  if (pt->k_per_seq == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq (host) is NULL");
+  bool any_chunk = false;
+  for (int s = 0; s < n_seq; ++s) {
+    const int ks = pt->k_per_seq[s];
+    if (ks < 0 || ks > pt->k_max)
+      return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq[%d] = %d outside [0, k_max %d]", s, ks, pt->k_max);
+    any_chunk |= ks > 0;
+  }
+  if (any_chunk) {
+    if (pt->chunk_slot == nullptr || pt->sel_chunk == nullptr)
+      return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot / sel_chunk is NULL");
+    if (pt->b > 0 && pt->keep_rows == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
+  }
+  return PDLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pdllm_abi_version(void) { return PDLLM_ABI_VERSION; }
+
+const char* pdllm_last_error(void) { return g_last_error.c_str(); }
+
+size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slot_rows) {
+  if (n_chunks < 0 || h_kv < 1 || slot_rows < 1) return 0;
+  const int64_t bytes = (int64_t)n_chunks * h_kv * slot_rows * 4;
+  return (size_t)((bytes + 255) / 256 * 256);
+}
+
+pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* chunk_slot,
+                                       int32_t n_chunks, const void* q_chunk, int32_t h_q,
+                                       const void* q_win, int32_t w, int32_t chunks_per_win,
+                                       float scale, void* o_chunk, float* key_score,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  pdllm_status st = check_pool(pool);
+  if (st != PDLLM_OK) return st;
+  if (n_chunks < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 0");
+  if (h_q < 1 || h_q % pool->h_kv != 0)
+    return fail(PDLLM_ERR_INVALID_ARG, "h_q %d must be a positive multiple of h_kv %d", h_q, pool->h_kv);
+  if (w < 1 || chunks_per_win < 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "w and chunks_per_win must be >= 1 (got %d, %d)", w, chunks_per_win);
+  if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
+  const int max_rows = pool->dtype == PDLLM_BF16 ? 257 : 4097;
+  if (pool->slot_rows > max_rows)
+    return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > %d is not supported for this dtype",
+                pool->slot_rows, max_rows);
+  if (n_chunks == 0) return ok();
+  if (chunk_slot == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot is NULL");
+  if ((st = check_tensor(q_chunk, "q_chunk")) != PDLLM_OK) return st;
+  if ((st = check_tensor(q_win, "q_win")) != PDLLM_OK) return st;
+  if ((st = check_tensor(o_chunk, "o_chunk")) != PDLLM_OK) return st;
+  if ((st = check_tensor(key_score, "key_score")) != PDLLM_OK) return st;
+  const size_t need = pdllm_prefill_score_workspace(n_chunks, pool->h_kv, pool->slot_rows);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(PDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  pdllm::PrefillArgs a{};
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.ps_slot = pool->stride_slot;
+  a.ps_row = pool->stride_row;
+  a.ps_head = pool->stride_head;
+  a.chunk_slot = chunk_slot;
+  a.q_chunk = q_chunk;
+  a.q_win = q_win;
+  a.o_chunk = o_chunk;
+  a.key_score = key_score;
+  a.part_score = static_cast<float*>(workspace);
+  a.n_chunks = n_chunks;
+  a.slot_rows = pool->slot_rows;
+  a.h_q = h_q;
+  a.h_kv = pool->h_kv;
+  a.group = h_q / pool->h_kv;
+  a.w = w;
+  a.chunks_per_win = chunks_per_win;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int err = pool->dtype == PDLLM_BF16 ? pdllm::launch_prefill_bf16(a, pool->d, stream)
+                                             : pdllm::launch_prefill_f32(a, pool->d, stream);
+  if ((st = hip_status(err, "chunk prefill launch")) != PDLLM_OK) return st;
+  if ((st = hip_status(pdllm::launch_score_finalize(a, stream), "score finalize launch")) != PDLLM_OK)
+    return st;
+  return ok();
+}
+
+pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t slot_rows,
+                               int32_t b, int32_t* keep_rows, void* stream) {
+  if (n_chunks < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 0");
+  if (slot_rows < 1) return fail(PDLLM_ERR_INVALID_ARG, "slot_rows must be >= 1");
+  if (slot_rows > 4097) return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > 4097 is not supported", slot_rows);
+  if (b < 0 || b > slot_rows - 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "b %d outside [0, slot_rows - 1 = %d]", b, slot_rows - 1);
+  if (n_chunks == 0 || b == 0) return ok();
+  if (key_score == nullptr || keep_rows == nullptr)
+    return fail(PDLLM_ERR_INVALID_ARG, "key_score / keep_rows is NULL");
+  pdllm_status st = hip_status(pdllm::launch_select_topb(key_score, n_chunks, slot_rows, b, keep_rows, stream),
+                               "top-B launch");
+  return st != PDLLM_OK ? st : ok();
+}
+
+pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t n_chunks,
+                               const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
+                               void* stream) {
+  if (n_seq < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_seq must be >= 0");
+  if (n_chunks < 1) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 1");
+  if (n_chunks > 8192) return fail(PDLLM_ERR_UNSUPPORTED, "n_chunks %d > 8192 is not supported", n_chunks);
+  if (k_max < 0 || k_max > n_chunks)
+    return fail(PDLLM_ERR_INVALID_ARG, "k_max %d outside [0, n_chunks %d]", k_max, n_chunks);
+  if (n_seq == 0 || k_max == 0) return ok();
+  if (k_per_seq == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq (host) is NULL");
+  for (int s = 0; s < n_seq; ++s)
+    if (k_per_seq[s] < 0 || k_per_seq[s] > k_max)
+      return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq[%d] = %d outside [0, k_max %d]", s, k_per_seq[s], k_max);
+  if (chunk_score == nullptr || sel_chunk == nullptr)
+    return fail(PDLLM_ERR_INVALID_ARG, "chunk_score / sel_chunk is NULL");
+  for (int s0 = 0; s0 < n_seq; s0 += pdllm::kMaxTopkSeqPerLaunch) {
+    pdllm::TopkArgs a{};
+    a.chunk_score = chunk_score;
+    a.sel_chunk = sel_chunk;
+    a.n_chunks = n_chunks;
+    a.k_max = k_max;
+    a.seq0 = s0;
+    a.n_seq_launch = std::min(pdllm::kMaxTopkSeqPerLaunch, n_seq - s0);
+    for (int i = 0; i < a.n_seq_launch; ++i) a.k[i] = k_per_seq[s0 + i];
+    pdllm_status st = hip_status(pdllm::launch_select_topk(a, stream), "top-K launch");
+    if (st != PDLLM_OK) return st;
+  }
+  return ok();
+}
+
+pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t b, int32_t l_d,
+                               int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
+                               int32_t num_splits, int32_t n_cu, int32_t* splits_per_seq,
+                               int32_t* tiles_per_split, int64_t* workspace_bytes) {
+  if (dtype != PDLLM_F32 && dtype != PDLLM_BF16) return fail(PDLLM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  pdllm::DecodePlan plan;
+  const char* err = "";
+  if (!pdllm::plan_decode(k_per_seq, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, n_cu, &plan, &err))
+    return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
+  for (int s = 0; s < n_seq; ++s) {
+    if (splits_per_seq) splits_per_seq[s] = plan.splits[s];
+    if (tiles_per_split) tiles_per_split[s] = plan.tiles_per_split[s];
+  }
+  if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+  return ok();
+}
+
+size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                         int32_t n_seq, int32_t l_d, int32_t h_q,
+                                         int32_t num_splits) {
+  if (check_decode(pool, pt, n_seq, l_d, h_q, num_splits) != PDLLM_OK) return 0;
+  pdllm::DecodePlan plan;
+  const char* err = "";
+  if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
+                          num_splits, device_cu_count(), &plan, &err))
+    return 0;
+  return (size_t)plan.workspace_bytes;
+}
+
+pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                     const void* q, const void* k_resp, const void* v_resp,
+                                     int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                     int32_t num_splits, void* o, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  pdllm_status st = check_decode(pool, pt, n_seq, l_d, h_q, num_splits);
+  if (st != PDLLM_OK) return st;
+  if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
+  if ((st = check_tensor(q, "q")) != PDLLM_OK) return st;
+  if ((st = check_tensor(k_resp, "k_resp")) != PDLLM_OK) return st;
+  if ((st = check_tensor(v_resp, "v_resp")) != PDLLM_OK) return st;
+  if ((st = check_tensor(o, "o")) != PDLLM_OK) return st;
+  if (lse != nullptr && !aligned16(lse)) return fail(PDLLM_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+
+  pdllm::DecodePlan plan;
+  const char* err = "";
+  if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
+                          num_splits, device_cu_count(), &plan, &err))
+    return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < (size_t)plan.workspace_bytes)
+      return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %lld bytes needed, %zu given",
+                  (long long)plan.workspace_bytes, workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned16(workspace)) return fail(PDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+
+  pdllm::DecodeArgs a = base_decode_args(pool, pt, q, k_resp, v_resp, l_d, h_q, scale, o, lse);
+  a.q_tiles = plan.q_tiles;
+  if (plan.workspace_bytes > 0) {
+    a.part_o = static_cast<float*>(workspace);
+    const int64_t part_bytes = (plan.part_floats * 4 + 255) / 256 * 256;
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
+  }
+  for (int s0 = 0; s0 < n_seq; s0 += pdllm::kMaxSeqPerLaunch) {
+    const int n_here = std::min(pdllm::kMaxSeqPerLaunch, n_seq - s0);
+    a.seq0 = s0;
+    a.n_seq_launch = n_here;
+    int64_t wg = 0;
+    bool merge = false;
+    for (int i = 0; i < pdllm::kMaxSeqPerLaunch; ++i) {
+      pdllm::DecodeSeq& q_ = a.seq[i];
+      q_ = pdllm::DecodeSeq{};
+      if (i >= n_here) continue;
+      const int s = s0 + i;
+      q_.k_s = plan.k_s[s];
+      q_.n_kv = plan.n_kv[s];
+      q_.n_splits = plan.splits[s];
+      q_.tiles_per_split = plan.tiles_per_split[s];
+      q_.wg_begin = (int32_t)wg;
+      q_.part_off = plan.part_off[s];
+      q_.lse_off = plan.lse_off[s];
+      wg += (int64_t)pool->h_kv * plan.q_tiles * plan.splits[s];
+      merge |= plan.splits[s] > 1;
+    }
+    if (wg > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "decode grid too large");
+    a.total_wg = (int32_t)wg;
+    const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(a, pool->d, stream)
+                                             : pdllm::launch_decode_f32(a, pool->d, stream);
+    if ((st = hip_status(e, "decode launch")) != PDLLM_OK) return st;
+    if (merge) {
+      st = hip_status(pdllm::launch_lse_merge(a, pool->d, pool->dtype == PDLLM_BF16, stream), "merge launch");
+      if (st != PDLLM_OK) return st;
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of
+// libpdllm.  Not part of the public interface (include/pdllm.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+namespace pdllm {
+
+// ---------------------------------------------------------------- planning
+// kv rows per tile of the split-KV decode; a split is a run of whole tiles
+constexpr int kDecodeTile = 64;
+// query rows (token x grouped head) handled by one decode workgroup
+constexpr int kDecodeRowsBf16 = 128;
+constexpr int kDecodeRowsF32 = 64;
+// sequences whose per-sequence plan travels in one launch's arguments
+constexpr int kMaxSeqPerLaunch = 16;
+
+struct DecodePlan {
+  int n_seq = 0;
+  int q_rows_per_wg = 0;   // query rows per workgroup
+  int q_tiles = 0;         // workgroups along the query rows of one (seq, kv head)
+  std::vector<int> k_s, n_kv, n_tiles, splits, tiles_per_split;
+  std::vector<int64_t> part_off, lse_off;   // float offsets into the workspace
+  int64_t part_floats = 0, lse_floats = 0;
+  int64_t workspace_bytes = 0;
+  int64_t total_workgroups = 0;
+};
+
+// Fills `plan`; returns false (with a message in *err) on invalid input.
+bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
+                 int d, int dtype, int num_splits, int n_cu, DecodePlan* plan,
+                 const char** err);
+
+// ---------------------------------------------------------------- decode
+struct DecodeSeq {
+  int32_t k_s;              // selected chunks of this sequence
+  int32_t n_kv;             // attended rows: k_s * (b + 1) + l_d
+  int32_t n_splits;
+  int32_t tiles_per_split;
+  int32_t wg_begin;         // first workgroup of this sequence in the launch
+  int32_t pad_;
+  int64_t part_off;         // float offset of its partial outputs
+  int64_t lse_off;          // float offset of its partial lse values
+};
+
+struct DecodeArgs {
+  const void* pool_k;
+  const void* pool_v;
+  int64_t ps_slot, ps_row, ps_head;   // pool strides (elements)
+  const int32_t* chunk_slot;
+  const int32_t* sel_chunk;
+  const int32_t* keep_rows;
+  const void* q;
+  const void* k_resp;
+  const void* v_resp;
+  void* o;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int32_t n_chunks_per_seq, k_max, b;
+  int32_t l_d, h_q, h_kv, group;
+  int32_t q_tiles;
+  int32_t seq0;             // first sequence of this launch
+  int32_t n_seq_launch;
+  int32_t total_wg;
+  float scale_log2;         // softmax scale * log2(e)
+  DecodeSeq seq[kMaxSeqPerLaunch];
+};
+
+// Launchers (return a hipError_t value as int).
+int launch_decode_bf16(const DecodeArgs& a, int d, void* stream);
+int launch_decode_f32(const DecodeArgs& a, int d, void* stream);
+int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_out, void* stream);
+
+// ---------------------------------------------------------------- prefill
+struct PrefillArgs {
+  const void* pool_k;
+  const void* pool_v;
+  int64_t ps_slot, ps_row, ps_head;
+  const int32_t* chunk_slot;
+  const void* q_chunk;
+  const void* q_win;
+  void* o_chunk;
+  float* key_score;
+  float* part_score;        // workspace [n_chunks][h_kv][slot_rows]
+  int32_t n_chunks, slot_rows, h_q, h_kv, group, w, chunks_per_win;
+  float scale_log2;
+};
+
+int launch_prefill_bf16(const PrefillArgs& a, int d, void* stream);
+int launch_prefill_f32(const PrefillArgs& a, int d, void* stream);
+int launch_score_finalize(const PrefillArgs& a, void* stream);
+
+// ---------------------------------------------------------------- select
+int launch_select_topb(const float* key_score, int n_chunks, int slot_rows, int b,
+                       int32_t* keep_rows, void* stream);
+constexpr int kMaxTopkSeqPerLaunch = 64;
+struct TopkArgs {
+  const float* chunk_score;
+  int32_t* sel_chunk;
+  int32_t n_chunks, k_max, seq0, n_seq_launch;
+  int32_t k[kMaxTopkSeqPerLaunch];
+};
+int launch_select_topk(const TopkArgs& a, void* stream);
+
+}  // namespace pdllm

@@ -1,0 +1,127 @@
+// Split planner of the split-KV decode (host only, deterministic).
+//
+// The decode attention of one sequence covers N_s = K_s (B + 1) + L_d kv
+// rows (every selected chunk's BOS row and B kept rows, then the response
+// rows; Prefilling-dLLM summary, Methodology 2 and 3).  "Attention kernel
+// optimization" splits that KV dimension into independently processed parts
+// merged by log-sum-exp.  Here a split is a run of whole 64-row kv tiles and
+// a workgroup computes one (sequence, kv head, query tile, split).
+//
+// With num_splits = 0 the planner picks one tiles-per-split value for the
+// call by a small cost model measured in tile-times:
+//   time(tps) = max( sum_wg (tiles_wg + c0) / slots,  max_wg (tiles_wg + c0) )
+//             + merge(max_splits)
+// where slots = n_cu * (workgroups resident per CU), c0 is a workgroup's
+// fixed cost (index table, query load, epilogue) and merge() charges the
+// extra merge pass and its partial-output traffic.  Ties go to fewer splits.
+#include <algorithm>
+#include <cstdint>
+
+#include "pdllm_internal.h"
+
+namespace pdllm {
+
+namespace {
+constexpr double kFixedTiles = 2.0;        // c0: per-workgroup overhead in tile-times
+constexpr double kMergeBase = 1.0;         // merge launch + pass, in tile-times
+constexpr double kMergePerSplit = 0.25;    // partial write + read per split
+constexpr int kResidentBf16 = 2;           // decode workgroups per CU (bf16 kernel)
+constexpr int kResidentF32 = 4;
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
+                 int d, int dtype, int num_splits, int n_cu, DecodePlan* plan,
+                 const char** err) {
+  if (n_seq < 1 || l_d < 1 || h_q < 1 || h_kv < 1 || d < 1 || b < 0 || num_splits < 0 ||
+      n_cu < 1 || h_q % h_kv != 0 || k_per_seq == nullptr || plan == nullptr) {
+    *err = "plan: invalid sizes (need n_seq, l_d, h_q, h_kv, d, n_cu >= 1, b >= 0, "
+           "num_splits >= 0, h_q % h_kv == 0)";
+    return false;
+  }
+  const int group = h_q / h_kv;
+  DecodePlan p;
+  p.n_seq = n_seq;
+  p.q_rows_per_wg = dtype == 1 ? kDecodeRowsBf16 : kDecodeRowsF32;
+  const int64_t q_rows = (int64_t)l_d * group;
+  p.q_tiles = (int)((q_rows + p.q_rows_per_wg - 1) / p.q_rows_per_wg);
+  p.k_s.resize(n_seq);
+  p.n_kv.resize(n_seq);
+  p.n_tiles.resize(n_seq);
+  int max_tiles = 1;
+  for (int s = 0; s < n_seq; ++s) {
+    if (k_per_seq[s] < 0) {
+      *err = "plan: k_per_seq entries must be >= 0";
+      return false;
+    }
+    const int64_t nkv = (int64_t)k_per_seq[s] * (b + 1) + l_d;
+    if (nkv > (int64_t)1 << 30) {
+      *err = "plan: too many attended rows";
+      return false;
+    }
+    p.k_s[s] = k_per_seq[s];
+    p.n_kv[s] = (int)nkv;
+    p.n_tiles[s] = (int)((nkv + kDecodeTile - 1) / kDecodeTile);
+    max_tiles = std::max(max_tiles, p.n_tiles[s]);
+  }
+  const int64_t per_split_wg = (int64_t)h_kv * p.q_tiles;
+
+  auto splits_for = [&](int s, int tps) { return (p.n_tiles[s] + tps - 1) / tps; };
+  p.splits.assign(n_seq, 1);
+  p.tiles_per_split.assign(n_seq, 1);
+  if (num_splits > 0) {
+    for (int s = 0; s < n_seq; ++s) {
+      const int want = std::min(num_splits, p.n_tiles[s]);
+      const int tps = (p.n_tiles[s] + want - 1) / want;
+      p.tiles_per_split[s] = tps;
+      p.splits[s] = splits_for(s, tps);
+    }
+  } else {
+    const double slots = (double)n_cu * (dtype == 1 ? kResidentBf16 : kResidentF32);
+    double best = 1e300;
+    int best_tps = max_tiles;
+    for (int tps = max_tiles; tps >= 1; --tps) {
+      double work = 0.0, longest = 0.0;
+      int max_splits = 1;
+      for (int s = 0; s < n_seq; ++s) {
+        const int ns = splits_for(s, tps);
+        max_splits = std::max(max_splits, ns);
+        const int last = p.n_tiles[s] - (ns - 1) * tps;
+        work += per_split_wg * ((ns - 1) * (tps + kFixedTiles) + (last + kFixedTiles));
+        longest = std::max(longest, std::min(tps, p.n_tiles[s]) + kFixedTiles);
+      }
+      double t = std::max(work / slots, longest);
+      if (max_splits > 1) t += kMergeBase + kMergePerSplit * max_splits;
+      if (t < best - 1e-9) {      // strictly better: ties keep fewer splits
+        best = t;
+        best_tps = tps;
+      }
+    }
+    for (int s = 0; s < n_seq; ++s) {
+      p.tiles_per_split[s] = best_tps;
+      p.splits[s] = splits_for(s, best_tps);
+    }
+  }
+
+  p.part_off.assign(n_seq, 0);
+  p.lse_off.assign(n_seq, 0);
+  int64_t part = 0, lse = 0;
+  p.total_workgroups = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    p.total_workgroups += per_split_wg * p.splits[s];
+    if (p.splits[s] > 1) {
+      p.part_off[s] = part;
+      p.lse_off[s] = lse;
+      part += (int64_t)p.splits[s] * l_d * h_q * d;
+      lse += (int64_t)p.splits[s] * l_d * h_q;
+    }
+  }
+  p.part_floats = part;
+  p.lse_floats = lse;
+  p.workspace_bytes = part ? align256(part * 4) + align256(lse * 4) : 0;
+  *plan = std::move(p);
+  return true;
+}
+
+}  // namespace pdllm

@@ -1,0 +1,107 @@
+// Top-B row selection per chunk and top-K chunk selection per sequence
+// (Prefilling-dLLM summary, Methodology 2: intra-chunk sparsity keeps the B
+// rows of a chunk with the largest cumulative attention weight, inter-chunk
+// sparsity keeps the K chunks with the largest score; Methodology 1: the K
+// most relevant chunks by s are selected).
+//
+// Both selections are exact and integer-only: a float score becomes an
+// order-preserving 32-bit key (-0 and +0 share one key, NaN gets the lowest
+// key), and candidate i gets the 64-bit key (key << 32) | ~i so that equal
+// scores rank the lower index first and all keys differ.  A candidate is kept
+// iff fewer than `count` candidates have a larger key (its rank); the kept
+// ones are written in ascending index order with a workgroup prefix count.
+#include "device_common.h"
+#include "pdllm_internal.h"
+
+namespace pdllm {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint64_t rank_key(float x, uint32_t index) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t key;
+  if (x != x) {
+    key = 0u;                               // NaN: after every number
+  } else {
+    if (x == 0.f) u = 0u;                   // -0 == +0
+    key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - index);
+}
+
+// Select the `count` best of the n keys in `keys` (LDS) and write their
+// indices + `index_base`, ascending, to out[0..count).
+__device__ void select_sorted(const uint64_t* keys, int n, int count, int index_base,
+                              int32_t* out, int* wave_counts) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int written = 0;
+  for (int base = 0; base < n; base += kThreads) {
+    const int i = base + tid;
+    bool keep = false;
+    if (i < n) {
+      const uint64_t mine = keys[i];
+      int rank = 0;
+      for (int j = 0; j < n; ++j) rank += keys[j] > mine ? 1 : 0;
+      keep = rank < count;
+    }
+    const uint64_t mask = __ballot(keep);
+    if (lane == 0) wave_counts[wave] = __popcll(mask);
+    __syncthreads();
+    int before = written;
+    for (int w = 0; w < wave; ++w) before += wave_counts[w];
+    const int in_wave = __popcll(mask & ((1ull << lane) - 1ull));
+    if (keep) out[before + in_wave] = i + index_base;
+    int round_total = 0;
+    for (int w = 0; w < kThreads / 64; ++w) round_total += wave_counts[w];
+    written += round_total;
+    __syncthreads();
+  }
+}
+
+// One workgroup per chunk.  Candidates are the content rows 1..slot_rows-1.
+__global__ __launch_bounds__(kThreads) void topb_kernel(const float* key_score, int slot_rows,
+                                                        int b, int32_t* keep_rows) {
+  __shared__ uint64_t keys[4096];
+  __shared__ int wave_counts[kThreads / 64];
+  const int c = blockIdx.x;
+  const int n = slot_rows - 1;
+  const float* row = key_score + (int64_t)c * slot_rows + 1;
+  for (int i = threadIdx.x; i < n; i += kThreads) keys[i] = rank_key(row[i], (uint32_t)i);
+  __syncthreads();
+  select_sorted(keys, n, b, 1, keep_rows + (int64_t)c * b, wave_counts);
+}
+
+// One workgroup per sequence; the K_s of this launch's sequences travel in
+// the arguments.  Entries K_s..k_max-1 are set to -1.
+__global__ __launch_bounds__(kThreads) void topk_kernel(const TopkArgs a) {
+  __shared__ uint64_t keys[8192];
+  __shared__ int wave_counts[kThreads / 64];
+  const int si = blockIdx.x;
+  const int s = a.seq0 + si;
+  const int ks = a.k[si];
+  const float* row = a.chunk_score + (int64_t)s * a.n_chunks;
+  int32_t* out = a.sel_chunk + (int64_t)s * a.k_max;
+  for (int i = threadIdx.x; i < a.n_chunks; i += kThreads) keys[i] = rank_key(row[i], (uint32_t)i);
+  for (int i = ks + threadIdx.x; i < a.k_max; i += kThreads) out[i] = -1;
+  __syncthreads();
+  select_sorted(keys, a.n_chunks, ks, 0, out, wave_counts);
+}
+
+}  // namespace
+
+int launch_select_topb(const float* key_score, int n_chunks, int slot_rows, int b,
+                       int32_t* keep_rows, void* stream) {
+  if (n_chunks == 0 || b == 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(topb_kernel, dim3(n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
+                     key_score, slot_rows, b, keep_rows);
+  return (int)hipGetLastError();
+}
+
+int launch_select_topk(const TopkArgs& a, void* stream) {
+  if (a.n_seq_launch == 0 || a.k_max == 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(a.n_seq_launch), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace pdllm

@@ -1,0 +1,234 @@
+/*
+ * pdllm.h -- C ABI of the chunk-sparse attention path of Prefilling-dLLM on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operations: the technical summary of "Prefilling-dLLM:
+ * Predictive Prefilling for Long-Context Inference in Diffusion Language
+ * Models" (gist.science, paper 2606.10537), sections Methodology 1 ("Chunked
+ * prefill and KV cache"), Methodology 2 ("Two-level sparsity"),
+ * Methodology 3 ("Decoding with static KV reuse") and "Attention kernel
+ * optimization".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named "device" are device memory owned by the caller; the
+ *   library never allocates, frees or retains them.  Pointers named "host"
+ *   are read synchronously during the call and may be reused on return.
+ * - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *   enqueued on it, nothing synchronises with the host, and no device memory
+ *   is allocated, so the calls can be captured in a HIP graph.
+ * - Arguments are validated on the host before anything is enqueued.  On any
+ *   status other than PDLLM_OK nothing was enqueued and the outputs are
+ *   untouched; pdllm_last_error() then describes the problem.  The library
+ *   never aborts and never throws across this boundary.
+ * - The contents of device index tables are trusted (chunk ids, slots and
+ *   rows must be in range); their shapes are checked.
+ * - Floating data is PDLLM_F32 (float) or PDLLM_BF16 (bfloat16 bits, round
+ *   to nearest even on output).  Softmax, accumulation and merges run in
+ *   float32.  The softmax scale is an explicit argument (usually 1/sqrt(d)).
+ * - Grouped-query attention: query head h reads KV head h / G with
+ *   G = h_q / h_kv, i.e. G consecutive query heads share one KV head.
+ * - Tensors are row-major with the last index contiguous.  Pool tensors
+ *   carry explicit element strides; every other tensor is dense.
+ * - bf16 tensors must be 16-byte aligned and their strides multiples of 8
+ *   elements; f32 tensors 16-byte aligned with strides multiples of 4.
+ */
+#ifndef PDLLM_H
+#define PDLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PDLLM_ABI_VERSION 1
+
+typedef enum {
+  PDLLM_OK = 0,
+  PDLLM_ERR_INVALID_ARG = 1,        /* a null pointer, bad size or inconsistent shape */
+  PDLLM_ERR_UNSUPPORTED = 2,        /* valid, but outside what the kernels implement  */
+  PDLLM_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace_bytes below the size query's answer  */
+  PDLLM_ERR_HIP = 4                 /* a HIP runtime error while enqueueing            */
+} pdllm_status;
+
+typedef enum { PDLLM_F32 = 0, PDLLM_BF16 = 1 } pdllm_dtype;
+
+/*
+ * One layer's static chunk KV pool (Methodology 1 and 3: every chunk's KV is
+ * computed once and cached; "Attention kernel optimization": the cached
+ * chunks sit non-contiguously).  A slot holds one chunk: slot_rows = C + 1
+ * rows, row 0 the chunk's BOS token, rows 1..C its tokens.
+ *   k, v   device  [n_slots][slot_rows][h_kv][d] with element strides
+ *                  stride_slot, stride_row, stride_head (d is contiguous)
+ */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t stride_slot;
+  int64_t stride_row;
+  int64_t stride_head;
+  int32_t n_slots;
+  int32_t slot_rows;
+  int32_t h_kv;
+  int32_t d;
+  int32_t dtype;                    /* pdllm_dtype */
+} pdllm_pool;
+
+/*
+ * The chunk page table of a decode call (Methodology 2: only the top-K
+ * chunks of a sequence, and only the top-B rows of each, are attended).
+ *   chunk_slot  device [n_seq * n_chunks_per_seq]   slot of chunk c of sequence
+ *                      s at index s * n_chunks_per_seq + c
+ *   sel_chunk   device [n_seq][k_max]   the selected chunk ids of a sequence
+ *                      (its first k_per_seq[s] entries are used), as written
+ *                      by pdllm_select_topK
+ *   keep_rows   device [n_seq * n_chunks_per_seq][b]   kept content rows
+ *                      (1..C) of every chunk, as written by pdllm_select_topB
+ *   k_per_seq   host   [n_seq]   K_s, 0 <= K_s <= k_max
+ * A selected chunk contributes its BOS row and its b kept rows, in that
+ * order; chunks are visited in sel_chunk order.
+ */
+typedef struct {
+  const int32_t* chunk_slot;
+  const int32_t* sel_chunk;
+  const int32_t* keep_rows;
+  const int32_t* k_per_seq;
+  int32_t n_chunks_per_seq;
+  int32_t k_max;
+  int32_t b;
+} pdllm_page_table;
+
+/* ------------------------------------------------------------------------ *
+ * Prefill side                                                              *
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace pdllm_chunk_prefill_score needs (0 when the arguments
+ * are invalid).  Pure host function. */
+size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slot_rows);
+
+/*
+ * Chunk-local bidirectional attention with fused per-key scoring
+ * (Methodology 1: each chunk, BOS first, is processed on its own with
+ * bidirectional attention inside the chunk; Methodology 2: a chunk's tokens
+ * are ranked by the cumulative bidirectional attention weight they receive
+ * from the query tokens).
+ *
+ *   q_chunk    device [n_chunks][slot_rows][h_q][d]  the chunk rows' queries
+ *   q_win      device [n_chunks / chunks_per_win][w][h_q][d]  query windows;
+ *              chunk c is scored by window c / chunks_per_win
+ *   o_chunk    device [n_chunks][slot_rows][h_q][d]  (pool dtype) out:
+ *              o[c,r,h] = sum_j softmax_j(scale <q_chunk[c,r,h], K[s,j,g]>) V[s,j,g]
+ *              with s = chunk_slot[c], g = h / G, j over the slot's rows
+ *   key_score  device [n_chunks][slot_rows] float out:
+ *              key_score[c,j] = sum_h sum_w softmax_j(scale <q_win[.,w,h], K[s,j,g]>)
+ *              (the window rows' softmax runs over the chunk's own rows only)
+ *   chunk_slot device [n_chunks]
+ *   workspace  device, >= pdllm_prefill_score_workspace(n_chunks, h_kv, slot_rows)
+ * Supported: f32 with d <= 128 (d % 4 == 0); bf16 with d in {64, 128} and
+ * slot_rows <= 257 (the chunk's K and V are held on chip).
+ * The per-key sums are reduced in a fixed order: results are bitwise
+ * reproducible run to run.
+ */
+pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* chunk_slot,
+                                       int32_t n_chunks, const void* q_chunk, int32_t h_q,
+                                       const void* q_win, int32_t w, int32_t chunks_per_win,
+                                       float scale, void* o_chunk, float* key_score,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Top-B rows per chunk (Methodology 2, intra-chunk sparsity).
+ *   key_score  device [n_chunks][slot_rows] float
+ *   keep_rows  device [n_chunks][b] int32 out: the b best rows among the
+ *              content rows 1..slot_rows-1 (row 0, the BOS anchor, is always
+ *              kept and is not a candidate), in ascending order.
+ * Order: larger score first; equal scores (-0 == +0) go to the lower row;
+ * NaN ranks after every number.  0 <= b <= slot_rows - 1, slot_rows <= 4097.
+ * Bit-exact: integer comparisons only.
+ */
+pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t slot_rows,
+                               int32_t b, int32_t* keep_rows, void* stream);
+
+/*
+ * Top-K chunks per sequence over given chunk scores (Methodology 1,
+ * selection of the K most relevant chunks by s; Methodology 2, inter-chunk
+ * sparsity).  Producing s itself needs the language model and is not part of
+ * this library.
+ *   chunk_score device [n_seq][n_chunks] float
+ *   k_per_seq   host   [n_seq]  0 <= K_s <= k_max <= n_chunks
+ *   sel_chunk   device [n_seq][k_max] int32 out: the K_s best chunk ids in
+ *               ascending order, then -1 up to k_max.
+ * Same order and ties as pdllm_select_topB.  n_chunks <= 65536.
+ */
+pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t n_chunks,
+                               const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
+                               void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Decode side                                                               *
+ * ------------------------------------------------------------------------ */
+
+/*
+ * The split plan of a decode call (host only, deterministic).  The attended
+ * rows of sequence s, N_s = K_s (b + 1) + l_d, are cut into kv tiles; a
+ * split is a run of consecutive tiles.  num_splits = 0 lets the planner pick
+ * the split count from the work and n_cu (the device's compute units);
+ * num_splits > 0 forces that many splits per sequence (capped at the
+ * sequence's tile count).
+ *   splits_per_seq  host [n_seq] out   tiles_per_split host [n_seq] out
+ *   workspace_bytes host out: the workspace the call needs
+ */
+pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t b, int32_t l_d,
+                               int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
+                               int32_t num_splits, int32_t n_cu, int32_t* splits_per_seq,
+                               int32_t* tiles_per_split, int64_t* workspace_bytes);
+
+/* Bytes of workspace pdllm_split_attn_decode needs on the current device
+ * (0 when the arguments are invalid).  Host function; queries the device's
+ * compute-unit count once (256 is assumed when no device is visible). */
+size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                         int32_t n_seq, int32_t l_d, int32_t h_q,
+                                         int32_t num_splits);
+
+/*
+ * Split-KV chunk-sparse decode attention with log-sum-exp merge
+ * (Methodology 3: the static cached rows of the selected chunks plus the
+ * freshly recomputed query/response rows are attended by every decode row,
+ * with no mask; "Attention kernel optimization": the KV dimension is split,
+ * each split is processed independently straight from the non-contiguous
+ * pool, and the splits are merged by a log-sum-exp reduction).
+ *
+ *   q        device [n_seq][l_d][h_q][d]
+ *   k_resp   device [n_seq][l_d][h_kv][d]   (pool dtype)
+ *   v_resp   device [n_seq][l_d][h_kv][d]
+ *   o        device [n_seq][l_d][h_q][d] out (pool dtype):
+ *            o[s,i,h] = sum_a softmax_a(scale <q[s,i,h], k_a[g]>) v_a[g] over
+ *            the attended rows a of sequence s (see pdllm_page_table) followed
+ *            by its l_d response rows
+ *   lse      device [n_seq][h_q][l_d] float out, nullable: natural-log
+ *            normaliser ln sum_a exp(scale <q, k_a>)
+ *   workspace device, >= pdllm_split_attn_decode_workspace(...) for the same
+ *            arguments (holds per-split partial outputs, float32)
+ * The result does not depend on num_splits beyond float32 rounding.
+ * Supported: f32 with d <= 128 (d % 4 == 0); bf16 with d in {64, 128}.
+ */
+pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                     const void* q, const void* k_resp, const void* v_resp,
+                                     int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                     int32_t num_splits, void* o, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+
+/* Message of the calling thread's last non-OK status ("" if none). */
+const char* pdllm_last_error(void);
+
+/* PDLLM_ABI_VERSION of the loaded library. */
+int pdllm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDLLM_H */

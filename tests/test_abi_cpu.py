@@ -1,0 +1,165 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/pdllm.h declares, plans deterministically, and rejects bad
+arguments with the documented status codes before touching a device.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = pytest.importorskip("diffusion_long_context_amd._lib")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"\b(pdllm_[a-zA-Z_]+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L.lib, n), f"{n} declared in include/ but not exported"
+    assert set(L.EXPORTS) <= names
+
+
+def test_abi_version():
+    assert L.lib.pdllm_abi_version() == 1
+
+
+def _pool(**kw):
+    f = dict(k=0x10000, v=0x20000, stride_slot=257 * 4 * 128, stride_row=4 * 128, stride_head=128,
+             n_slots=128, slot_rows=257, h_kv=4, d=128, dtype=1)
+    f.update(kw)
+    return L.Pool(f["k"], f["v"], f["stride_slot"], f["stride_row"], f["stride_head"], f["n_slots"],
+                  f["slot_rows"], f["h_kv"], f["d"], f["dtype"])
+
+
+def _pt(ks, **kw):
+    arr = (ctypes.c_int32 * len(ks))(*ks)
+    f = dict(chunk_slot=0x30000, sel_chunk=0x40000, keep_rows=0x50000, n_chunks_per_seq=128,
+             k_max=16, b=256)
+    f.update(kw)
+    pt = L.PageTable(f["chunk_slot"], f["sel_chunk"], f["keep_rows"], ctypes.cast(arr, ctypes.c_void_p),
+                     f["n_chunks_per_seq"], f["k_max"], f["b"])
+    return pt, arr
+
+
+def _decode(pool, pt, n_seq=1, l_d=256, h_q=28, ws=None, ws_bytes=0, q=0x60000, o=0x90000, scale=0.088,
+            splits=0):
+    return L.lib.pdllm_split_attn_decode(ctypes.byref(pool) if pool is not None else None,
+                                         ctypes.byref(pt) if pt is not None else None,
+                                         q, 0x70000, 0x80000, n_seq, l_d, h_q, scale, splits, o, None,
+                                         ws, ws_bytes, None)
+
+
+def _err():
+    return L.lib.pdllm_last_error().decode()
+
+
+@pytest.mark.parametrize("mutate,code,msg", [
+    (dict(pool=None), INVALID, "pool is NULL"),
+    (dict(dtype=7), INVALID, "dtype"),
+    (dict(d=96), UNSUPPORTED, "head dim"),
+    (dict(h_q=27), INVALID, "multiple of h_kv"),
+    (dict(l_d=0), INVALID, ">= 1"),
+    (dict(k_per_seq=[17]), INVALID, "k_per_seq[0]"),
+    (dict(k_per_seq=[-1]), INVALID, "k_per_seq[0]"),
+    (dict(b=257), INVALID, "b 257"),
+    (dict(k_max=129), INVALID, "k_max"),
+    (dict(stride_head=64), INVALID, "strides"),
+    (dict(stride_head=132), INVALID, "multiples"),
+    (dict(k=0x10008), INVALID, "aligned"),
+    (dict(q=0), INVALID, "q is NULL"),
+    (dict(o=0x90004), INVALID, "aligned"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(splits=-1), INVALID, "num_splits"),
+    (dict(), WS_SMALL, "workspace"),
+])
+def test_decode_validation(mutate, code, msg):
+    pool_kw = {k: mutate[k] for k in ("dtype", "d", "stride_head", "stride_row", "k") if k in mutate}
+    pool = None if "pool" in mutate else _pool(**pool_kw)
+    pt_kw = {k: mutate[k] for k in ("b", "k_max") if k in mutate}
+    pt, _keep = _pt(mutate.get("k_per_seq", [16]), **pt_kw)
+    call = {k: mutate[k] for k in ("h_q", "l_d", "q", "o", "scale", "splits") if k in mutate}
+    st = _decode(pool, pt, **call)
+    assert st == code, _err()
+    assert msg in _err()
+
+
+def test_decode_workspace_query_matches_plan():
+    pool = _pool()
+    pt, _keep = _pt([16])
+    ws = L.lib.pdllm_split_attn_decode_workspace(ctypes.byref(pool), ctypes.byref(pt), 1, 256, 28, 0)
+    splits, tps, plan_ws = L.decode_plan([16], 256, 256, 28, 4, 128, 1, 0, n_cu=256)
+    assert ws == plan_ws > 0
+    assert splits[0] > 1
+
+
+def test_prefill_validation():
+    pool = _pool()
+    f = L.lib.pdllm_chunk_prefill_score
+    args = lambda **kw: [ctypes.byref(kw.get("pool", pool)), 0x30000, kw.get("n", 128), 0x60000,
+                         kw.get("h_q", 28), 0x70000, kw.get("w", 64), kw.get("cpw", 128), 0.088, 0x90000,
+                         0xA0000, kw.get("ws", None), kw.get("ws_bytes", 0), None]
+    assert f(*args(h_q=30)) == INVALID
+    assert f(*args(w=0)) == INVALID
+    assert f(*args(cpw=0)) == INVALID
+    assert f(*args()) == WS_SMALL
+    need = L.lib.pdllm_prefill_score_workspace(128, 4, 257)
+    assert need >= 128 * 4 * 257 * 4
+    assert f(*args(pool=_pool(slot_rows=300, stride_slot=300 * 512))) == UNSUPPORTED
+    assert f(*args(n=0)) == OK                       # nothing to do, nothing enqueued
+
+
+def test_select_validation():
+    tb = L.lib.pdllm_select_topB
+    assert tb(0x1000, 4, 33, 33, 0x2000, None) == INVALID          # b > slot_rows - 1
+    assert tb(0x1000, 4, 5000, 3, 0x2000, None) == UNSUPPORTED
+    assert tb(0x1000, -1, 33, 3, 0x2000, None) == INVALID
+    assert tb(0x1000, 4, 33, 0, 0x2000, None) == OK                # b = 0: nothing to do
+    tk = L.lib.pdllm_select_topK
+    ks = (ctypes.c_int32 * 2)(3, 9)
+    assert tk(0x1000, 2, 8, ks, 8, 0x2000, None) == INVALID        # K_s > k_max
+    assert tk(0x1000, 2, 8, ks, 9, 0x2000, None) == INVALID        # k_max > n_chunks
+    assert tk(0x1000, 2, 9000, ks, 9, 0x2000, None) == UNSUPPORTED
+    assert tk(0x1000, 0, 8, ks, 8, 0x2000, None) == OK
+
+
+@pytest.mark.parametrize("ks,b,l_d,g,dtype", [
+    ([16], 256, 256, 7, 1), ([8], 128, 256, 7, 1), ([8, 16, 24, 32], 128, 512, 7, 1),
+    ([2], 16, 32, 1, 0), ([0, 1, 40], 7, 3, 2, 1), ([5], 0, 1, 1, 0),
+])
+def test_plan_properties(ks, b, l_d, g, dtype):
+    h_kv = 4 if g == 7 else 2
+    h_q = g * h_kv
+    d = 128 if dtype else 64
+    for num_splits in (0, 1, 2, 3, 1000):
+        a = L.decode_plan(ks, b, l_d, h_q, h_kv, d, dtype, num_splits)
+        assert a == L.decode_plan(ks, b, l_d, h_q, h_kv, d, dtype, num_splits)   # deterministic
+        splits, tps, ws = a
+        need = 0
+        for s, k in enumerate(ks):
+            n_tiles = -(-(k * (b + 1) + l_d) // 64)
+            assert splits[s] >= 1 and tps[s] >= 1
+            assert (splits[s] - 1) * tps[s] < n_tiles <= splits[s] * tps[s]
+            if num_splits:
+                assert splits[s] <= min(num_splits, n_tiles)
+            if splits[s] > 1:
+                need += splits[s] * l_d * h_q * (d + 1) * 4
+        assert (ws == 0) == (need == 0) and ws >= need
+
+
+def test_plan_rejects_bad_sizes():
+    with pytest.raises(L.PdllmError):
+        L.decode_plan([4], 8, 16, 6, 4, 128, 1)
+    with pytest.raises(L.PdllmError):
+        L.decode_plan([-1], 8, 16, 8, 4, 128, 1)

@@ -1,0 +1,162 @@
+"""GPU parity of pdllm_split_attn_decode against the fp64 oracle, through the
+C ABI, on seeded inputs: the Tiny fp32 case, small bf16 shapes spanning
+several tiles with ragged tails, the 8K / 32K / 128K workloads, forced split
+counts, and the degenerate cases (no chunks, no kept rows, one row)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _parity import TOL, assert_close, dev, host, max_abs, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(inp, sel, keep, cfg, num_splits=0):
+    from diffusion_long_context_amd import _lib as L
+    call = L.Decode(dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot), dev(sel), dev(keep),
+                    cfg.k_per_seq, dev(inp.q), dev(inp.k_resp), dev(inp.v_resp), cfg.scale,
+                    num_splits=num_splits)
+    o, lse = call()
+    import torch
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def _oracle(inp, sel, keep, cfg, heads=None):
+    return oracle.split_attn_decode(inp.pool_k, inp.pool_v, inp.chunk_slot, sel, keep, cfg.k_per_seq,
+                                    inp.q, inp.k_resp, inp.v_resp, cfg.scale, heads=heads)
+
+
+def _compare(o, lse, ro, rlse, cfg, what, heads=None):
+    kind = cfg.dtype
+    if heads is not None:
+        o, ro = o[:, :, heads], ro[:, :, heads]
+        lse, rlse = lse[:, heads], rlse[:, heads]
+    r, m = assert_close(o, ro, kind, what)
+    ml = max_abs(lse, rlse)
+    assert ml <= TOL[kind]["lse"], f"{what}: lse max-abs {ml:.3e}"
+    say(f"  {what}: rel-L2 {r:.2e} max-abs {m:.2e} lse {ml:.2e}")
+
+
+def test_tiny_f32(device):
+    cfg = synth.config("tiny")
+    inp = synth.generate(cfg, 0)
+    sel, keep = synth.random_page_table(cfg, 0)
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    for ns in (0, 1, 2, 3):
+        say(f"tiny f32 decode, num_splits={ns}")
+        o, lse = _run_gpu(inp, sel, keep, cfg, ns)
+        _compare(o, lse, ro, rlse, cfg, f"tiny splits={ns}")
+
+
+SMALL = [
+    # (name, overrides)
+    ("g7_d128", dict(h_q=7, h_kv=1, d=128, n_chunks=6, chunk=40, k_per_seq=(3,), b=17, l_d=33)),
+    ("g7x4_d128", dict(h_q=28, h_kv=4, d=128, n_chunks=5, chunk=64, k_per_seq=(2,), b=64, l_d=20)),
+    ("g2_d64_multi", dict(h_q=4, h_kv=2, d=64, n_chunks=4, chunk=31, k_per_seq=(4, 0, 1), b=9, l_d=70,
+                          n_seq=3)),
+    ("g1_d64_b0", dict(h_q=3, h_kv=3, d=64, n_chunks=7, chunk=16, k_per_seq=(5,), b=0, l_d=5)),
+    ("one_row", dict(h_q=8, h_kv=2, d=128, n_chunks=3, chunk=8, k_per_seq=(0,), b=2, l_d=1)),
+    ("f32_d32", dict(h_q=6, h_kv=2, d=32, dtype="f32", n_chunks=5, chunk=20, k_per_seq=(3, 5), b=11,
+                     l_d=9, n_seq=2)),
+    ("f32_d128", dict(h_q=2, h_kv=1, d=128, dtype="f32", n_chunks=4, chunk=70, k_per_seq=(4,), b=70,
+                      l_d=17)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes(device, name, kw):
+    base = dict(name=name, dtype="bf16", w=4, n_seq=1)
+    base.update(kw)
+    cfg = synth.Config(**base)
+    for seed in (0, 1):
+        inp = synth.generate(cfg, seed)
+        sel, keep = synth.random_page_table(cfg, seed)
+        ro, rlse = _oracle(inp, sel, keep, cfg)
+        for ns in (0, 1, 2, 5):
+            say(f"{name} seed={seed} num_splits={ns}")
+            o, lse = _run_gpu(inp, sel, keep, cfg, ns)
+            _compare(o, lse, ro, rlse, cfg, f"{name} seed {seed} splits {ns}")
+
+
+@pytest.mark.parametrize("name", ["s8", "s32"])
+def test_full_size_single_sequence(device, name):
+    cfg = synth.config(name)
+    inp = synth.generate(cfg, 0)
+    sel, keep = synth.random_page_table(cfg, 0)
+    say(f"{name}: oracle")
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    say(f"{name}: gpu, planner's split count")
+    o, lse = _run_gpu(inp, sel, keep, cfg, 0)
+    _compare(o, lse, ro, rlse, cfg, f"{name} planner")
+
+
+def test_s32_split_invariance(device):
+    """Any forced split count gives the oracle's result (and nearly the same
+    bits as one split)."""
+    cfg = synth.config("s32")
+    inp = synth.generate(cfg, 1)
+    sel, keep = synth.random_page_table(cfg, 1)
+    heads = [0, 6, 7, 13, 27]
+    ro, rlse = _oracle(inp, sel, keep, cfg, heads=heads)
+    base = None
+    for ns in (1, 2, 3, 7, 23, 69):
+        say(f"s32 num_splits={ns}")
+        o, lse = _run_gpu(inp, sel, keep, cfg, ns)
+        _compare(o, lse, ro, rlse, cfg, f"s32 splits {ns}", heads=heads)
+        if base is None:
+            base = o
+        else:
+            assert max_abs(o, base) <= 2 * 2 ** -8 * max(1.0, np.abs(base).max())
+
+
+def test_s128_batch_sampled_heads(device):
+    cfg = synth.config("s128")
+    say("s128: generating inputs")
+    inp = synth.generate(cfg, 0)
+    sel, keep = synth.random_page_table(cfg, 0)
+    heads = [0, 5, 9, 20, 27]
+    say("s128: oracle on sampled heads")
+    ro, rlse = _oracle(inp, sel, keep, cfg, heads=heads)
+    say("s128: gpu")
+    o, lse = _run_gpu(inp, sel, keep, cfg, 0)
+    _compare(o, lse, ro, rlse, cfg, "s128", heads=heads)
+
+
+def test_identical_keys_give_mean_of_values(device):
+    cfg = synth.Config("same", 14, 2, 128, "bf16", 4, 48, (3,), 20, 40, 4)
+    inp = synth.generate(cfg, 3)
+    sel, keep = synth.random_page_table(cfg, 3)
+    inp.pool_k[:] = inp.pool_k[0, 0]
+    inp.k_resp[:] = inp.pool_k[0, 0]
+    say("identical keys")
+    o, _ = _run_gpu(inp, sel, keep, cfg, 2)
+    ro, _ = _oracle(inp, sel, keep, cfg)
+    _, vv = oracle.attended_kv(inp.pool_k, inp.pool_v, inp.chunk_slot, sel, keep, 3, 0, 4, inp.k_resp,
+                               inp.v_resp)
+    g_of = np.arange(cfg.h_q) // (cfg.h_q // cfg.h_kv)
+    mean = vv.mean(axis=0)[g_of]                       # [h_q][d]
+    assert_close(o[0], np.broadcast_to(mean, o[0].shape), "bf16", "identical keys")
+    assert_close(o, ro, "bf16", "identical keys vs oracle")
+
+
+def test_full_selection_equals_dense(device):
+    cfg = synth.Config("dense", 8, 2, 64, "bf16", 4, 30, (4, 4), 30, 12, 4, n_seq=2)
+    inp = synth.generate(cfg, 5)
+    sel = np.tile(np.arange(4, dtype=np.int32), (2, 1))
+    keep = np.tile(np.arange(1, 31, dtype=np.int32), (8, 1))
+    say("K = N, B = C")
+    o, lse = _run_gpu(inp, sel, keep, cfg, 3)
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    _compare(o, lse, ro, rlse, cfg, "dense")
+
+
+def test_rerun_is_bitwise_identical(device):
+    cfg = synth.config("s8")
+    inp = synth.generate(cfg, 2)
+    sel, keep = synth.random_page_table(cfg, 2)
+    say("s8 rerun determinism")
+    a, la = _run_gpu(inp, sel, keep, cfg, 0)
+    b, lb = _run_gpu(inp, sel, keep, cfg, 0)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
