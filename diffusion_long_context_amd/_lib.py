@@ -62,7 +62,7 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_select_topK.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     lib.pdllm_decode_plan.restype = ctypes.c_int
     lib.pdllm_decode_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp,
-                                      P(i64)]
+                                      P(i32), P(i64)]
     lib.pdllm_split_attn_decode_workspace.restype = sz
     lib.pdllm_split_attn_decode_workspace.argtypes = [P(Pool), P(PageTable), i32, i32, i32, i32]
     lib.pdllm_split_attn_decode.restype = ctypes.c_int
@@ -176,15 +176,19 @@ def select_topk(chunk_score: torch.Tensor, k_per_seq: Sequence[int], k_max: int,
     return sel_chunk
 
 
-def decode_plan(k_per_seq, b, l_d, h_q, h_kv, d, dtype, num_splits=0, n_cu=256):
-    """pdllm_decode_plan (host only): returns (splits, tiles_per_split, workspace_bytes)."""
+def decode_plan(k_per_seq, b, l_d, h_q, h_kv, d, dtype, num_splits=0, n_cu=256, with_rows=False):
+    """pdllm_decode_plan (host only): returns (splits, tiles_per_split,
+    workspace_bytes), and the query rows per workgroup if ``with_rows``."""
     n_seq = len(k_per_seq)
     ks = (ctypes.c_int32 * n_seq)(*[int(x) for x in k_per_seq])
     splits = (ctypes.c_int32 * n_seq)()
     tps = (ctypes.c_int32 * n_seq)()
+    rows = ctypes.c_int32(0)
     ws = ctypes.c_int64(0)
     _check(lib.pdllm_decode_plan(ks, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, n_cu, splits,
-                                 tps, ctypes.byref(ws)), "pdllm_decode_plan")
+                                 tps, ctypes.byref(rows), ctypes.byref(ws)), "pdllm_decode_plan")
+    if with_rows:
+        return list(splits), list(tps), ws.value, rows.value
     return list(splits), list(tps), ws.value
 
 

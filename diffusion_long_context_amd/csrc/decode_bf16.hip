@@ -6,8 +6,8 @@
 // each selected chunk -- read in place from the non-contiguous chunk pool --
 // followed by the sequence's recomputed response rows.  The kv rows are split
 // into runs of 64-row tiles; each workgroup handles one (sequence, kv head,
-// 128 query rows, split) and emits either the final output (single split) or
-// a float32 partial output and its log-sum-exp for the merge kernel.
+// 128 or 256 query rows, split) and emits either the final output (single
+// split) or a float32 partial output and its log-sum-exp for the merge kernel.
 //
 // Design for CDNA4:
 // * Query rows of one kv head are packed as (token, grouped head) pairs, so
@@ -18,10 +18,13 @@
 //   B operand directly (no shuffle through LDS).
 // * K/V tiles are gathered straight from pool slots into LDS through a
 //   per-workgroup row-offset table (no gather-to-contiguous copy); V is stored
-//   transposed so the PV A operand is two 8-byte LDS reads.  The next tile's
-//   global loads are issued before the current tile's MFMAs.
-// * Online softmax in base 2 with the scale folded into log2(e); per-lane
-//   partial row sums are reduced across lanes once, at the end.
+//   transposed so the PV A operand is two 8-byte LDS reads.  Tiles are
+//   double-buffered in LDS (one barrier per tile); the global loads of tile
+//   t+2 are in flight while tile t computes.
+// * Online softmax in base 2: the scale and log2(e) fold into one FMA before
+//   v_exp_f32, the running max moves lazily (see kRescaleLog2), and the row
+//   sums come out of the PV MFMA with an all-ones operand.
+#include "attn_tile.h"
 #include "device_common.h"
 #include "pdllm_internal.h"
 
@@ -29,20 +32,16 @@ namespace pdllm {
 namespace {
 
 constexpr int kTile = kDecodeTile;         // kv rows per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveRows = kDecodeRowsBf16 / kWaves;   // 32 query rows per wave
-constexpr int kTableTiles = 16;            // row-offset table capacity (tiles)
-constexpr int64_t kMaskedRow = INT64_MIN;
-static_assert(kWaveRows == 32, "two 16-row MFMA column blocks per wave");
+constexpr int kTableTiles = 8;             // row-pointer table capacity (tiles)
 
 template <int D>
 struct Smem {
   static constexpr int KP = D + 8;         // K tile pitch (elements): 16-row reads conflict-free
   static constexpr int VP = kTile + 4;     // V^T pitch (elements): 16 d-rows hit distinct banks
-  uint16_t k[kTile * KP];
-  uint16_t vt[D * VP];
-  int64_t rowoff[kTableTiles * kTile];
+  uint16_t k[2][kTile * KP];               // double-buffered tiles
+  uint16_t vt[2][D * VP];
+  gptr16 kptr[kTableTiles * kTile];        // K / V address of each attended row
+  gptr16 vptr[kTableTiles * kTile];
 };
 
 // Element offset of attended row v of sequence s for kv head g.  Pool rows
@@ -65,15 +64,17 @@ __device__ __forceinline__ int64_t resolve_row(const DecodeArgs& a, int s, int g
   return -1 - ((((int64_t)s * a.l_d + j) * a.h_kv + g) * D);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(const DecodeArgs a) {
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kRows = 32 * WAVES;        // query rows of the workgroup
   __shared__ Smem<D> sm;
   constexpr int KP = Smem<D>::KP, VP = Smem<D>::VP;
-  constexpr int DC = D / 32;               // 32-wide k chunks of QK^T
-  constexpr int DB = D / 16;               // 16-row d blocks of O^T
+  using Attn = WaveAttn<D, KP, VP>;
+  constexpr int DC = Attn::DC, DB = Attn::DB;
   constexpr int TPR = D / 8;               // loader threads per kv row (16 B each)
   constexpr int RPT = kTile * TPR / kThreads;   // kv rows per loader thread
-  static_assert(RPT == 2 || RPT == 4, "D must be 64 or 128");
+  static_assert(RPT == 1 || RPT == 2 || RPT == 4, "loader mapping");
 
   // ---- work item: (sequence, kv head, query tile, split)
   const int wg = xcd_remap(blockIdx.x, a.total_wg);
@@ -97,197 +98,125 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(const DecodeAr
   const int lr = lane & 15, lj = lane >> 4;
   const int G = a.group;
   const int rows_total = a.l_d * G;
-
-  // ---- queries: B-operand fragments of S^T (lane: query column lr, d = 32 dc + 8 lj ..)
-  bf16x8 qf[2][DC];
-  int qrow[2];
-  {
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int r = qt * kDecodeRowsBf16 + wave * kWaveRows + 16 * b + lr;
-      qrow[b] = r;
-      if (r < rows_total) {
-        const int i = r / G, h = g * G + (r - i * G);
-        const uint16_t* p = qb + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj;
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) qf[b][dc] = *reinterpret_cast<const bf16x8*>(p + 32 * dc);
-      } else {
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) qf[b][dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      }
-    }
-  }
-
-  // ---- row-offset table for tiles [tw, tw + kTableTiles)
-  auto build_table = [&](int tw) {
-    const int nrow = (min(tw + kTableTiles, t_end) - tw) * kTile;
-    for (int idx = tid; idx < nrow; idx += kThreads) {
-      const int v = tw * kTile + idx;
-      sm.rowoff[idx] = v < n_kv ? resolve_row<D>(a, s, g, k_s, v) : kMaskedRow;
-    }
-  };
-
-  // ---- tile loader: thread owns RPT consecutive kv rows x 8 d values
-  const int ld_d0 = 8 * (tid % TPR);
-  const int ld_r0 = RPT * (tid / TPR);
   const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k);
   const uint16_t* pv = static_cast<const uint16_t*>(a.pool_v);
   const uint16_t* rk = static_cast<const uint16_t*>(a.k_resp);
   const uint16_t* rv = static_cast<const uint16_t*>(a.v_resp);
-  u32x4 kreg[RPT], vreg[RPT];
-  auto load_tile = [&](int t, int tw) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int64_t off = sm.rowoff[(t - tw) * kTile + ld_r0 + i];
-      if (off != kMaskedRow) {
-        const bool pool = off >= 0;
-        const int64_t e = (pool ? off : -1 - off) + ld_d0;
-        kreg[i] = *reinterpret_cast<const u32x4*>((pool ? pk : rk) + e);
-        vreg[i] = *reinterpret_cast<const u32x4*>((pool ? pv : rv) + e);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
+
+  // ---- row-pointer table for tiles [tw, tw + kTableTiles); rows past n_kv
+  // point at the sequence's first response row (finite data, masked scores)
+  auto build_table = [&](int tw) {
+    const int nrow = (min(tw + kTableTiles, t_end) - tw) * kTile;
+    for (int idx = tid; idx < nrow; idx += kThreads) {
+      const int v = tw * kTile + idx;
+      const int64_t off = resolve_row<D>(a, s, g, k_s, min(v, n_kv - 1));
+      const bool pool = off >= 0;
+      const int64_t e = pool ? off : -1 - off;
+      sm.kptr[idx] = (gptr16)((pool ? pk : rk) + e);
+      sm.vptr[idx] = (gptr16)((pool ? pv : rv) + e);
     }
   };
-  auto store_tile = [&]() {
+  int tw = t_begin;
+  build_table(tw);
+
+  // ---- queries: B-operand fragments of S^T (lane: query column lr, d = 32 dc + 8 lj ..)
+  bf16x8 qf[2][DC];
+  int qrow[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int r = qt * kRows + wave * 32 + 16 * b + lr;
+    qrow[b] = r;
+    if (r < rows_total) {
+      const int i = r / G, h = g * G + (r - i * G);
+      load_q<DC>(qf[b], static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
+    } else {
+      zero_q<DC>(qf[b]);
+    }
+  }
+
+  // ---- tile loader: thread owns RPT consecutive kv rows x 8 d values
+  const int ld_d0 = 8 * (tid % TPR);
+  const int ld_r0 = RPT * (tid / TPR);
+  u32x4 kreg[RPT], vreg[RPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int idx = (t - tw) * kTile + ld_r0 + i;
+      kreg[i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(sm.kptr[idx] + ld_d0);
+      vreg[i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(sm.vptr[idx] + ld_d0);
+    }
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[(ld_r0 + i) * KP + ld_d0]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1, sh = (e & 1) * 16;
-      uint16_t* dst = &sm.vt[(ld_d0 + e) * VP + ld_r0];
+      uint16_t* dst = &sm.vt[buf][(ld_d0 + e) * VP + ld_r0];
       if constexpr (RPT == 4) {
         const uint32_t lo = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
         const uint32_t hi = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
         *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-      } else {
+      } else if constexpr (RPT == 2) {
         *reinterpret_cast<uint32_t*>(dst) =
             ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
+      } else {
+        *dst = (uint16_t)((vreg[0][w] >> sh) & 0xffffu);
       }
     }
   };
 
-  // ---- accumulators: O^T blocks (lane: query column lr, d = 16 db + 4 lj + e)
-  f32x4 acc[DB][2];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  Attn at;
+  at.init();
   const float sl2 = a.scale_log2;
+  const int k_lane = lr * KP + 8 * lj;      // lane offsets inside one LDS buffer
+  const int v_lane = lr * VP + 4 * lj;
 
-  auto compute_tile = [&](int t) {
-    f32x4 sc[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.k[(16 * kb + lr) * KP + 32 * dc + 8 * lj]);
-        sc[kb][0] = mfma16x16x32(ka, qf[0][dc], sc[kb][0]);
-        sc[kb][1] = mfma16x16x32(ka, qf[1][dc], sc[kb][1]);
-      }
-    }
-    // lane holds S^T[kv = 16 kb + 4 lj + e][q = lr]
-    const int kv0 = t * kTile;
-    const bool tail = kv0 + kTile > n_kv;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = sc[kb][b][e] * sl2;
-          if (tail && kv0 + 16 * kb + 4 * lj + e >= n_kv) x = -INFINITY;
-          sc[kb][b][e] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = wave_xor_max(mx, 16);
-      mx = wave_xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[b], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[b] - m_use);
-      m_run[b] = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(sc[kb][b][e] - m_use);
-          sc[kb][b][e] = p;
-          psum += p;
-        }
-      l_run[b] = l_run[b] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][b] *= alpha;
-      // B operand of O^T += V^T P^T for kv chunk kc: elements 0..3 are kv
-      // 32 kc + 4 lj + e, elements 4..7 are kv 32 kc + 16 + 4 lj + e.
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        pf[kc][b] = bf16x8{(__bf16)sc[2 * kc][b][0], (__bf16)sc[2 * kc][b][1],
-                           (__bf16)sc[2 * kc][b][2], (__bf16)sc[2 * kc][b][3],
-                           (__bf16)sc[2 * kc + 1][b][0], (__bf16)sc[2 * kc + 1][b][1],
-                           (__bf16)sc[2 * kc + 1][b][2], (__bf16)sc[2 * kc + 1][b][3]};
-    }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vp = &sm.vt[(16 * db + lr) * VP + 32 * kc + 4 * lj];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        acc[db][0] = mfma16x16x32(va, pf[kc][0], acc[db][0]);
-        acc[db][1] = mfma16x16x32(va, pf[kc][1], acc[db][1]);
-      }
-    }
-  };
-
-  // ---- main loop: register prefetch of tile t+1 while tile t computes
-  int tw = t_begin;
-  build_table(tw);
+  // ---- main loop: tile t computes from LDS buffer (t - t_begin) & 1 while
+  // tile t+1 is stored into the other buffer and tile t+2 is being loaded;
+  // one barrier per tile
+  __syncthreads();                         // row table ready
+  load_tile(t_begin);
+  store_tile(0);
+  if (t_begin + 1 < t_end) load_tile(t_begin + 1);
   __syncthreads();
-  load_tile(t_begin, tw);
   for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();                       // every wave is done with the previous tile
-    store_tile();
-    if (t + 1 < t_end && t + 1 - tw >= kTableTiles) {
-      tw = t + 1;                          // nobody reads the table until the barrier below
-      build_table(tw);
+    const int buf = (t - t_begin) & 1;
+    const uint16_t* kb = &sm.k[0][0] + buf * (kTile * KP) + k_lane;
+    const uint16_t* vb = &sm.vt[0][0] + buf * (D * VP) + v_lane;
+    at.template step<4>(kb, vb, qf, sl2, n_kv - t * kTile, lj);
+    if (t + 1 < t_end) {
+      store_tile(buf ^ 1);                 // that buffer was last read by tile t-1
+      if (t + 2 < t_end) {
+        if (t + 2 - tw >= kTableTiles) {   // refill the row table (rare)
+          __syncthreads();                 // every wave has read the old table
+          tw = t + 2;
+          build_table(tw);
+          __syncthreads();
+        }
+        load_tile(t + 2);
+      }
     }
     __syncthreads();
-    if (t + 1 < t_end) load_tile(t + 1, tw);
-    compute_tile(t);
   }
 
   // ---- epilogue
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    float l = l_run[b];
-    l = wave_xor_sum(l, 16);
-    l = wave_xor_sum(l, 32);
     const int r = qrow[b];
     if (r >= rows_total) continue;
     const int i = r / G, h = g * G + (r - i * G);
-    const float inv = 1.f / l;
-    const float lse_v = m_run[b] * kLn2 + logf(l);
+    const float inv = 1.f / at.row_sum(b);
+    const float lse_v = at.lse(b);
     if (n_splits == 1) {
-      uint16_t* op = static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 4 * lj;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 x = acc[db][b] * inv;
-        *reinterpret_cast<u32x2*>(op + 16 * db) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-      }
+      store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 4 * lj,
+                       at.acc, b, inv);
       if (a.lse != nullptr && lj == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
     } else {
       float* pp = a.part_o + a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 4 * lj;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = acc[db][b] * inv;
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = at.acc[db][b] * inv;
       if (lj == 0) a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;
     }
   }
@@ -344,12 +273,17 @@ int merge_launch(const DecodeArgs& a, void* stream) {
 
 }  // namespace
 
-int launch_decode_bf16(const DecodeArgs& a, int d, void* stream) {
-  const dim3 grid(a.total_wg), block(kThreads);
-  if (d == 128)
-    hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, block, 0, (hipStream_t)stream, a);
-  else if (d == 64)
-    hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, (hipStream_t)stream, a);
+int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream) {
+  const dim3 grid(a.total_wg);
+  const hipStream_t st = (hipStream_t)stream;
+  if (d == 128 && q_rows_per_wg == 256)
+    hipLaunchKernelGGL((decode_bf16_kernel<128, 8>), grid, dim3(512), 0, st, a);
+  else if (d == 128 && q_rows_per_wg == 128)
+    hipLaunchKernelGGL((decode_bf16_kernel<128, 4>), grid, dim3(256), 0, st, a);
+  else if (d == 64 && q_rows_per_wg == 256)
+    hipLaunchKernelGGL((decode_bf16_kernel<64, 8>), grid, dim3(512), 0, st, a);
+  else if (d == 64 && q_rows_per_wg == 128)
+    hipLaunchKernelGGL((decode_bf16_kernel<64, 4>), grid, dim3(256), 0, st, a);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();

@@ -13,6 +13,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Pointers known to be in device global memory (loads through them are
+// global_load, which does not share the LDS wait counter as flat loads do).
+typedef __attribute__((address_space(1))) const uint16_t* gptr16;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

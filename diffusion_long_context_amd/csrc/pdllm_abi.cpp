@@ -11,7 +11,7 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/pdllm.h"
+#include "pdllm.h"
 #include "pdllm_internal.h"
 
 namespace {
@@ -276,7 +276,8 @@ pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t 
 pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t b, int32_t l_d,
                                int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
                                int32_t num_splits, int32_t n_cu, int32_t* splits_per_seq,
-                               int32_t* tiles_per_split, int64_t* workspace_bytes) {
+                               int32_t* tiles_per_split, int32_t* q_rows_per_wg,
+                               int64_t* workspace_bytes) {
   if (dtype != PDLLM_F32 && dtype != PDLLM_BF16) return fail(PDLLM_ERR_INVALID_ARG, "bad dtype %d", dtype);
   pdllm::DecodePlan plan;
   const char* err = "";
@@ -286,6 +287,7 @@ pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t 
     if (splits_per_seq) splits_per_seq[s] = plan.splits[s];
     if (tiles_per_split) tiles_per_split[s] = plan.tiles_per_split[s];
   }
+  if (q_rows_per_wg) *q_rows_per_wg = plan.q_rows_per_wg;
   if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
   return ok();
 }
@@ -358,7 +360,7 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
     }
     if (wg > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "decode grid too large");
     a.total_wg = (int32_t)wg;
-    const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(a, pool->d, stream)
+    const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(a, pool->d, plan.q_rows_per_wg, stream)
                                              : pdllm::launch_decode_f32(a, pool->d, stream);
     if ((st = hip_status(e, "decode launch")) != PDLLM_OK) return st;
     if (merge) {

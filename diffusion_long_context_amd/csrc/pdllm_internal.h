@@ -12,8 +12,10 @@ namespace pdllm {
 // ---------------------------------------------------------------- planning
 // kv rows per tile of the split-KV decode; a split is a run of whole tiles
 constexpr int kDecodeTile = 64;
-// query rows (token x grouped head) handled by one decode workgroup
-constexpr int kDecodeRowsBf16 = 128;
+// query rows (token x grouped head) handled by one decode workgroup: the bf16
+// kernel runs 4 or 8 wavefronts of 32 rows, the planner picks per call
+constexpr int kDecodeRowsBf16Small = 128;
+constexpr int kDecodeRowsBf16Large = 256;
 constexpr int kDecodeRowsF32 = 64;
 // sequences whose per-sequence plan travels in one launch's arguments
 constexpr int kMaxSeqPerLaunch = 16;
@@ -71,7 +73,7 @@ struct DecodeArgs {
 };
 
 // Launchers (return a hipError_t value as int).
-int launch_decode_bf16(const DecodeArgs& a, int d, void* stream);
+int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream);
 int launch_decode_f32(const DecodeArgs& a, int d, void* stream);
 int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_out, void* stream);
 

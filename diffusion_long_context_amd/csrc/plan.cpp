@@ -8,13 +8,15 @@
 // a workgroup computes one (sequence, kv head, query tile, split).
 //
 // With num_splits = 0 the planner picks one tiles-per-split value for the
-// call by a small cost model measured in tile-times:
-//   time(tps) = max( sum_wg (tiles_wg + c0) / slots,  max_wg (tiles_wg + c0) )
-//             + merge(max_splits)
-// where slots = n_cu * (workgroups resident per CU), c0 is a workgroup's
-// fixed cost (index table, query load, epilogue) and merge() charges the
-// extra merge pass and its partial-output traffic.  Ties go to fewer splits.
+// call by a small cost model measured in tile-times.  Workgroups of one call
+// have nearly equal length, so they run in rounds of `slots` (compute units
+// times the workgroups resident per CU):
+//   time(tps) = ceil(n_wg / slots) * (tps + c0) + merge(max_splits)
+// where c0 is a workgroup's fixed cost (index table, query load, epilogue)
+// and merge() charges the extra merge pass and its partial-output traffic.
+// Ties go to fewer splits.
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 #include "pdllm_internal.h"
@@ -25,7 +27,8 @@ namespace {
 constexpr double kFixedTiles = 2.0;        // c0: per-workgroup overhead in tile-times
 constexpr double kMergeBase = 1.0;         // merge launch + pass, in tile-times
 constexpr double kMergePerSplit = 0.25;    // partial write + read per split
-constexpr int kResidentBf16 = 2;           // decode workgroups per CU (bf16 kernel)
+constexpr int kResidentBf16Large = 1;      // 8-wave bf16 workgroups per CU
+constexpr int kResidentBf16Small = 2;      // 4-wave bf16 workgroups per CU
 constexpr int kResidentF32 = 4;
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -41,11 +44,9 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
     return false;
   }
   const int group = h_q / h_kv;
+  const int64_t q_rows = (int64_t)l_d * group;
   DecodePlan p;
   p.n_seq = n_seq;
-  p.q_rows_per_wg = dtype == 1 ? kDecodeRowsBf16 : kDecodeRowsF32;
-  const int64_t q_rows = (int64_t)l_d * group;
-  p.q_tiles = (int)((q_rows + p.q_rows_per_wg - 1) / p.q_rows_per_wg);
   p.k_s.resize(n_seq);
   p.n_kv.resize(n_seq);
   p.n_tiles.resize(n_seq);
@@ -65,12 +66,20 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
     p.n_tiles[s] = (int)((nkv + kDecodeTile - 1) / kDecodeTile);
     max_tiles = std::max(max_tiles, p.n_tiles[s]);
   }
-  const int64_t per_split_wg = (int64_t)h_kv * p.q_tiles;
-
   auto splits_for = [&](int s, int tps) { return (p.n_tiles[s] + tps - 1) / tps; };
+
+  // (query rows per workgroup, workgroups resident per CU) candidates
+  struct Shape { int rows, resident; };
+  const Shape bf16_shapes[2] = {{kDecodeRowsBf16Large, kResidentBf16Large},
+                                {kDecodeRowsBf16Small, kResidentBf16Small}};
+  const Shape f32_shapes[1] = {{kDecodeRowsF32, kResidentF32}};
+  const Shape* shapes = dtype == 1 ? bf16_shapes : f32_shapes;
+  const int n_shapes = dtype == 1 ? 2 : 1;
+
   p.splits.assign(n_seq, 1);
   p.tiles_per_split.assign(n_seq, 1);
   if (num_splits > 0) {
+    p.q_rows_per_wg = shapes[0].rows;
     for (int s = 0; s < n_seq; ++s) {
       const int want = std::min(num_splits, p.n_tiles[s]);
       const int tps = (p.n_tiles[s] + want - 1) / want;
@@ -78,31 +87,38 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
       p.splits[s] = splits_for(s, tps);
     }
   } else {
-    const double slots = (double)n_cu * (dtype == 1 ? kResidentBf16 : kResidentF32);
     double best = 1e300;
-    int best_tps = max_tiles;
-    for (int tps = max_tiles; tps >= 1; --tps) {
-      double work = 0.0, longest = 0.0;
-      int max_splits = 1;
-      for (int s = 0; s < n_seq; ++s) {
-        const int ns = splits_for(s, tps);
-        max_splits = std::max(max_splits, ns);
-        const int last = p.n_tiles[s] - (ns - 1) * tps;
-        work += per_split_wg * ((ns - 1) * (tps + kFixedTiles) + (last + kFixedTiles));
-        longest = std::max(longest, std::min(tps, p.n_tiles[s]) + kFixedTiles);
-      }
-      double t = std::max(work / slots, longest);
-      if (max_splits > 1) t += kMergeBase + kMergePerSplit * max_splits;
-      if (t < best - 1e-9) {      // strictly better: ties keep fewer splits
-        best = t;
-        best_tps = tps;
+    int best_tps = max_tiles, best_rows = shapes[0].rows;
+    for (int si = 0; si < n_shapes; ++si) {
+      const int64_t q_tiles = (q_rows + shapes[si].rows - 1) / shapes[si].rows;
+      const double slots = (double)n_cu * shapes[si].resident;
+      for (int tps = max_tiles; tps >= 1; --tps) {
+        int64_t n_wg = 0;
+        int max_splits = 1, longest = 1;
+        for (int s = 0; s < n_seq; ++s) {
+          const int ns = splits_for(s, tps);
+          max_splits = std::max(max_splits, ns);
+          longest = std::max(longest, std::min(tps, p.n_tiles[s]));
+          n_wg += (int64_t)h_kv * q_tiles * ns;
+        }
+        const double rounds = std::ceil((double)n_wg / slots);
+        double t = rounds * (longest + kFixedTiles);
+        if (max_splits > 1) t += kMergeBase + kMergePerSplit * max_splits;
+        if (t < best - 1e-9) {      // strictly better: ties keep fewer splits, larger tiles
+          best = t;
+          best_tps = tps;
+          best_rows = shapes[si].rows;
+        }
       }
     }
+    p.q_rows_per_wg = best_rows;
     for (int s = 0; s < n_seq; ++s) {
       p.tiles_per_split[s] = best_tps;
       p.splits[s] = splits_for(s, best_tps);
     }
   }
+  p.q_tiles = (int)((q_rows + p.q_rows_per_wg - 1) / p.q_rows_per_wg);
+  const int64_t per_split_wg = (int64_t)h_kv * p.q_tiles;
 
   p.part_off.assign(n_seq, 0);
   p.lse_off.assign(n_seq, 0);

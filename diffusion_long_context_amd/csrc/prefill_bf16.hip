@@ -14,11 +14,13 @@
 // into LDS once -- up to 288 rows x 128 d x 2 tensors, about 150 KiB of the
 // 160 KiB -- and every query row of the G grouped heads streams past it, so
 // HBM traffic is one read of Q and the pool slot and one write of O.
-// Wavefronts take 32-row blocks round-robin: chunk-row blocks run
-// S^T = K Q^T, an online softmax over 64-row kv steps and O^T += V^T P^T;
-// window-row blocks run S = Q K^T (which leaves each lane one key column),
-// an exact row softmax over all keys, and accumulate each key's weight in
-// registers.  Per-wave key sums meet in LDS and are added in wave order.
+// Wavefronts take 32-row blocks round-robin, with the next block's queries
+// loaded while the current one computes: chunk-row blocks run the shared
+// attention step (attn_tile.h) over 64-row kv steps; window-row blocks run
+// S = Q K^T (which leaves each lane one key column), an exact row softmax
+// over all keys, and accumulate each key's weight in registers.  Per-wave
+// key sums meet in LDS and are added in wave order.
+#include "attn_tile.h"
 #include "device_common.h"
 #include "pdllm_internal.h"
 
@@ -38,8 +40,11 @@ struct PSmem {
   uint16_t vt[D * VP];
 };
 
-template <int D>
+// NKB = 16-row kv blocks of the chunk padded to 32 rows (compile-time, so
+// every loop over keys is static).
+template <int D, int NKB>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillArgs a) {
+  static_assert(NKB % 2 == 0 && NKB <= kMaxKb, "kv blocks");
   __shared__ PSmem<D> sm;
   constexpr int KP = PSmem<D>::KP, VP = PSmem<D>::VP;
   constexpr int DC = D / 32, DB = D / 16;
@@ -49,8 +54,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int c = blockIdx.x / a.h_kv;
   const int g = blockIdx.x - c * a.h_kv;
   const int R = a.slot_rows;
-  const int rpad = (R + 31) & ~31;
-  const int nkb = rpad / 16;
+  constexpr int rpad = 16 * NKB;
   const int slot = a.chunk_slot[c];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lj = lane >> 4;
@@ -94,195 +98,157 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int n_cb = (n_rows_c + 31) / 32;
   const int n_rows_w = a.w * G;
   const int n_wb = (n_rows_w + 31) / 32;
-  const uint16_t* qc = static_cast<const uint16_t*>(a.q_chunk);
+  const int n_items = n_cb + n_wb;
+  const uint16_t* qc = static_cast<const uint16_t*>(a.q_chunk) + (int64_t)c * R * a.h_q * D;
   const uint16_t* qw = static_cast<const uint16_t*>(a.q_win) +
                        (int64_t)(c / a.chunks_per_win) * a.w * a.h_q * D;
-  uint16_t* oc = static_cast<uint16_t*>(a.o_chunk);
+  uint16_t* oc = static_cast<uint16_t*>(a.o_chunk) + (int64_t)c * R * a.h_q * D;
+  using Attn = WaveAttn<D, KP, VP>;
+  const uint16_t* k_lane = &sm.k[lr * KP + 8 * lj];
+  const uint16_t* v_lane = &sm.vt[lr * VP + 4 * lj];
 
-  float colsum[kMaxKb];                     // lane: key 16 kb + lr, summed over its rows
-#pragma unroll
-  for (int kb = 0; kb < kMaxKb; ++kb) colsum[kb] = 0.f;
-
-  auto load_q = [&](const uint16_t* base, int first, int n_rows, bf16x8 (&qf)[2][DC]) {
+  // query fragments of work item `it`: 32 chunk rows (it < n_cb) or 32 window rows
+  auto fetch = [&](int it, bf16x8 (&qf)[2][DC]) {
+    const bool win = it >= n_cb;
+    const uint16_t* base = win ? qw : qc;
+    const int first = (win ? it - n_cb : it) * 32;
+    const int n_rows = win ? n_rows_w : n_rows_c;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int x = first + 16 * b + lr;
       if (x < n_rows) {
         const int r = x / G, h = g * G + (x - r * G);
-        const uint16_t* p = base + ((int64_t)r * a.h_q + h) * D + 8 * lj;
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) qf[b][dc] = *reinterpret_cast<const bf16x8*>(p + 32 * dc);
+        load_q<DC>(qf[b], base + ((int64_t)r * a.h_q + h) * D + 8 * lj);
       } else {
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) qf[b][dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        zero_q<DC>(qf[b]);
       }
     }
   };
 
-  for (int item = wave; item < n_cb + n_wb; item += kWaves) {
-    bf16x8 qf[2][DC];
+  float colsum[NKB];                       // lane: key 16 kb + lr, summed over its window rows
+
+  // ---- one work item: 32 chunk rows (attention output) or 32 window rows
+  auto process = [&](int item, const bf16x8 (&qf)[2][DC]) {
+    __builtin_amdgcn_sched_barrier(0);     // keep items apart: no cross-item hoisting
     if (item < n_cb) {
-      // ================= chunk rows: attention output =================
-      const int first = item * 32;
-      load_q(qc + (int64_t)c * R * a.h_q * D, first, n_rows_c, qf);
-      f32x4 acc[DB][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-      auto step = [&](int kv0, auto nk_tag) {
-        constexpr int NK = decltype(nk_tag)::value;       // 16-row kv blocks in this step
-        f32x4 sc[NK][2];
-#pragma unroll
-        for (int kb = 0; kb < NK; ++kb) sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-          for (int kb = 0; kb < NK; ++kb) {
-            const bf16x8 ka =
-                *reinterpret_cast<const bf16x8*>(&sm.k[(kv0 + 16 * kb + lr) * KP + 32 * dc + 8 * lj]);
-            sc[kb][0] = mfma16x16x32(ka, qf[0][dc], sc[kb][0]);
-            sc[kb][1] = mfma16x16x32(ka, qf[1][dc], sc[kb][1]);
-          }
-        const bool tail = kv0 + 16 * NK > R;
-        bf16x8 pf[NK / 2][2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < NK; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float x = sc[kb][b][e] * sl2;
-              if (tail && kv0 + 16 * kb + 4 * lj + e >= R) x = -INFINITY;
-              sc[kb][b][e] = x;
-              mx = fmaxf(mx, x);
-            }
-          mx = wave_xor_max(mx, 16);
-          mx = wave_xor_max(mx, 32);
-          const float m_new = fmaxf(m_run[b], mx);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = exp2f(m_run[b] - m_use);
-          m_run[b] = m_new;
-          float psum = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < NK; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p = exp2f(sc[kb][b][e] - m_use);
-              sc[kb][b][e] = p;
-              psum += p;
-            }
-          l_run[b] = l_run[b] * alpha + psum;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db][b] *= alpha;
-#pragma unroll
-          for (int kc = 0; kc < NK / 2; ++kc)
-            pf[kc][b] = bf16x8{(__bf16)sc[2 * kc][b][0], (__bf16)sc[2 * kc][b][1],
-                               (__bf16)sc[2 * kc][b][2], (__bf16)sc[2 * kc][b][3],
-                               (__bf16)sc[2 * kc + 1][b][0], (__bf16)sc[2 * kc + 1][b][1],
-                               (__bf16)sc[2 * kc + 1][b][2], (__bf16)sc[2 * kc + 1][b][3]};
-        }
-#pragma unroll
-        for (int kc = 0; kc < NK / 2; ++kc)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const uint16_t* vp = &sm.vt[(16 * db + lr) * VP + kv0 + 32 * kc + 4 * lj];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            acc[db][0] = mfma16x16x32(va, pf[kc][0], acc[db][0]);
-            acc[db][1] = mfma16x16x32(va, pf[kc][1], acc[db][1]);
-          }
-      };
-      int kv0 = 0;
-      for (; kv0 + 64 <= rpad; kv0 += 64) step(kv0, std::integral_constant<int, 4>{});
-      if (kv0 < rpad) step(kv0, std::integral_constant<int, 2>{});
-
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float l = l_run[b];
-        l = wave_xor_sum(l, 16);
-        l = wave_xor_sum(l, 32);
-        const int x = first + 16 * b + lr;
-        if (x >= n_rows_c) continue;
-        const int r = x / G, h = g * G + (x - r * G);
-        const float inv = 1.f / l;
-        uint16_t* op = oc + (((int64_t)c * R + r) * a.h_q + h) * D + 4 * lj;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const f32x4 v = acc[db][b] * inv;
-          *reinterpret_cast<u32x2*>(op + 16 * db) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      Attn at;
+      at.init();
+      // 64-row steps; a last 32-row remainder runs as a step over the final
+      // 64 rows with the first 32 masked (they were already attended)
+      if constexpr (NKB < 4) {
+        at.template step<NKB>(k_lane, v_lane, qf, sl2, R, lj);
+      } else {
+        constexpr int n_steps = (NKB + 3) / 4;
+#pragma unroll 1
+        for (int st = 0; st < n_steps; ++st) {
+          const int kv0 = st * 64 + 64 > rpad ? rpad - 64 : st * 64;
+          at.template step<4>(k_lane + kv0 * KP, v_lane + kv0, qf, sl2, R - kv0, lj, st * 64 - kv0);
         }
       }
-    } else {
-      // ================= window rows: per-key weight =================
-      const int first = (item - n_cb) * 32;
-      load_q(qw, first, n_rows_w, qf);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        f32x4 sw[kMaxKb];
+        const int x = item * 32 + 16 * b + lr;
+        if (x >= n_rows_c) continue;
+        const int r = x / G, h = g * G + (x - r * G);
+        store_o_bf16<DB>(oc + ((int64_t)r * a.h_q + h) * D + 4 * lj, at.acc, b, 1.f / at.row_sum(b));
+      }
+    } else {
+      // S = Q K^T leaves lane (lr, lj) the keys 16 kb + lr of rows 4 lj + e, so
+      // each key's weight accumulates in registers with no per-block shuffles.
+      const int first = (item - n_cb) * 32;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int kb = 0; kb < kMaxKb; ++kb) {
-          sw[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (kb < nkb) {
+      for (int b = 0; b < 2; ++b) {
+        f32x4 sw[NKB];
+        // key blocks in pairs; the scheduling barrier keeps at most one pair's
+        // K fragments in registers
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-              const bf16x8 kf =
-                  *reinterpret_cast<const bf16x8*>(&sm.k[(16 * kb + lr) * KP + 32 * dc + 8 * lj]);
-              sw[kb] = mfma16x16x32(qf[b][dc], kf, sw[kb]);     // S[q = 4 lj + e][key = 16 kb + lr]
-            }
+        for (int kb = 0; kb < NKB; kb += 2) {
+          bf16x8 kf[2][DC];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc)
+              kf[u][dc] = *reinterpret_cast<const bf16x8*>(k_lane + 16 * (kb + u) * KP + 32 * dc);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            sw[kb + u] = mfma16x16x32(qf[b][0], kf[u][0], zero);
+#pragma unroll
+            for (int dc = 1; dc < DC; ++dc) sw[kb + u] = mfma16x16x32(qf[b][dc], kf[u][dc], sw[kb + u]);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // keys past R: only the last two blocks can hold any
+#pragma unroll
+        for (int kb = NKB - 2; kb < NKB; ++kb)
+          if (16 * kb + lr >= R) sw[kb] = ninf;
         float mx[4], sum[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx[e] = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kMaxKb; ++kb) {
-          const bool live = kb < nkb && 16 * kb + lr < R;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = live ? sw[kb][e] * sl2 : -INFINITY;
-            sw[kb][e] = x;
-            mx[e] = fmaxf(mx[e], x);
-          }
-        }
-#pragma unroll
         for (int e = 0; e < 4; ++e) {
-          mx[e] = wave_xor_max(mx[e], 1);
-          mx[e] = wave_xor_max(mx[e], 2);
-          mx[e] = wave_xor_max(mx[e], 4);
-          mx[e] = wave_xor_max(mx[e], 8);
+          float m = fmaxf(sw[0][e], sw[1][e]);
+#pragma unroll
+          for (int kb = 2; kb < NKB; kb += 2) m = fmaxf(fmaxf(m, sw[kb][e]), sw[kb + 1][e]);
+          m = wave_xor_max(m, 1);
+          m = wave_xor_max(m, 2);
+          m = wave_xor_max(m, 4);
+          m = wave_xor_max(m, 8);
+          mx[e] = -m * sl2;
           sum[e] = 0.f;
         }
 #pragma unroll
-        for (int kb = 0; kb < kMaxKb; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = exp2f(sw[kb][e] - mx[e]);
+            const float p = __builtin_amdgcn_exp2f(fmaf(sw[kb][e], sl2, mx[e]));
             sw[kb][e] = p;
             sum[e] += p;
           }
         float wgt[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sum[e] = wave_xor_sum(sum[e], 1);
-          sum[e] = wave_xor_sum(sum[e], 2);
-          sum[e] = wave_xor_sum(sum[e], 4);
-          sum[e] = wave_xor_sum(sum[e], 8);
-          const bool valid = first + 16 * b + 4 * lj + e < n_rows_w;
-          wgt[e] = valid ? 1.f / sum[e] : 0.f;
+          float t = sum[e];
+          t = wave_xor_sum(t, 1);
+          t = wave_xor_sum(t, 2);
+          t = wave_xor_sum(t, 4);
+          t = wave_xor_sum(t, 8);
+          wgt[e] = first + 16 * b + 4 * lj + e < n_rows_w ? 1.f / t : 0.f;
         }
 #pragma unroll
-        for (int kb = 0; kb < kMaxKb; ++kb)
-          colsum[kb] += sw[kb][0] * wgt[0] + sw[kb][1] * wgt[1] + sw[kb][2] * wgt[2] + sw[kb][3] * wgt[3];
+        for (int kb = 0; kb < NKB; ++kb)
+          colsum[kb] = fmaf(sw[kb][3], wgt[3], fmaf(sw[kb][2], wgt[2], fmaf(sw[kb][1], wgt[1],
+                            fmaf(sw[kb][0], wgt[0], colsum[kb]))));
       }
     }
+  };
+
+  // ---- phase 1: chunk-row items (round-robin over waves), unrolled twice
+  // over two query register sets so the next item's queries load while the
+  // current item computes
+  {
+    bf16x8 qa[2][DC], qb[2][DC];
+    if (wave < n_cb) fetch(wave, qa);
+    for (int item = wave; item < n_cb; item += 2 * kWaves) {
+      if (item + kWaves < n_cb) fetch(item + kWaves, qb);
+      process(item, qa);
+      if (item + kWaves >= n_cb) break;
+      if (item + 2 * kWaves < n_cb) fetch(item + 2 * kWaves, qa);
+      process(item + kWaves, qb);
+    }
+  }
+  // ---- phase 2: window-row items, continuing the round-robin numbering so
+  // waves with fewer chunk items take window items first
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) colsum[kb] = 0.f;
+  for (int item = n_cb + ((wave - n_cb) % kWaves + kWaves) % kWaves; item < n_items; item += kWaves) {
+    bf16x8 qf[2][DC];
+    fetch(item, qf);
+    process(item, qf);
   }
 
   // ---- per-key sums: across the 4 lane groups, then across waves in order
 #pragma unroll
-  for (int kb = 0; kb < kMaxKb; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     colsum[kb] = wave_xor_sum(colsum[kb], 16);
     colsum[kb] = wave_xor_sum(colsum[kb], 32);
   }
@@ -290,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   float* red = reinterpret_cast<float*>(sm.k);
   if (lj == 0) {
 #pragma unroll
-    for (int kb = 0; kb < kMaxKb; ++kb) red[wave * kMaxRows + 16 * kb + lr] = colsum[kb];
+    for (int kb = 0; kb < NKB; ++kb) red[wave * kMaxRows + 16 * kb + lr] = colsum[kb];
   }
   __syncthreads();
   float* part = a.part_score + ((int64_t)c * a.h_kv + g) * R;
@@ -313,18 +279,32 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(const float* part, 
   key_score[idx] = s;
 }
 
+template <int D>
+int prefill_launch(const PrefillArgs& a, void* stream) {
+  const dim3 grid(a.n_chunks * a.h_kv), block(kThreads);
+  const hipStream_t st = (hipStream_t)stream;
+  switch ((a.slot_rows + 31) / 32) {
+    case 1: hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_bf16_kernel<D, 4>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((prefill_bf16_kernel<D, 6>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_bf16_kernel<D, 8>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((prefill_bf16_kernel<D, 10>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((prefill_bf16_kernel<D, 12>), grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((prefill_bf16_kernel<D, 14>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_bf16_kernel<D, 16>), grid, block, 0, st, a); break;
+    case 9: hipLaunchKernelGGL((prefill_bf16_kernel<D, 18>), grid, block, 0, st, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
 }  // namespace
 
 int launch_prefill_bf16(const PrefillArgs& a, int d, void* stream) {
   if (a.n_chunks == 0) return (int)hipSuccess;
-  const dim3 grid(a.n_chunks * a.h_kv), block(kThreads);
-  if (d == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, (hipStream_t)stream, a);
-  else if (d == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, (hipStream_t)stream, a);
-  else
-    return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  if (d == 128) return prefill_launch<128>(a, stream);
+  if (d == 64) return prefill_launch<64>(a, stream);
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_score_finalize(const PrefillArgs& a, void* stream) {

@@ -126,8 +126,9 @@ size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slo
  *              (the window rows' softmax runs over the chunk's own rows only)
  *   chunk_slot device [n_chunks]
  *   workspace  device, >= pdllm_prefill_score_workspace(n_chunks, h_kv, slot_rows)
- * Supported: f32 with d <= 128 (d % 4 == 0); bf16 with d in {64, 128} and
- * slot_rows <= 257 (the chunk's K and V are held on chip).
+ * Supported: f32 with d in {16, 32, 64, 128} and slot_rows <= 4097; bf16
+ * with d in {64, 128} and slot_rows <= 257 (the chunk's K and V are held on
+ * chip).
  * The per-key sums are reduced in a fixed order: results are bitwise
  * reproducible run to run.
  */
@@ -177,12 +178,15 @@ pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t 
  * num_splits > 0 forces that many splits per sequence (capped at the
  * sequence's tile count).
  *   splits_per_seq  host [n_seq] out   tiles_per_split host [n_seq] out
+ *   q_rows_per_wg   host out: query rows (token x grouped head) per workgroup
  *   workspace_bytes host out: the workspace the call needs
+ * Any output pointer may be NULL.
  */
 pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t b, int32_t l_d,
                                int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
                                int32_t num_splits, int32_t n_cu, int32_t* splits_per_seq,
-                               int32_t* tiles_per_split, int64_t* workspace_bytes);
+                               int32_t* tiles_per_split, int32_t* q_rows_per_wg,
+                               int64_t* workspace_bytes);
 
 /* Bytes of workspace pdllm_split_attn_decode needs on the current device
  * (0 when the arguments are invalid).  Host function; queries the device's
@@ -211,7 +215,7 @@ size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_pag
  *   workspace device, >= pdllm_split_attn_decode_workspace(...) for the same
  *            arguments (holds per-split partial outputs, float32)
  * The result does not depend on num_splits beyond float32 rounding.
- * Supported: f32 with d <= 128 (d % 4 == 0); bf16 with d in {64, 128}.
+ * Supported: f32 with d in {16, 32, 64, 128}; bf16 with d in {64, 128}.
  */
 pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
                                      const void* q, const void* k_resp, const void* v_resp,

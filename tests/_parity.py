@@ -4,7 +4,11 @@ error metrics, and the tolerances every comparison uses.
 Tolerances:
   bf16 outputs       rel-L2 <= 5e-3 and max-abs <= 2e-2 over the tensor
   f32 outputs        rel-L2 <= 1e-5 and max-abs <= 1e-5
-  lse                max-abs <= 1e-3 (bf16 inputs), 1e-5 (f32 inputs)
+  lse                max-abs <= 2e-3 (bf16 inputs), 1e-5 (f32 inputs).  The bf16
+                     kernels normalise with the row sum of the bf16-rounded
+                     probabilities they feed to the PV product; rounding each p
+                     to bf16 moves that sum by at most a factor (1 +- 2^-9), so
+                     |d lse| <= ln(1 + 2^-9) = 1.95e-3.
   key_score          rel-L2 <= 1e-4 (bf16 inputs), 1e-6 (f32 inputs)
   selected indices   bit-exact
 """
@@ -14,7 +18,7 @@ import numpy as np
 import torch
 
 TOL = {
-    "bf16": dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3, score_rel_l2=1e-4),
+    "bf16": dict(rel_l2=5e-3, max_abs=2e-2, lse=2e-3, score_rel_l2=1e-4),
     "f32": dict(rel_l2=1e-5, max_abs=1e-5, lse=1e-5, score_rel_l2=1e-6),
 }
 
