@@ -2,20 +2,25 @@
 // to a block of kv rows whose K (row-major) and V (transposed) sit in LDS.
 // Shared by the split-KV decode kernel and the chunk prefill kernel.
 //
-// Layout (v_mfma_f32_16x16x32_bf16; lane = 16 lj + lr):
-//   S^T = K Q^T : lane holds S^T[kv = 16 kb + 4 lj + e][q = 16 b + lr]
-//   O^T += V^T P^T : lane holds O^T[d = 16 db + 4 lj + e][q = 16 b + lr]
-// so every lane owns whole query columns and the probabilities it computes
-// are directly the PV product's B operand.  For a 32-row kv chunk kc the B
-// operand's elements 0..3 are kv 32 kc + 4 lj + e and 4..7 are
-// kv 32 kc + 16 + 4 lj + e; the V^T A operand is read in the same order.
+// The contractions run on v_mfma_f32_32x32x16_bf16 (the 16x16x32 variant
+// reaches only about half the dense bf16 rate on this chip).  Lane l = 32 j + c
+// (c = l % 32, j = l / 32):
+//   S^T = K Q^T : lane holds S^T[kv = 32 kb + 8 m + 4 j + t][q = c], i = 4 m + t
+//   O^T += V^T P^T : lane holds O^T[d = 32 db + 8 m + 4 j + t][q = c]
+// so every lane owns one query column; the row max needs one exchange with
+// lane l ^ 32.  For the 16-row kv chunk h of block kb, the PV B operand is the
+// lane's accumulator registers 8 h .. 8 h + 7 (kv 32 kb + 16 h + 8 u + 4 j + t,
+// element 4 u + t).  V stays row-major in LDS like K; its A operand (V^T rows)
+// comes from two ds_read_b64_tr_b16: inside each 16-lane group, lane 4 a + b
+// receives element e of the 8-byte row addressed by lane a + 4 e (offset b),
+// so lane s = a + 4 e of group g points at kv row 4 j + e (+ 8 for the second
+// read) and d column 16 (g % 2) + 4 a (see v_lane_offset).
 //
 // Online softmax in base 2 (scale * log2 e folded into one FMA before
-// v_exp_f32).  A row's reference max only moves when a block's max exceeds
-// it by more than 2^kRescaleLog2, so the accumulators are rescaled rarely and
-// probabilities stay below 2^8.  The row sums come from the PV MFMA with an
-// all-ones A operand, i.e. they are sums of the same bf16 probabilities the
-// PV product uses.
+// v_exp_f32).  A row's reference max only moves when a block's max exceeds it
+// by more than 2^kRescaleLog2, so the accumulators are rescaled rarely and
+// probabilities stay below 2^8.  Row sums are float32 sums of the unrounded
+// probabilities.
 #pragma once
 
 #include "device_common.h"
@@ -24,141 +29,165 @@ namespace pdllm {
 
 constexpr float kRescaleLog2 = 8.0f;
 
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on one wavefront: lane l
+// supplies A row l % 32 and B column l % 32 with the eight k values
+// 8 (l / 32) .. 8 (l / 32) + 7, and receives D column l % 32, rows
+// 8 (i / 4) + 4 (l / 32) + i % 4 for i = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value of lane l ^ 32.
+__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Lane offset (elements) into a row-major V tile of pitch VP for the
+// transposing reads: kv row 4 j + e and d column 16 (g % 2) + 4 a, where
+// lane = 16 g + a + 4 e and j = lane / 32.
+__device__ __forceinline__ int v_lane_offset(int lane, int vp) {
+  const int s = lane & 15, g = lane >> 4;
+  return (4 * (lane >> 5) + (s >> 2)) * vp + 16 * (g & 1) + 4 * (s & 3);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) s16x4*)(p)));
+}
 
 template <int D, int KP, int VP>
 struct WaveAttn {
-  static constexpr int DC = D / 32;   // 32-wide d chunks of QK^T
-  static constexpr int DB = D / 16;   // 16-row d blocks of O^T
+  static constexpr int DC = D / 16;   // 16-wide d chunks of QK^T
+  static constexpr int DB = D / 32;   // 32-row d blocks of O^T
 
-  f32x4 acc[DB][2];
-  f32x4 lacc[2];
-  float m_run[2];
+  f32x16 acc[DB];
+  float l_run;                        // this lane's partial row sum (its kv half)
+  float m_run;                        // reference max (log2 units, scaled)
 
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lacc[0] = lacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[0] = m_run[1] = -INFINITY;
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    l_run = 0.f;
+    m_run = -INFINITY;
   }
 
-  // Attend to kv rows [0, 16 NK) of an LDS block; only rows in
+  // Attend to kv rows [0, 32 NK) of an LDS block; only rows in
   // [valid_lo, valid_hi) count, the rest are masked (a wave-uniform branch,
-  // taken only by a partial block).  k_lane = &K[lr][8 lj] (pitch KP) and vt_lane = &V^T[lr][4 lj]
-  // (pitch VP) are the lane's base addresses, so every fragment read below is
-  // the base plus a compile-time offset.
+  // taken only by a partial block).  k_lane = &K[c][8 j] (pitch KP) and
+  // v_lane = V + v_lane_offset(lane, VP) (row-major V, pitch VP) are the
+  // lane's base addresses, so every fragment read below is the base plus a
+  // compile-time offset.
   template <int NK>
   __device__ __forceinline__ void step(const uint16_t* __restrict__ k_lane,
-                                       const uint16_t* __restrict__ vt_lane,
-                                       const bf16x8 (&qf)[2][DC], float sl2, int valid_hi, int lj,
-                                       int valid_lo = 0) {
-    static_assert(NK % 2 == 0, "kv blocks come in 32-row pairs");
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 sc[NK][2];
-    __builtin_amdgcn_s_setprio(1);          // MFMA phases win issue over softmax phases
+                                       const uint16_t* __restrict__ v_lane, const bf16x8 (&qf)[DC],
+                                       float sl2, int valid_hi, int j, int valid_lo = 0) {
+    f32x16 sc[NK];
 #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lane + 16 * kb * KP);
-      sc[kb][0] = mfma16x16x32(ka, qf[0][0], zero);
-      sc[kb][1] = mfma16x16x32(ka, qf[1][0], zero);
-    }
+    for (int kb = 0; kb < NK; ++kb)
+      sc[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(k_lane + 32 * kb * KP), qf[0], f32x16{});
 #pragma unroll
-    for (int dc = 1; dc < DC; ++dc) {
+    for (int dc = 1; dc < DC; ++dc)
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lane + 16 * kb * KP + 32 * dc);
-        sc[kb][0] = mfma16x16x32(ka, qf[0][dc], sc[kb][0]);
-        sc[kb][1] = mfma16x16x32(ka, qf[1][dc], sc[kb][1]);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if (valid_hi < 16 * NK || valid_lo > 0) {
+      for (int kb = 0; kb < NK; ++kb)
+        sc[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(k_lane + 32 * kb * KP + 16 * dc), qf[dc], sc[kb]);
+    if (__builtin_expect(valid_hi < 32 * NK || valid_lo > 0, 0)) {
+      // rows r valid iff valid_lo <= r < valid_hi, as one unsigned compare
+      const unsigned span = (unsigned)(valid_hi - valid_lo);
 #pragma unroll
       for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * kb + 4 * lj + e;
-          if (r >= valid_hi || r < valid_lo) sc[kb][0][e] = sc[kb][1][e] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int r = 32 * kb + 8 * (i >> 2) + 4 * j + (i & 3);
+          if ((unsigned)(r - valid_lo) >= span) sc[kb][i] = -INFINITY;
         }
     }
-    bf16x8 pf[NK / 2][2];
+    float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = fmaxf(fmaxf(sc[0][b][0], sc[0][b][1]), fmaxf(sc[0][b][2], sc[0][b][3]));
+    for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-      for (int kb = 1; kb < NK; ++kb) {
-        mx = fmaxf(fmaxf(mx, sc[kb][b][0]), sc[kb][b][1]);
-        mx = fmaxf(fmaxf(mx, sc[kb][b][2]), sc[kb][b][3]);
-      }
-      mx = wave_xor_max(mx, 16);
-      mx = wave_xor_max(mx, 32);
-      const float ms = mx * sl2;
-      const bool need = ms > m_run[b] + kRescaleLog2;
-      if (__ballot(need)) {
-        const float m_new = need ? ms : m_run[b];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
-        m_run[b] = m_new;
+      for (int i = kb ? 0 : 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[kb][i]), sc[kb][i + 1]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float ms = mx * sl2;
+    const bool need = ms > m_run + kRescaleLog2;
+    if (__ballot(need)) {
+      const float m_new = need ? ms : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][b] *= alpha;
-        lacc[b] *= alpha;
-      }
-      const float neg_m = -m_run[b];
-#pragma unroll
-      for (int kb = 0; kb < NK; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[kb][b][e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][b][e], sl2, neg_m));
-#pragma unroll
-      for (int kc = 0; kc < NK / 2; ++kc)
-        pf[kc][b] = bf16x8{(__bf16)sc[2 * kc][b][0], (__bf16)sc[2 * kc][b][1],
-                           (__bf16)sc[2 * kc][b][2], (__bf16)sc[2 * kc][b][3],
-                           (__bf16)sc[2 * kc + 1][b][0], (__bf16)sc[2 * kc + 1][b][1],
-                           (__bf16)sc[2 * kc + 1][b][2], (__bf16)sc[2 * kc + 1][b][3]};
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      l_run *= alpha;
     }
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-    __builtin_amdgcn_s_setprio(1);
+    const float neg_m = -m_run;
+    float ps = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < NK / 2; ++kc) {
+    for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vp = vt_lane + 16 * db * VP + 32 * kc;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        acc[db][0] = mfma16x16x32(va, pf[kc][0], acc[db][0]);
-        acc[db][1] = mfma16x16x32(va, pf[kc][1], acc[db][1]);
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, neg_m));
+        sc[kb][i] = p;
+        ps += p;
       }
-      lacc[0] = mfma16x16x32(ones, pf[kc][0], lacc[0]);
-      lacc[1] = mfma16x16x32(ones, pf[kc][1], lacc[1]);
+    l_run += ps;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 pf = bf16x8{(__bf16)sc[kb][8 * h + 0], (__bf16)sc[kb][8 * h + 1],
+                                 (__bf16)sc[kb][8 * h + 2], (__bf16)sc[kb][8 * h + 3],
+                                 (__bf16)sc[kb][8 * h + 4], (__bf16)sc[kb][8 * h + 5],
+                                 (__bf16)sc[kb][8 * h + 6], (__bf16)sc[kb][8 * h + 7]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint16_t* vp = v_lane + (32 * kb + 16 * h) * VP + 32 * db;
+          const bf16x4 lo = lds_read_tr16(vp);
+          const bf16x4 hi = lds_read_tr16(vp + 8 * VP);
+          const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[db] = mfma32x32x16(va, pf, acc[db]);
+        }
+      }
     }
-    __builtin_amdgcn_s_setprio(0);
   }
 
-  // Row sum and natural-log normaliser of column block b.
-  __device__ __forceinline__ float row_sum(int b) const { return lacc[b][0]; }
-  __device__ __forceinline__ float lse(int b) const { return m_run[b] * kLn2 + logf(lacc[b][0]); }
+  // Full row sum (both kv halves) and natural-log normaliser.
+  __device__ __forceinline__ float row_sum() const { return l_run + swap_halves(l_run); }
+  __device__ __forceinline__ float lse(float l) const { return m_run * kLn2 + logf(l); }
 };
 
-// Query fragments (B operand of S^T): lane column lr of block b, d = 32 dc + 8 lj ...
+// Query fragments (B operand of S^T): lane column c, d = 16 dc + 8 j ...
 template <int DC>
 __device__ __forceinline__ void zero_q(bf16x8 (&qf)[DC]) {
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) qf[dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
 }
 
-template <int DC>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[DC], const uint16_t* row_plus_8lj) {
+template <int DC, int STRIDE>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[DC], const uint16_t* row_plus_8j) {
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(row_plus_8lj + 32 * dc);
+  for (int dc = 0; dc < DC; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(row_plus_8j + STRIDE * dc);
 }
 
-// Store a wavefront's O^T column (query column lr of block b) as 4 bf16 per d block.
+// Store a wavefront's O^T column (query column c) with 4 consecutive d per
+// accumulator group: row_plus_4j = &O[row][4 j].
 template <int DB>
-__device__ __forceinline__ void store_o_bf16(uint16_t* row_plus_4lj, const f32x4 (&acc)[DB][2], int b,
-                                             float inv) {
+__device__ __forceinline__ void store_o_bf16(uint16_t* row_plus_4j, const f32x16 (&acc)[DB], float inv) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const f32x4 x = acc[db][b] * inv;
-    *reinterpret_cast<u32x2*>(row_plus_4lj + 16 * db) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-  }
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float x0 = acc[db][4 * m] * inv, x1 = acc[db][4 * m + 1] * inv;
+      const float x2 = acc[db][4 * m + 2] * inv, x3 = acc[db][4 * m + 3] * inv;
+      *reinterpret_cast<u32x2*>(row_plus_4j + 32 * db + 8 * m) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+    }
+}
+
+template <int DB>
+__device__ __forceinline__ void store_o_f32(float* row_plus_4j, const f32x16 (&acc)[DB], float inv) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<f32x4*>(row_plus_4j + 32 * db + 8 * m) =
+          f32x4{acc[db][4 * m], acc[db][4 * m + 1], acc[db][4 * m + 2], acc[db][4 * m + 3]} * inv;
 }
 
 }  // namespace pdllm

@@ -13,17 +13,17 @@
 // * Query rows of one kv head are packed as (token, grouped head) pairs, so
 //   the G = h_q / h_kv heads sharing a kv head make the contraction dense.
 // * Each wavefront owns 32 query rows; S^T = K Q^T and O^T += V^T P^T run on
-//   v_mfma_f32_16x16x32_bf16.  Computing S transposed leaves each lane with
-//   the probabilities of one query column, which feed the PV product as its
-//   B operand directly (no shuffle through LDS).
+//   v_mfma_f32_32x32x16_bf16 (attn_tile.h).  Computing S transposed leaves
+//   each lane with the probabilities of one query column, which feed the PV
+//   product as its B operand directly (no shuffle through LDS).
 // * K/V tiles are gathered straight from pool slots into LDS through a
-//   per-workgroup row-offset table (no gather-to-contiguous copy); V is stored
-//   transposed so the PV A operand is two 8-byte LDS reads.  Tiles are
+//   per-workgroup row-pointer table (no gather-to-contiguous copy); K and V
+//   are stored row-major and the PV A operand is read with gfx950's
+//   transposing LDS load (ds_read_b64_tr_b16).  Tiles are
 //   double-buffered in LDS (one barrier per tile); the global loads of tile
 //   t+2 are in flight while tile t computes.
 // * Online softmax in base 2: the scale and log2(e) fold into one FMA before
-//   v_exp_f32, the running max moves lazily (see kRescaleLog2), and the row
-//   sums come out of the PV MFMA with an all-ones operand.
+//   v_exp_f32 and the running max moves lazily (see kRescaleLog2).
 #include "attn_tile.h"
 #include "device_common.h"
 #include "pdllm_internal.h"
@@ -36,10 +36,10 @@ constexpr int kTableTiles = 8;             // row-pointer table capacity (tiles)
 
 template <int D>
 struct Smem {
-  static constexpr int KP = D + 8;         // K tile pitch (elements): 16-row reads conflict-free
-  static constexpr int VP = kTile + 4;     // V^T pitch (elements): 16 d-rows hit distinct banks
-  uint16_t k[2][kTile * KP];               // double-buffered tiles
-  uint16_t vt[2][D * VP];
+  static constexpr int KP = D + 8;         // K pitch (elements): 8-row 16-byte reads conflict-free
+  static constexpr int VP = D + 16;        // V pitch (elements): transposing reads conflict-free
+  uint16_t k[2][kTile * KP];               // double-buffered tiles, both row-major
+  uint16_t v[2][kTile * VP];
   gptr16 kptr[kTableTiles * kTile];        // K / V address of each attended row
   gptr16 vptr[kTableTiles * kTile];
 };
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const int t_end = min(t_begin + tps, n_tiles);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lj = lane >> 4;
+  const int lc = lane & 31, lj = lane >> 5;     // query column, kv / d half
   const int G = a.group;
   const int rows_total = a.l_d * G;
   const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k);
@@ -119,19 +119,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   int tw = t_begin;
   build_table(tw);
 
-  // ---- queries: B-operand fragments of S^T (lane: query column lr, d = 32 dc + 8 lj ..)
-  bf16x8 qf[2][DC];
-  int qrow[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int r = qt * kRows + wave * 32 + 16 * b + lr;
-    qrow[b] = r;
-    if (r < rows_total) {
-      const int i = r / G, h = g * G + (r - i * G);
-      load_q<DC>(qf[b], static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
-    } else {
-      zero_q<DC>(qf[b]);
-    }
+  // ---- queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc + 8 lj ..)
+  bf16x8 qf[DC];
+  const int qrow = qt * kRows + wave * 32 + lc;
+  if (qrow < rows_total) {
+    const int i = qrow / G, h = g * G + (qrow - i * G);
+    load_q<DC, 16>(qf, static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
+  } else {
+    zero_q<DC>(qf);
   }
 
   // ---- tile loader: thread owns RPT consecutive kv rows x 8 d values
@@ -148,30 +143,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
+    for (int i = 0; i < RPT; ++i) {
       *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      uint16_t* dst = &sm.vt[buf][(ld_d0 + e) * VP + ld_r0];
-      if constexpr (RPT == 4) {
-        const uint32_t lo = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
-        const uint32_t hi = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-      } else if constexpr (RPT == 2) {
-        *reinterpret_cast<uint32_t*>(dst) =
-            ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
-      } else {
-        *dst = (uint16_t)((vreg[0][w] >> sh) & 0xffffu);
-      }
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[i];
     }
   };
 
   Attn at;
   at.init();
   const float sl2 = a.scale_log2;
-  const int k_lane = lr * KP + 8 * lj;      // lane offsets inside one LDS buffer
-  const int v_lane = lr * VP + 4 * lj;
+  const int k_lane = lc * KP + 8 * lj;      // lane offsets inside one LDS buffer
+  const int v_lane = v_lane_offset(lane, VP);
 
   // ---- main loop: tile t computes from LDS buffer (t - t_begin) & 1 while
   // tile t+1 is stored into the other buffer and tile t+2 is being loaded;
@@ -184,8 +166,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = (t - t_begin) & 1;
     const uint16_t* kb = &sm.k[0][0] + buf * (kTile * KP) + k_lane;
-    const uint16_t* vb = &sm.vt[0][0] + buf * (D * VP) + v_lane;
-    at.template step<4>(kb, vb, qf, sl2, n_kv - t * kTile, lj);
+    const uint16_t* vb = &sm.v[0][0] + buf * (kTile * VP) + v_lane;
+    at.template step<kTile / 32>(kb, vb, qf, sl2, n_kv - t * kTile, lj);
     if (t + 1 < t_end) {
       store_tile(buf ^ 1);                 // that buffer was last read by tile t-1
       if (t + 2 < t_end) {
@@ -201,22 +183,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     __syncthreads();
   }
 
-  // ---- epilogue
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int r = qrow[b];
-    if (r >= rows_total) continue;
-    const int i = r / G, h = g * G + (r - i * G);
-    const float inv = 1.f / at.row_sum(b);
-    const float lse_v = at.lse(b);
+  // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
+  const float l = at.row_sum();
+  if (qrow < rows_total) {
+    const int i = qrow / G, h = g * G + (qrow - i * G);
+    const float inv = 1.f / l;
+    const float lse_v = at.lse(l);
     if (n_splits == 1) {
       store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 4 * lj,
-                       at.acc, b, inv);
+                       at.acc, inv);
       if (a.lse != nullptr && lj == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
     } else {
-      float* pp = a.part_o + a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 4 * lj;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + 16 * db) = at.acc[db][b] * inv;
+      store_o_f32<DB>(a.part_o + a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 4 * lj,
+                      at.acc, inv);
       if (lj == 0) a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;
     }
   }

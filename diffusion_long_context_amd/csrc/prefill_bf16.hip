@@ -10,16 +10,17 @@
 // and the finalize kernel sums part over g in a fixed order into key_score.
 //
 // Design for CDNA4: one workgroup of 8 wavefronts per (chunk, kv head).  The
-// chunk's whole K (row-major) and V (transposed) for that kv head are staged
-// into LDS once -- up to 288 rows x 128 d x 2 tensors, about 150 KiB of the
-// 160 KiB -- and every query row of the G grouped heads streams past it, so
+// chunk's whole K and V (both row-major) for that kv head are staged into LDS
+// once -- up to 288 rows x 128 d x 2 tensors, about 158 KiB of the 160 KiB --
+// and every query row of the G grouped heads streams past it, so
 // HBM traffic is one read of Q and the pool slot and one write of O.
 // Wavefronts take 32-row blocks round-robin, with the next block's queries
 // loaded while the current one computes: chunk-row blocks run the shared
-// attention step (attn_tile.h) over 64-row kv steps; window-row blocks run
-// S = Q K^T (which leaves each lane one key column), an exact row softmax
-// over all keys, and accumulate each key's weight in registers.  Per-wave
-// key sums meet in LDS and are added in wave order.
+// attention step (attn_tile.h, 32x32x16 MFMA) over 64-row kv steps;
+// window-row blocks run S = Q K^T on the 16x16x32 MFMA (which leaves each
+// lane one key column), an exact row softmax over all keys, and accumulate
+// each key's weight in registers.  Per-wave key sums meet in LDS and are
+// added in wave order.
 #include "attn_tile.h"
 #include "device_common.h"
 #include "pdllm_internal.h"
@@ -34,10 +35,11 @@ constexpr int kMaxKb = kMaxRows / 16;      // 16-row kv blocks
 
 template <int D>
 struct PSmem {
-  static constexpr int KP = D + 8;          // K pitch (elements)
-  static constexpr int VP = kMaxRows + 4;   // V^T pitch: 292 = 4 mod 8 -> conflict-free 16-row reads
-  uint16_t k[kMaxRows * KP];
-  uint16_t vt[D * VP];
+  static constexpr int KP = D + 8;          // K pitch (elements): 8-row 16-byte reads conflict-free
+  static constexpr int VP = D + 16;         // V pitch (elements): transposing reads conflict-free
+  uint16_t k[kMaxRows * KP];                // both row-major
+  uint16_t v[kMaxRows * VP];
+  int next_item;                            // dynamic hand-out of chunk-row items
 };
 
 // NKB = 16-row kv blocks of the chunk padded to 32 rows (compile-time, so
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   static_assert(NKB % 2 == 0 && NKB <= kMaxKb, "kv blocks");
   __shared__ PSmem<D> sm;
   constexpr int KP = PSmem<D>::KP, VP = PSmem<D>::VP;
-  constexpr int DC = D / 32, DB = D / 16;
+  constexpr int DC = D / 32;               // 32-wide d chunks (16x16x32 MFMA)
   constexpr int TPR = D / 8;
   static_assert(kThreads % TPR == 0, "loader mapping");
 
@@ -57,40 +59,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   constexpr int rpad = 16 * NKB;
   const int slot = a.chunk_slot[c];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lj = lane >> 4;
+  const int lr = lane & 15, lj = lane >> 4;  // 16x16 layout (window items)
   const int G = a.group;
   const float sl2 = a.scale_log2;
 
-  // ---- stage the chunk's K and V^T (rows >= R are zero)
+  // ---- stage the chunk's K and V (rows >= R are zero); every load is issued
+  // before the first LDS store so the staging costs one memory round trip
   {
     const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k);
     const uint16_t* pv = static_cast<const uint16_t*>(a.pool_v);
     const int64_t base = (int64_t)slot * a.ps_slot + (int64_t)g * a.ps_head;
     const int d0 = 8 * (tid % TPR);
-    constexpr int kQuadsPerPass = kThreads / TPR;
-    for (int r0 = 4 * (tid / TPR); r0 < rpad; r0 += 4 * kQuadsPerPass) {
-      u32x4 kr[4], vr[4];
+    constexpr int kRowsPerPass = 4 * (kThreads / TPR);
+    constexpr int kPasses = (rpad + kRowsPerPass - 1) / kRowsPerPass;
+    const int r_first = 4 * (tid / TPR);
+    u32x4 kr[kPasses][4], vr[kPasses][4];
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
+        const int r = r_first + ps * kRowsPerPass + i;
         if (r < R) {
           const int64_t off = base + (int64_t)r * a.ps_row + d0;
-          kr[i] = *reinterpret_cast<const u32x4*>(pk + off);
-          vr[i] = *reinterpret_cast<const u32x4*>(pv + off);
+          kr[ps][i] = *reinterpret_cast<const u32x4*>(pk + off);
+          vr[ps][i] = *reinterpret_cast<const u32x4*>(pv + off);
         } else {
-          kr[i] = vr[i] = u32x4{0, 0, 0, 0};
+          kr[ps][i] = vr[ps][i] = u32x4{0, 0, 0, 0};
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sm.k[(r0 + i) * KP + d0]) = kr[i];
+    for (int ps = 0; ps < kPasses; ++ps)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        const uint32_t lo = ((vr[0][w] >> sh) & 0xffffu) | (((vr[1][w] >> sh) & 0xffffu) << 16);
-        const uint32_t hi = ((vr[2][w] >> sh) & 0xffffu) | (((vr[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&sm.vt[(d0 + e) * VP + r0]) = u32x2{lo, hi};
+      for (int i = 0; i < 4; ++i) {
+        const int r = r_first + ps * kRowsPerPass + i;
+        if (r < rpad) {
+          *reinterpret_cast<u32x4*>(&sm.k[r * KP + d0]) = kr[ps][i];
+          *reinterpret_cast<u32x4*>(&sm.v[r * VP + d0]) = vr[ps][i];
+        }
       }
-    }
+    if (tid == 0) sm.next_item = kWaves;  // items 0..kWaves-1 go to waves 0..kWaves-1
   }
   __syncthreads();
 
@@ -104,146 +111,151 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
                        (int64_t)(c / a.chunks_per_win) * a.w * a.h_q * D;
   uint16_t* oc = static_cast<uint16_t*>(a.o_chunk) + (int64_t)c * R * a.h_q * D;
   using Attn = WaveAttn<D, KP, VP>;
-  const uint16_t* k_lane = &sm.k[lr * KP + 8 * lj];
-  const uint16_t* v_lane = &sm.vt[lr * VP + 4 * lj];
+  constexpr int DC32 = Attn::DC;            // 16-wide d chunks (32x32x16 MFMA)
+  const int lc = lane & 31, lh = lane >> 5; // 32x32 layout: query column, half
+  const uint16_t* k_lane = &sm.k[lc * KP + 8 * lh];
+  const uint16_t* v_lane = &sm.v[v_lane_offset(lane, VP)];
 
-  // query fragments of work item `it`: 32 chunk rows (it < n_cb) or 32 window rows
-  auto fetch = [&](int it, bf16x8 (&qf)[2][DC]) {
-    const bool win = it >= n_cb;
-    const uint16_t* base = win ? qw : qc;
-    const int first = (win ? it - n_cb : it) * 32;
-    const int n_rows = win ? n_rows_w : n_rows_c;
+  auto fetch_c = [&](int item, bf16x8 (&qf)[DC32]) {
+    const int x = item * 32 + lc;
+    if (x < n_rows_c) {
+      const int r = x / G, h = g * G + (x - r * G);
+      load_q<DC32, 16>(qf, qc + ((int64_t)r * a.h_q + h) * D + 8 * lh);
+    } else {
+      zero_q<DC32>(qf);
+    }
+  };
+  auto attend = [&](int item, const bf16x8 (&qf)[DC32]) {
+    __builtin_amdgcn_sched_barrier(0);     // keep items apart: no cross-item hoisting
+    Attn at;
+    at.init();
+    if constexpr (NKB < 4) {
+      at.template step<NKB / 2>(k_lane, v_lane, qf, sl2, R, lh);
+    } else {
+      // 64-row steps; a last 32-row remainder runs as a step over the final
+      // 64 rows with the first 32 masked (they were already attended)
+      constexpr int n_steps = (NKB + 3) / 4;
+#pragma unroll 1
+      for (int st = 0; st < n_steps; ++st) {
+        const int kv0 = st * 64 + 64 > rpad ? rpad - 64 : st * 64;
+        at.template step<2>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, R - kv0, lh, st * 64 - kv0);
+      }
+    }
+    const float l = at.row_sum();
+    const int x = item * 32 + lc;
+    if (x < n_rows_c) {
+      const int r = x / G, h = g * G + (x - r * G);
+      store_o_bf16<Attn::DB>(oc + ((int64_t)r * a.h_q + h) * D + 4 * lh, at.acc, 1.f / l);
+    }
+  };
+  // ---- phase 1: window-row items, a fixed round-robin over waves (so the
+  // per-key sums are added in a fixed order).  S = Q K^T on the 16x16x32 MFMA
+  // leaves lane (lr, lj) the keys 16 kb + lr of rows 4 lj + e, so each key's
+  // weight accumulates in registers with no per-item shuffles.
+  float colsum[NKB];                       // lane: key 16 kb + lr, summed over its window rows
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) colsum[kb] = 0.f;
+  const uint16_t* k16 = &sm.k[lr * KP + 8 * lj];
+  for (int item = n_cb + wave; item < n_items; item += kWaves) {
+    const int first = (item - n_cb) * 32;
+    bf16x8 qf[2][DC];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int x = first + 16 * b + lr;
-      if (x < n_rows) {
+      if (x < n_rows_w) {
         const int r = x / G, h = g * G + (x - r * G);
-        load_q<DC>(qf[b], base + ((int64_t)r * a.h_q + h) * D + 8 * lj);
+        load_q<DC, 32>(qf[b], qw + ((int64_t)r * a.h_q + h) * D + 8 * lj);
       } else {
         zero_q<DC>(qf[b]);
       }
     }
-  };
-
-  float colsum[NKB];                       // lane: key 16 kb + lr, summed over its window rows
-
-  // ---- one work item: 32 chunk rows (attention output) or 32 window rows
-  auto process = [&](int item, const bf16x8 (&qf)[2][DC]) {
-    __builtin_amdgcn_sched_barrier(0);     // keep items apart: no cross-item hoisting
-    if (item < n_cb) {
-      Attn at;
-      at.init();
-      // 64-row steps; a last 32-row remainder runs as a step over the final
-      // 64 rows with the first 32 masked (they were already attended)
-      if constexpr (NKB < 4) {
-        at.template step<NKB>(k_lane, v_lane, qf, sl2, R, lj);
-      } else {
-        constexpr int n_steps = (NKB + 3) / 4;
-#pragma unroll 1
-        for (int st = 0; st < n_steps; ++st) {
-          const int kv0 = st * 64 + 64 > rpad ? rpad - 64 : st * 64;
-          at.template step<4>(k_lane + kv0 * KP, v_lane + kv0, qf, sl2, R - kv0, lj, st * 64 - kv0);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x4 sw[NKB];
+      // key blocks in pairs; the scheduling barrier keeps at most one pair's
+      // K fragments in registers
+#pragma unroll
+      for (int kb = 0; kb < NKB; kb += 2) {
+        bf16x8 kf[2][DC];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc)
+            kf[u][dc] = *reinterpret_cast<const bf16x8*>(k16 + 16 * (kb + u) * KP + 32 * dc);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          sw[kb + u] = mfma16x16x32(qf[b][0], kf[u][0], zero);
+#pragma unroll
+          for (int dc = 1; dc < DC; ++dc) sw[kb + u] = mfma16x16x32(qf[b][dc], kf[u][dc], sw[kb + u]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // keys past R: only the last two blocks can hold any
+#pragma unroll
+      for (int kb = NKB - 2; kb < NKB; ++kb)
+        if (16 * kb + lr >= R) sw[kb] = ninf;
+      float mx[4], sum[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float m = fmaxf(sw[0][e], sw[1][e]);
+#pragma unroll
+        for (int kb = 2; kb < NKB; kb += 2) m = fmaxf(fmaxf(m, sw[kb][e]), sw[kb + 1][e]);
+        m = wave_xor_max(m, 1);
+        m = wave_xor_max(m, 2);
+        m = wave_xor_max(m, 4);
+        m = wave_xor_max(m, 8);
+        mx[e] = -m * sl2;
+        sum[e] = 0.f;
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int x = item * 32 + 16 * b + lr;
-        if (x >= n_rows_c) continue;
-        const int r = x / G, h = g * G + (x - r * G);
-        store_o_bf16<DB>(oc + ((int64_t)r * a.h_q + h) * D + 4 * lj, at.acc, b, 1.f / at.row_sum(b));
-      }
-    } else {
-      // S = Q K^T leaves lane (lr, lj) the keys 16 kb + lr of rows 4 lj + e, so
-      // each key's weight accumulates in registers with no per-block shuffles.
-      const int first = (item - n_cb) * 32;
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x4 sw[NKB];
-        // key blocks in pairs; the scheduling barrier keeps at most one pair's
-        // K fragments in registers
-#pragma unroll
-        for (int kb = 0; kb < NKB; kb += 2) {
-          bf16x8 kf[2][DC];
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int dc = 0; dc < DC; ++dc)
-              kf[u][dc] = *reinterpret_cast<const bf16x8*>(k_lane + 16 * (kb + u) * KP + 32 * dc);
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            sw[kb + u] = mfma16x16x32(qf[b][0], kf[u][0], zero);
-#pragma unroll
-            for (int dc = 1; dc < DC; ++dc) sw[kb + u] = mfma16x16x32(qf[b][dc], kf[u][dc], sw[kb + u]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // keys past R: only the last two blocks can hold any
-#pragma unroll
-        for (int kb = NKB - 2; kb < NKB; ++kb)
-          if (16 * kb + lr >= R) sw[kb] = ninf;
-        float mx[4], sum[4];
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float m = fmaxf(sw[0][e], sw[1][e]);
-#pragma unroll
-          for (int kb = 2; kb < NKB; kb += 2) m = fmaxf(fmaxf(m, sw[kb][e]), sw[kb + 1][e]);
-          m = wave_xor_max(m, 1);
-          m = wave_xor_max(m, 2);
-          m = wave_xor_max(m, 4);
-          m = wave_xor_max(m, 8);
-          mx[e] = -m * sl2;
-          sum[e] = 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sw[kb][e], sl2, mx[e]));
+          sw[kb][e] = p;
+          sum[e] += p;
         }
+      float wgt[4];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sw[kb][e], sl2, mx[e]));
-            sw[kb][e] = p;
-            sum[e] += p;
-          }
-        float wgt[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float t = sum[e];
-          t = wave_xor_sum(t, 1);
-          t = wave_xor_sum(t, 2);
-          t = wave_xor_sum(t, 4);
-          t = wave_xor_sum(t, 8);
-          wgt[e] = first + 16 * b + 4 * lj + e < n_rows_w ? 1.f / t : 0.f;
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          colsum[kb] = fmaf(sw[kb][3], wgt[3], fmaf(sw[kb][2], wgt[2], fmaf(sw[kb][1], wgt[1],
-                            fmaf(sw[kb][0], wgt[0], colsum[kb]))));
+      for (int e = 0; e < 4; ++e) {
+        float t = sum[e];
+        t = wave_xor_sum(t, 1);
+        t = wave_xor_sum(t, 2);
+        t = wave_xor_sum(t, 4);
+        t = wave_xor_sum(t, 8);
+        wgt[e] = first + 16 * b + 4 * lj + e < n_rows_w ? 1.f / t : 0.f;
       }
-    }
-  };
-
-  // ---- phase 1: chunk-row items (round-robin over waves), unrolled twice
-  // over two query register sets so the next item's queries load while the
-  // current item computes
-  {
-    bf16x8 qa[2][DC], qb[2][DC];
-    if (wave < n_cb) fetch(wave, qa);
-    for (int item = wave; item < n_cb; item += 2 * kWaves) {
-      if (item + kWaves < n_cb) fetch(item + kWaves, qb);
-      process(item, qa);
-      if (item + kWaves >= n_cb) break;
-      if (item + 2 * kWaves < n_cb) fetch(item + 2 * kWaves, qa);
-      process(item + kWaves, qb);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        colsum[kb] = fmaf(sw[kb][3], wgt[3], fmaf(sw[kb][2], wgt[2], fmaf(sw[kb][1], wgt[1],
+                          fmaf(sw[kb][0], wgt[0], colsum[kb]))));
     }
   }
-  // ---- phase 2: window-row items, continuing the round-robin numbering so
-  // waves with fewer chunk items take window items first
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) colsum[kb] = 0.f;
-  for (int item = n_cb + ((wave - n_cb) % kWaves + kWaves) % kWaves; item < n_items; item += kWaves) {
-    bf16x8 qf[2][DC];
-    fetch(item, qf);
-    process(item, qf);
+
+  // ---- phase 2: chunk-row items, 32 (row, grouped head) pairs each, handed
+  // out dynamically (each item's output does not depend on which wave runs
+  // it), which evens out the window items and the waves' unequal issue
+  // priority; the next item's queries load while the current item computes
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&sm.next_item, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  {
+    bf16x8 qa[DC32], qb[DC32];
+    int item = wave;
+    if (item < n_cb) fetch_c(item, qa);
+    while (item < n_cb) {
+      const int nxt = grab();
+      if (nxt < n_cb) fetch_c(nxt, qb);
+      attend(item, qa);
+      if (nxt >= n_cb) break;
+      item = grab();
+      if (item < n_cb) fetch_c(item, qa);
+      attend(nxt, qb);
+    }
   }
 
   // ---- per-key sums: across the 4 lane groups, then across waves in order
