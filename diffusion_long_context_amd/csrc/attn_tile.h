@@ -8,7 +8,7 @@
 //   S^T = K Q^T : lane holds S^T[kv = 32 kb + 8 m + 4 j + t][q = c], i = 4 m + t
 //   O^T += V^T P^T : lane holds O^T[d = 32 db + 8 m + 4 j + t][q = c]
 // so every lane owns one query column; the row max needs one exchange with
-// lane l ^ 32.  For the 16-row kv chunk h of block kb, the PV B operand is the
+// lane l ^ 32 (v_permlane32_swap).  For the 16-row kv chunk h of block kb, the PV B operand is the
 // lane's accumulator registers 8 h .. 8 h + 7 (kv 32 kb + 16 h + 8 u + 4 j + t,
 // element 4 u + t).  V stays row-major in LDS like K; its A operand (V^T rows)
 // comes from two ds_read_b64_tr_b16: inside each 16-lane group, lane 4 a + b
@@ -37,8 +37,18 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Value of lane l ^ 32.
-__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+// max / sum of a value and its copy in lane l ^ 32.  v_permlane32_swap with
+// the same register as both operands leaves one output holding lanes 0..31
+// twice and the other lanes 32..63 twice, so combining the two outputs
+// lane-wise combines each lane with its partner (a VALU op, no LDS trip).
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -71,17 +81,11 @@ struct WaveAttn {
     m_run = -INFINITY;
   }
 
-  // Attend to kv rows [0, 32 NK) of an LDS block; only rows in
-  // [valid_lo, valid_hi) count, the rest are masked (a wave-uniform branch,
-  // taken only by a partial block).  k_lane = &K[c][8 j] (pitch KP) and
-  // v_lane = V + v_lane_offset(lane, VP) (row-major V, pitch VP) are the
-  // lane's base addresses, so every fragment read below is the base plus a
-  // compile-time offset.
+  // S^T for kv rows [0, 32 NK) of an LDS block: k_lane = &K[c][8 j] (pitch
+  // KP), so every fragment read is the base plus a compile-time offset.
   template <int NK>
-  __device__ __forceinline__ void step(const uint16_t* __restrict__ k_lane,
-                                       const uint16_t* __restrict__ v_lane, const bf16x8 (&qf)[DC],
-                                       float sl2, int valid_hi, int j, int valid_lo = 0) {
-    f32x16 sc[NK];
+  __device__ __forceinline__ void qk(f32x16 (&sc)[NK], const uint16_t* __restrict__ k_lane,
+                                     const bf16x8 (&qf)[DC]) const {
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb)
       sc[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(k_lane + 32 * kb * KP), qf[0], f32x16{});
@@ -90,6 +94,15 @@ struct WaveAttn {
 #pragma unroll
       for (int kb = 0; kb < NK; ++kb)
         sc[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(k_lane + 32 * kb * KP + 16 * dc), qf[dc], sc[kb]);
+  }
+
+  // Online softmax of the block's scores and O^T += V^T P^T.  Only rows in
+  // [valid_lo, valid_hi) count, the rest are masked (a wave-uniform branch,
+  // taken only by a partial block).  v_lane = V + v_lane_offset(lane, VP)
+  // (row-major V, pitch VP).
+  template <int NK>
+  __device__ __forceinline__ void softmax_pv(f32x16 (&sc)[NK], const uint16_t* __restrict__ v_lane,
+                                             float sl2, int valid_hi, int j, int valid_lo = 0) {
     if (__builtin_expect(valid_hi < 32 * NK || valid_lo > 0, 0)) {
       // rows r valid iff valid_lo <= r < valid_hi, as one unsigned compare
       const unsigned span = (unsigned)(valid_hi - valid_lo);
@@ -106,7 +119,7 @@ struct WaveAttn {
     for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
       for (int i = kb ? 0 : 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[kb][i]), sc[kb][i + 1]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = max_halves(mx);
     const float ms = mx * sl2;
     const bool need = ms > m_run + kRescaleLog2;
     if (__ballot(need)) {
@@ -148,8 +161,18 @@ struct WaveAttn {
     }
   }
 
+  // Both halves of one block step.
+  template <int NK>
+  __device__ __forceinline__ void step(const uint16_t* __restrict__ k_lane,
+                                       const uint16_t* __restrict__ v_lane, const bf16x8 (&qf)[DC],
+                                       float sl2, int valid_hi, int j, int valid_lo = 0) {
+    f32x16 sc[NK];
+    qk<NK>(sc, k_lane, qf);
+    softmax_pv<NK>(sc, v_lane, sl2, valid_hi, j, valid_lo);
+  }
+
   // Full row sum (both kv halves) and natural-log normaliser.
-  __device__ __forceinline__ float row_sum() const { return l_run + swap_halves(l_run); }
+  __device__ __forceinline__ float row_sum() const { return sum_halves(l_run); }
   __device__ __forceinline__ float lse(float l) const { return m_run * kLn2 + logf(l); }
 };
 

@@ -37,9 +37,10 @@ constexpr int kTableTiles = 8;             // row-pointer table capacity (tiles)
 template <int D>
 struct Smem {
   static constexpr int KP = D + 8;         // K pitch (elements): 8-row 16-byte reads conflict-free
-  static constexpr int VP = D + 16;        // V pitch (elements): transposing reads conflict-free
-  uint16_t k[2][kTile * KP];               // double-buffered tiles, both row-major
-  uint16_t v[2][kTile * VP];
+  static constexpr int VP = D + 32;        // V pitch (elements): transposing reads conflict-free
+                                           // on the 64-bank LDS (4 rows x 64 B per 32 lanes)
+  uint16_t k[2][kTile * KP];               // double-buffered tiles, both row-major;
+  uint16_t v[2][kTile * VP];               // K runs one tile ahead of V
   gptr16 kptr[kTableTiles * kTile];        // K / V address of each attended row
   gptr16 vptr[kTableTiles * kTile];
 };
@@ -129,24 +130,34 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     zero_q<DC>(qf);
   }
 
-  // ---- tile loader: thread owns RPT consecutive kv rows x 8 d values
+  // ---- tile loader: thread owns RPT consecutive kv rows x 8 d values; the
+  // K rows it carries belong to one tile and the V rows to the tile before
   const int ld_d0 = 8 * (tid % TPR);
   const int ld_r0 = RPT * (tid / TPR);
   u32x4 kreg[RPT], vreg[RPT];
-  auto load_tile = [&](int t) {
+  auto load_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int idx = (t - tw) * kTile + ld_r0 + i;
       kreg[i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(sm.kptr[idx] + ld_d0);
+    }
+  };
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int idx = (t - tw) * kTile + ld_r0 + i;
       vreg[i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(sm.vptr[idx] + ld_d0);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
+    for (int i = 0; i < RPT; ++i)
       *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[i];
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
       *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[i];
-    }
   };
 
   Attn at;
@@ -154,33 +165,55 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const float sl2 = a.scale_log2;
   const int k_lane = lc * KP + 8 * lj;      // lane offsets inside one LDS buffer
   const int v_lane = v_lane_offset(lane, VP);
+  constexpr int NK = kTile / 32;
+  const uint16_t* k_base = &sm.k[0][0] + k_lane;
+  const uint16_t* v_base = &sm.v[0][0] + v_lane;
 
-  // ---- main loop: tile t computes from LDS buffer (t - t_begin) & 1 while
-  // tile t+1 is stored into the other buffer and tile t+2 is being loaded;
-  // one barrier per tile
+  // ---- software pipeline over tiles (local index u = t - t_begin):
+  // iteration u issues S^T of tile u+1 before the softmax and PV of tile u,
+  // so each wave's VALU work overlaps its own matrix work.  Tile u's K sits
+  // in K buffer u & 1 from iteration u-2 on, its V in V buffer u & 1 from
+  // iteration u-1 on; iteration u stores K of tile u+2 and V of tile u+1
+  // (loaded during iteration u-1) and starts the loads of K u+3 and V u+2.
+  // One barrier per tile.
+  const int n_loc = t_end - t_begin;
   __syncthreads();                         // row table ready
-  load_tile(t_begin);
-  store_tile(0);
-  if (t_begin + 1 < t_end) load_tile(t_begin + 1);
+  load_k(t_begin);
+  load_v(t_begin);
+  store_k(0);
+  store_v(0);
+  if (n_loc > 1) {
+    load_k(t_begin + 1);
+    store_k(1);
+  }
+  if (n_loc > 2) load_k(t_begin + 2);
+  if (n_loc > 1) load_v(t_begin + 1);
   __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const uint16_t* kb = &sm.k[0][0] + buf * (kTile * KP) + k_lane;
-    const uint16_t* vb = &sm.v[0][0] + buf * (kTile * VP) + v_lane;
-    at.template step<kTile / 32>(kb, vb, qf, sl2, n_kv - t * kTile, lj);
-    if (t + 1 < t_end) {
-      store_tile(buf ^ 1);                 // that buffer was last read by tile t-1
-      if (t + 2 < t_end) {
-        if (t + 2 - tw >= kTableTiles) {   // refill the row table (rare)
-          __syncthreads();                 // every wave has read the old table
-          tw = t + 2;
-          build_table(tw);
-          __syncthreads();
-        }
-        load_tile(t + 2);
+  f32x16 sc_a[NK], sc_b[NK];
+  at.template qk<NK>(sc_a, k_base, qf);
+  __syncthreads();                         // K buffer 0 is rewritten in iteration 0
+
+  auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK]) {
+    const int t = t_begin + u;
+    if (u + 1 < n_loc) at.template qk<NK>(nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf);
+    at.template softmax_pv<NK>(cur, v_base + (u & 1) * (kTile * VP), sl2, n_kv - t * kTile, lj);
+    if (u + 2 < n_loc) store_k(u & 1);
+    if (u + 1 < n_loc) store_v((u + 1) & 1);
+    if (u + 2 < n_loc) {
+      if (t + 3 - tw >= kTableTiles) {     // refill the row table (rare)
+        __syncthreads();                   // every wave has read the old table
+        tw = t + 2;
+        build_table(tw);
+        __syncthreads();
       }
+      if (u + 3 < n_loc) load_k(t + 3);
+      load_v(t + 2);
     }
     __syncthreads();
+  };
+  for (int u = 0; u < n_loc; u += 2) {
+    iter(u, sc_a, sc_b);
+    if (u + 1 < n_loc) iter(u + 1, sc_b, sc_a);
   }
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
@@ -219,16 +252,36 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
   const float* pl = a.part_lse + a.seq[si].lse_off + row;
   const float* po = a.part_o + a.seq[si].part_off + (int64_t)row * D + e0;
   const int64_t sl = rows, so = (int64_t)rows * D;
+  // splits are visited in groups of kBatch so that the group's loads are in
+  // flight together
+  constexpr int kBatch = 8;
   float mx = -INFINITY;
-  for (int j = 0; j < n_splits; ++j) mx = fmaxf(mx, pl[j * sl]);
-  float tot = 0.f;
-  for (int j = 0; j < n_splits; ++j) tot += expf(pl[j * sl] - mx);
-  const float inv = 1.f / tot;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < n_splits; ++j) {
-    const float wj = expf(pl[j * sl] - mx) * inv;
-    o += wj * *reinterpret_cast<const f32x4*>(po + j * so);
+  for (int j0 = 0; j0 < n_splits; j0 += kBatch) {
+    float t[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) t[u] = j0 + u < n_splits ? pl[(j0 + u) * sl] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mx = fmaxf(mx, t[u]);
   }
+  float tot = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < n_splits; j0 += kBatch) {
+    float t[kBatch];
+    f32x4 x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool in = j0 + u < n_splits;
+      t[u] = in ? pl[(j0 + u) * sl] : -INFINITY;
+      x[u] = in ? *reinterpret_cast<const f32x4*>(po + (j0 + u) * so) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = expf(t[u] - mx);    // 0 for an empty split (lse = -inf)
+      tot += w;
+      o += w * x[u];
+    }
+  }
+  o *= 1.f / tot;
   const int s = a.seq0 + si;
   const int i = row / a.h_q, h = row - i * a.h_q;
   const int64_t out = ((int64_t)s * rows + row) * D + e0;

@@ -129,17 +129,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     __builtin_amdgcn_sched_barrier(0);     // keep items apart: no cross-item hoisting
     Attn at;
     at.init();
-    if constexpr (NKB < 4) {
-      at.template step<NKB / 2>(k_lane, v_lane, qf, sl2, R, lh);
-    } else {
-      // 64-row steps; a last 32-row remainder runs as a step over the final
-      // 64 rows with the first 32 masked (they were already attended)
-      constexpr int n_steps = (NKB + 3) / 4;
+    // 64-row steps over rows [0, 64 (NKB / 4)), the last one masked at R;
+    // when NKB % 4 == 2 the remaining 32 rows (R = C + 1 puts a single row
+    // there for C a multiple of 64) run as one 32-row step
+    constexpr int n_full = NKB / 4;
 #pragma unroll 1
-      for (int st = 0; st < n_steps; ++st) {
-        const int kv0 = st * 64 + 64 > rpad ? rpad - 64 : st * 64;
-        at.template step<2>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, R - kv0, lh, st * 64 - kv0);
-      }
+    for (int st = 0; st < n_full; ++st)
+      at.template step<2>(k_lane + st * 64 * KP, v_lane + st * 64 * VP, qf, sl2, R - st * 64, lh);
+    if constexpr (NKB % 4 == 2) {
+      constexpr int kv0 = 64 * n_full;
+      at.template step<1>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, R - kv0, lh);
     }
     const float l = at.row_sum();
     const int x = item * 32 + lc;

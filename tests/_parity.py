@@ -4,11 +4,12 @@ error metrics, and the tolerances every comparison uses.
 Tolerances:
   bf16 outputs       rel-L2 <= 5e-3 and max-abs <= 2e-2 over the tensor
   f32 outputs        rel-L2 <= 1e-5 and max-abs <= 1e-5
-  lse                max-abs <= 2e-3 (bf16 inputs), 1e-5 (f32 inputs).  The bf16
-                     kernels normalise with the row sum of the bf16-rounded
-                     probabilities they feed to the PV product; rounding each p
-                     to bf16 moves that sum by at most a factor (1 +- 2^-9), so
-                     |d lse| <= ln(1 + 2^-9) = 1.95e-3.
+  lse                max-abs <= 2e-3 (bf16 inputs), 1e-5 (f32 inputs).  The bound
+                     allows a kernel to normalise with the row sum of the
+                     bf16-rounded probabilities it feeds to the PV product:
+                     rounding each p to bf16 moves that sum by at most a factor
+                     (1 +- 2^-9), so |d lse| <= ln(1 + 2^-9) = 1.95e-3.  (The
+                     current kernels sum the unrounded float32 probabilities.)
   key_score          rel-L2 <= 1e-4 (bf16 inputs), 1e-6 (f32 inputs)
   selected indices   bit-exact
 """
