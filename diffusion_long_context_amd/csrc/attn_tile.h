@@ -96,13 +96,15 @@ struct WaveAttn {
         sc[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(k_lane + 32 * kb * KP + 16 * dc), qf[dc], sc[kb]);
   }
 
-  // Online softmax of the block's scores and O^T += V^T P^T.  Only rows in
-  // [valid_lo, valid_hi) count, the rest are masked (a wave-uniform branch,
-  // taken only by a partial block).  v_lane = V + v_lane_offset(lane, VP)
-  // (row-major V, pitch VP).
+  // The softmax and PV of one block come in three parts, so that a caller can
+  // interleave the S^T MFMAs of the next block with this block's exp work.
+  //
+  // (1) Mask, row max and the lazy rescale (the only branches).  Only rows in
+  // [valid_lo, valid_hi) count; the rest are masked (a wave-uniform branch,
+  // taken only by a partial block).
   template <int NK>
-  __device__ __forceinline__ void softmax_pv(f32x16 (&sc)[NK], const uint16_t* __restrict__ v_lane,
-                                             float sl2, int valid_hi, int j, int valid_lo = 0) {
+  __device__ __forceinline__ void prep(f32x16 (&sc)[NK], float sl2, int valid_hi, int j,
+                                       int valid_lo = 0) {
     if (__builtin_expect(valid_hi < 32 * NK || valid_lo > 0, 0)) {
       // rows r valid iff valid_lo <= r < valid_hi, as one unsigned compare
       const unsigned span = (unsigned)(valid_hi - valid_lo);
@@ -130,45 +132,80 @@ struct WaveAttn {
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       l_run *= alpha;
     }
+  }
+
+  // (2) p = 2^(s * sl2 - m) in place, the row sums (float32, unrounded p)
+  // and the bf16 P fragments (B operands of
+  // PV: fragment 2 kb + h holds the lane's registers 8 h .. 8 h + 7 of block
+  // kb).  With NXT, the S^T MFMAs of the next block (K at k_next) are issued
+  // interleaved with that VALU work, about five VALU ops per MFMA.
+  template <int NK, bool NXT>
+  __device__ __forceinline__ void exp_qk(f32x16 (&sc)[NK], bf16x8 (&pf)[2 * NK], f32x16 (&sn)[NK],
+                                         const uint16_t* __restrict__ k_next,
+                                         const bf16x8 (&qf)[DC], float sl2) {
     const float neg_m = -m_run;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, neg_m));
-        sc[kb][i] = p;
-        ps += p;
+        sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], sl2, neg_m));
+        ps += sc[kb][i];
       }
     l_run += ps;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pf[2 * kb + h] = bf16x8{(__bf16)sc[kb][8 * h + 0], (__bf16)sc[kb][8 * h + 1],
+                                (__bf16)sc[kb][8 * h + 2], (__bf16)sc[kb][8 * h + 3],
+                                (__bf16)sc[kb][8 * h + 4], (__bf16)sc[kb][8 * h + 5],
+                                (__bf16)sc[kb][8 * h + 6], (__bf16)sc[kb][8 * h + 7]};
+    if constexpr (NXT) {
+      qk<NK>(sn, k_next, qf);
+      // schedule: four K fragment reads ahead, then per MFMA about five VALU
+      // ops and the next fragment read
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int m = 0; m < NK * DC; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+        if (m + 4 < NK * DC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  }
+
+  // (3) O^T += V^T P^T.  v_lane = V + v_lane_offset(lane, VP) (row-major V,
+  // pitch VP).
+  template <int NK>
+  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2 * NK], const uint16_t* __restrict__ v_lane) {
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 pf = bf16x8{(__bf16)sc[kb][8 * h + 0], (__bf16)sc[kb][8 * h + 1],
-                                 (__bf16)sc[kb][8 * h + 2], (__bf16)sc[kb][8 * h + 3],
-                                 (__bf16)sc[kb][8 * h + 4], (__bf16)sc[kb][8 * h + 5],
-                                 (__bf16)sc[kb][8 * h + 6], (__bf16)sc[kb][8 * h + 7]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const uint16_t* vp = v_lane + (32 * kb + 16 * h) * VP + 32 * db;
           const bf16x4 lo = lds_read_tr16(vp);
           const bf16x4 hi = lds_read_tr16(vp + 8 * VP);
           const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[db] = mfma32x32x16(va, pf, acc[db]);
+          acc[db] = mfma32x32x16(va, pf[2 * kb + h], acc[db]);
         }
       }
     }
   }
 
-  // Both halves of one block step.
+  // One whole block step, no interleaving.
   template <int NK>
   __device__ __forceinline__ void step(const uint16_t* __restrict__ k_lane,
                                        const uint16_t* __restrict__ v_lane, const bf16x8 (&qf)[DC],
                                        float sl2, int valid_hi, int j, int valid_lo = 0) {
     f32x16 sc[NK];
+    bf16x8 pf[2 * NK];
     qk<NK>(sc, k_lane, qf);
-    softmax_pv<NK>(sc, v_lane, sl2, valid_hi, j, valid_lo);
+    prep<NK>(sc, sl2, valid_hi, j, valid_lo);
+    exp_qk<NK, false>(sc, pf, sc, nullptr, qf, sl2);
+    pv<NK>(pf, v_lane);
   }
 
   // Full row sum (both kv halves) and natural-log normaliser.
@@ -189,17 +226,28 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[DC], const uint16_t* row_plu
   for (int dc = 0; dc < DC; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(row_plus_8j + STRIDE * dc);
 }
 
-// Store a wavefront's O^T column (query column c) with 4 consecutive d per
-// accumulator group: row_plus_4j = &O[row][4 j].
+// Store a wavefront's O^T columns as bf16 rows, 16 bytes per lane and
+// store: for accumulator block db and m-pair p, lane (c, j) holds d =
+// 32 db + 16 p + 8 m' + 4 j + t (m' = 0, 1).  One v_permlane32_swap of the
+// m' = 0 values (X) with the m' = 1 values (Y) leaves lane c with X of lanes
+// c and c + 32 (d = 32 db + 16 p + 0..7) and lane c + 32 with Y of both
+// (d = 32 db + 16 p + 8..15).  row_plus_8j = &O[row][8 j]; lanes c and c + 32
+// (same row) must both take part.
 template <int DB>
-__device__ __forceinline__ void store_o_bf16(uint16_t* row_plus_4j, const f32x16 (&acc)[DB], float inv) {
+__device__ __forceinline__ void store_o_bf16(uint16_t* row_plus_8j, const f32x16 (&acc)[DB], float inv) {
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float x0 = acc[db][4 * m] * inv, x1 = acc[db][4 * m + 1] * inv;
-      const float x2 = acc[db][4 * m + 2] * inv, x3 = acc[db][4 * m + 3] * inv;
-      *reinterpret_cast<u32x2*>(row_plus_4j + 32 * db + 8 * m) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+    for (int p = 0; p < 2; ++p) {
+      uint32_t x[2], y[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        x[h] = pack_bf16x2(acc[db][8 * p + 2 * h] * inv, acc[db][8 * p + 2 * h + 1] * inv);
+        y[h] = pack_bf16x2(acc[db][8 * p + 4 + 2 * h] * inv, acc[db][8 * p + 4 + 2 * h + 1] * inv);
+      }
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+      *reinterpret_cast<u32x4*>(row_plus_8j + 32 * db + 16 * p) = u32x4{s0[0], s1[0], s0[1], s1[1]};
     }
 }
 

@@ -20,8 +20,8 @@
 //   per-workgroup row-pointer table (no gather-to-contiguous copy); K and V
 //   are stored row-major and the PV A operand is read with gfx950's
 //   transposing LDS load (ds_read_b64_tr_b16).  Tiles are
-//   double-buffered in LDS (one barrier per tile); the global loads of tile
-//   t+2 are in flight while tile t computes.
+//   double-buffered in LDS (one barrier per tile); the global loads of tiles
+//   t+2 and t+3 are in flight (in staging registers) while tile t computes.
 // * Online softmax in base 2: the scale and log2(e) fold into one FMA before
 //   v_exp_f32 and the running max moves lazily (see kRescaleLog2).
 #include "attn_tile.h"
@@ -39,8 +39,8 @@ struct Smem {
   static constexpr int KP = D + 8;         // K pitch (elements): 8-row 16-byte reads conflict-free
   static constexpr int VP = D + 32;        // V pitch (elements): transposing reads conflict-free
                                            // on the 64-bank LDS (4 rows x 64 B per 32 lanes)
-  uint16_t k[2][kTile * KP];               // double-buffered tiles, both row-major;
-  uint16_t v[2][kTile * VP];               // K runs one tile ahead of V
+  uint16_t k[2][kTile * KP];               // double-buffered tiles, both row-major
+  uint16_t v[2][kTile * VP];
   gptr16 kptr[kTableTiles * kTile];        // K / V address of each attended row
   gptr16 vptr[kTableTiles * kTile];
 };
@@ -85,11 +85,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const int n_kv = a.seq[si].n_kv;
   const int n_splits = a.seq[si].n_splits;
   const int tps = a.seq[si].tiles_per_split;
+  // query tiles vary fastest, so the workgroups that share one (kv head,
+  // split) -- and therefore its K/V rows -- sit on one XCD and hit its L2
   int local = wg - a.seq[si].wg_begin;
-  const int split = local % n_splits;
-  local /= n_splits;
   const int qt = local % a.q_tiles;
-  const int g = local / a.q_tiles;
+  local /= a.q_tiles;
+  const int split = local % n_splits;
+  const int g = local / n_splits;
   const int s = a.seq0 + si;
   const int n_tiles = (n_kv + kTile - 1) / kTile;
   const int t_begin = split * tps;
@@ -130,34 +132,43 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     zero_q<DC>(qf);
   }
 
-  // ---- tile loader: thread owns RPT consecutive kv rows x 8 d values; the
-  // K rows it carries belong to one tile and the V rows to the tile before
+  // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values of
+  // a tile.  K runs one tile ahead of V: load unit a carries K of tile a and
+  // V of tile a-1 (local tile numbers u = t - t_begin, clamped to the split,
+  // so a unit past its end re-reads valid rows that are never stored).
+  // STAGES staging register sets let a unit's loads be issued STAGES
+  // iterations before its LDS store.
+  constexpr int STAGES = RPT <= 2 ? 2 : 1;
   const int ld_d0 = 8 * (tid % TPR);
   const int ld_r0 = RPT * (tid / TPR);
-  u32x4 kreg[RPT], vreg[RPT];
-  auto load_k = [&](int t) {
+  const int n_loc = t_end - t_begin;
+  u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
+  gptr16 kp_next[RPT], vp_next[RPT];       // row pointers of the next unit to load
+  auto fetch_ptrs = [&](int uk, int uv) {  // local tiles of the K and V rows
+    const int ik = (t_begin + min(uk, n_loc - 1) - tw) * kTile + ld_r0;
+    const int iv = (t_begin + min(max(uv, 0), n_loc - 1) - tw) * kTile + ld_r0;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int idx = (t - tw) * kTile + ld_r0 + i;
-      kreg[i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(sm.kptr[idx] + ld_d0);
+      kp_next[i] = sm.kptr[ik + i];
+      vp_next[i] = sm.vptr[iv + i];
     }
   };
-  auto load_v = [&](int t) {
+  auto load_unit = [&](int set) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int idx = (t - tw) * kTile + ld_r0 + i;
-      vreg[i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(sm.vptr[idx] + ld_d0);
+      kreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(kp_next[i] + ld_d0);
+      vreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(vp_next[i] + ld_d0);
     }
   };
-  auto store_k = [&](int buf) {
+  auto store_k = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[set][i];
   };
-  auto store_v = [&](int buf) {
+  auto store_v = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[i];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[set][i];
   };
 
   Attn at;
@@ -169,51 +180,69 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const uint16_t* k_base = &sm.k[0][0] + k_lane;
   const uint16_t* v_base = &sm.v[0][0] + v_lane;
 
-  // ---- software pipeline over tiles (local index u = t - t_begin):
-  // iteration u issues S^T of tile u+1 before the softmax and PV of tile u,
-  // so each wave's VALU work overlaps its own matrix work.  Tile u's K sits
-  // in K buffer u & 1 from iteration u-2 on, its V in V buffer u & 1 from
-  // iteration u-1 on; iteration u stores K of tile u+2 and V of tile u+1
-  // (loaded during iteration u-1) and starts the loads of K u+3 and V u+2.
-  // One barrier per tile.
-  const int n_loc = t_end - t_begin;
+  // ---- prologue: K and V of tile 0 and K of tile 1 into LDS, units 2 ..
+  // 1 + STAGES in flight, S^T of tile 0 computed
   __syncthreads();                         // row table ready
-  load_k(t_begin);
-  load_v(t_begin);
-  store_k(0);
-  store_v(0);
-  if (n_loc > 1) {
-    load_k(t_begin + 1);
-    store_k(1);
+  fetch_ptrs(0, 0);
+  load_unit(0);
+  store_k(0, 0);
+  store_v(0, 0);
+  fetch_ptrs(1, 1);
+  load_unit(0);
+  store_k(1, 0);
+#pragma unroll
+  for (int i = 0; i < STAGES; ++i) {
+    fetch_ptrs(2 + i, 1 + i);
+    load_unit((2 + i) % STAGES);
   }
-  if (n_loc > 2) load_k(t_begin + 2);
-  if (n_loc > 1) load_v(t_begin + 1);
+  fetch_ptrs(2 + STAGES, 1 + STAGES);
   __syncthreads();
   f32x16 sc_a[NK], sc_b[NK];
   at.template qk<NK>(sc_a, k_base, qf);
   __syncthreads();                         // K buffer 0 is rewritten in iteration 0
 
+  // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
+  // u & 1, whose tile u was last read in iteration u-1; V of tile u+1 into V
+  // buffer (u+1) & 1, last read by tile u-1), issues the loads of unit
+  // u+2+STAGES into the staging set just freed, then runs the softmax of
+  // tile u with the S^T MFMAs of tile u+1 interleaved, and the PV of tile u.
+  // Every iteration issues exactly one unit's loads, so the wait before a
+  // store covers only loads issued STAGES iterations earlier.  One barrier
+  // per tile.
   auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK]) {
-    const int t = t_begin + u;
-    if (u + 1 < n_loc) at.template qk<NK>(nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf);
-    at.template softmax_pv<NK>(cur, v_base + (u & 1) * (kTile * VP), sl2, n_kv - t * kTile, lj);
-    if (u + 2 < n_loc) store_k(u & 1);
-    if (u + 1 < n_loc) store_v((u + 1) & 1);
-    if (u + 2 < n_loc) {
-      if (t + 3 - tw >= kTableTiles) {     // refill the row table (rare)
+    const int set = u % STAGES;
+    if (u + 2 < n_loc) store_k(u & 1, set);
+    if (u + 1 < n_loc) store_v((u + 1) & 1, set);
+    load_unit(set);
+    const int un = u + 3 + STAGES;         // the unit the next iteration loads
+    if (un <= n_loc) {                     // beyond, the clamped pointers stay valid
+      if (t_begin + min(un, n_loc - 1) - tw >= kTableTiles) {   // refill the row table (rare)
         __syncthreads();                   // every wave has read the old table
-        tw = t + 2;
+        tw = t_begin + min(un, n_loc - 1) - 1;
         build_table(tw);
         __syncthreads();
       }
-      if (u + 3 < n_loc) load_k(t + 3);
-      load_v(t + 2);
+      fetch_ptrs(un, un - 1);
     }
+    const int t = t_begin + u;
+    bf16x8 pf[2 * NK];
+    at.template prep<NK>(cur, sl2, n_kv - t * kTile, lj);
+    if (u + 1 < n_loc)
+      at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
+    else
+      at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
+    at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP));
     __syncthreads();
   };
-  for (int u = 0; u < n_loc; u += 2) {
-    iter(u, sc_a, sc_b);
-    if (u + 1 < n_loc) iter(u + 1, sc_b, sc_a);
+  {
+    // both halves unconditional inside the loop, so the loop head is reached
+    // only after the second half's loads (exact wait counts before stores)
+    int u = 0;
+    for (; u + 1 < n_loc; u += 2) {
+      iter(u, sc_a, sc_b);
+      iter(u + 1, sc_b, sc_a);
+    }
+    if (u < n_loc) iter(u, sc_a, sc_b);
   }
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
@@ -223,7 +252,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     const float inv = 1.f / l;
     const float lse_v = at.lse(l);
     if (n_splits == 1) {
-      store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 4 * lj,
+      store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj,
                        at.acc, inv);
       if (a.lse != nullptr && lj == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
     } else {

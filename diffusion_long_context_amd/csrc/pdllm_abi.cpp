@@ -167,7 +167,7 @@ const char* pdllm_last_error(void) { return g_last_error.c_str(); }
 
 size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slot_rows) {
   if (n_chunks < 0 || h_kv < 1 || slot_rows < 1) return 0;
-  const int64_t bytes = (int64_t)n_chunks * h_kv * slot_rows * 4;
+  const int64_t bytes = (int64_t)n_chunks * h_kv * pdllm::kPrefillParts * slot_rows * 4;
   return (size_t)((bytes + 255) / 256 * 256);
 }
 
@@ -220,6 +220,7 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
   a.w = w;
   a.chunks_per_win = chunks_per_win;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.parts = pool->dtype == PDLLM_BF16 ? pdllm::kPrefillParts : 1;
   const int err = pool->dtype == PDLLM_BF16 ? pdllm::launch_prefill_bf16(a, pool->d, stream)
                                              : pdllm::launch_prefill_f32(a, pool->d, stream);
   if ((st = hip_status(err, "chunk prefill launch")) != PDLLM_OK) return st;

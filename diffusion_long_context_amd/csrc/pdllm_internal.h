@@ -87,11 +87,15 @@ struct PrefillArgs {
   const void* q_win;
   void* o_chunk;
   float* key_score;
-  float* part_score;        // workspace [n_chunks][h_kv][slot_rows]
+  float* part_score;        // workspace [n_chunks][h_kv][parts][slot_rows]
   int32_t n_chunks, slot_rows, h_q, h_kv, group, w, chunks_per_win;
+  int32_t parts;            // partial key-score rows per (chunk, kv head)
   float scale_log2;
 };
 
+// partial key-score rows per (chunk, kv head): one per wavefront of the bf16
+// kernel, one for the f32 kernel; the workspace is sized for the larger
+constexpr int kPrefillParts = 8;
 int launch_prefill_bf16(const PrefillArgs& a, int d, void* stream);
 int launch_prefill_f32(const PrefillArgs& a, int d, void* stream);
 int launch_score_finalize(const PrefillArgs& a, void* stream);

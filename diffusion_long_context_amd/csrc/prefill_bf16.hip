@@ -6,8 +6,9 @@
 // Methodology 2: a chunk's rows are ranked by the cumulative attention weight
 // they receive from the query tokens):
 //   o_chunk[c,r,h]   = sum_j softmax_j(scale <q_chunk[c,r,h], K[slot,j,g]>) V[slot,j,g]
-//   part[c,g,j]      = sum_{h in group g} sum_w softmax_j(scale <q_win[w,h], K[slot,j,g]>)
-// and the finalize kernel sums part over g in a fixed order into key_score.
+//   part[c,g,p,j]    = sum over the window rows wave p handled (heads h in
+//                      group g) of softmax_j(scale <q_win[w,h], K[slot,j,g]>)
+// and the finalize kernel sums part over g, then p, in a fixed order into key_score.
 //
 // Design for CDNA4: one workgroup of 8 wavefronts per (chunk, kv head).  The
 // chunk's whole K and V (both row-major) for that kv head are staged into LDS
@@ -19,8 +20,9 @@
 // attention step (attn_tile.h, 32x32x16 MFMA) over 64-row kv steps;
 // window-row blocks run S = Q K^T on the 16x16x32 MFMA (which leaves each
 // lane one key column), an exact row softmax over all keys, and accumulate
-// each key's weight in registers.  Per-wave key sums meet in LDS and are
-// added in wave order.
+// each key's weight in registers.  Each wave writes its per-key sums as one
+// partial row; the finalize kernel adds them over waves and kv heads in a
+// fixed order.
 #include "attn_tile.h"
 #include "device_common.h"
 #include "pdllm_internal.h"
@@ -116,14 +118,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const uint16_t* k_lane = &sm.k[lc * KP + 8 * lh];
   const uint16_t* v_lane = &sm.v[v_lane_offset(lane, VP)];
 
+  // Query rows past the end (the last item's tail, or an item number past
+  // the last one) are clamped to the last row: those lanes compute the same
+  // output as the lane that owns it and store the same bytes to the same
+  // address, so loads and stores need no branch and the memory counter
+  // waits stay exact (the next item's query prefetch is not waited on
+  // together with this item's stores).
+  auto row_of = [&](int item) { return min(item * 32 + lc, n_rows_c - 1); };
   auto fetch_c = [&](int item, bf16x8 (&qf)[DC32]) {
-    const int x = item * 32 + lc;
-    if (x < n_rows_c) {
-      const int r = x / G, h = g * G + (x - r * G);
-      load_q<DC32, 16>(qf, qc + ((int64_t)r * a.h_q + h) * D + 8 * lh);
-    } else {
-      zero_q<DC32>(qf);
-    }
+    const int x = row_of(item);
+    const int r = x / G, h = g * G + (x - r * G);
+    load_q<DC32, 16>(qf, qc + ((int64_t)r * a.h_q + h) * D + 8 * lh);
   };
   auto attend = [&](int item, const bf16x8 (&qf)[DC32]) {
     __builtin_amdgcn_sched_barrier(0);     // keep items apart: no cross-item hoisting
@@ -141,11 +146,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       at.template step<1>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, R - kv0, lh);
     }
     const float l = at.row_sum();
-    const int x = item * 32 + lc;
-    if (x < n_rows_c) {
-      const int r = x / G, h = g * G + (x - r * G);
-      store_o_bf16<Attn::DB>(oc + ((int64_t)r * a.h_q + h) * D + 4 * lh, at.acc, 1.f / l);
-    }
+    const int x = row_of(item);
+    const int r = x / G, h = g * G + (x - r * G);
+    store_o_bf16<Attn::DB>(oc + ((int64_t)r * a.h_q + h) * D + 8 * lh, at.acc, 1.f / l);
   };
   // ---- phase 1: window-row items, a fixed round-robin over waves (so the
   // per-key sums are added in a fixed order).  S = Q K^T on the 16x16x32 MFMA
@@ -233,6 +236,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   }
 
+  // per-key sums of this wave: across its 4 lane groups, then one row of
+  // the partial key scores (the finalize kernel adds the waves and kv heads
+  // in a fixed order)
+  {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      colsum[kb] = wave_xor_sum(colsum[kb], 16);
+      colsum[kb] = wave_xor_sum(colsum[kb], 32);
+    }
+    float* part = a.part_score + (((int64_t)c * a.h_kv + g) * a.parts + wave) * R;
+    if (lj == 0) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        if (16 * kb + lr < R) part[16 * kb + lr] = colsum[kb];
+    }
+  }
+
   // ---- phase 2: chunk-row items, 32 (row, grouped head) pairs each, handed
   // out dynamically (each item's output does not depend on which wave runs
   // it), which evens out the window items and the waves' unequal issue
@@ -242,51 +262,44 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     if (lane == 0) v = atomicAdd(&sm.next_item, 1);
     return __builtin_amdgcn_readfirstlane(v);
   };
-  {
+  // The first pair is peeled so that the loop head sees the same pending
+  // memory operations from both paths: the loads of one item's queries,
+  // the stores of the item before it, the loads of the next item's queries.
+  if (wave < n_cb) {
     bf16x8 qa[DC32], qb[DC32];
     int item = wave;
-    if (item < n_cb) fetch_c(item, qa);
-    while (item < n_cb) {
-      const int nxt = grab();
-      if (nxt < n_cb) fetch_c(nxt, qb);
-      attend(item, qa);
-      if (nxt >= n_cb) break;
+    fetch_c(item, qa);
+    int nxt = grab();
+    fetch_c(nxt, qb);
+    attend(item, qa);
+    if (nxt < n_cb) {
       item = grab();
-      if (item < n_cb) fetch_c(item, qa);
-      attend(nxt, qb);
+      fetch_c(item, qa);
+      while (true) {
+        attend(nxt, qb);
+        if (item >= n_cb) break;
+        nxt = grab();
+        fetch_c(nxt, qb);
+        attend(item, qa);
+        if (nxt >= n_cb) break;
+        item = grab();
+        fetch_c(item, qa);
+      }
     }
-  }
-
-  // ---- per-key sums: across the 4 lane groups, then across waves in order
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    colsum[kb] = wave_xor_sum(colsum[kb], 16);
-    colsum[kb] = wave_xor_sum(colsum[kb], 32);
-  }
-  __syncthreads();                          // K/V no longer needed: reuse LDS
-  float* red = reinterpret_cast<float*>(sm.k);
-  if (lj == 0) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) red[wave * kMaxRows + 16 * kb + lr] = colsum[kb];
-  }
-  __syncthreads();
-  float* part = a.part_score + ((int64_t)c * a.h_kv + g) * R;
-  for (int j = tid; j < R; j += kThreads) {
-    float s = 0.f;
-    for (int w = 0; w < kWaves; ++w) s += red[w * kMaxRows + j];
-    part[j] = s;
   }
 }
 
-// key_score[c][j] = sum over kv heads g = 0 .. h_kv-1 (in that order) of part[c][g][j].
+// key_score[c][j] = sum over kv heads g = 0 .. h_kv-1 and, inside each, over
+// the partial rows p = 0 .. parts-1 (in that order) of part[c][g][p][j].
 __global__ __launch_bounds__(256) void score_finalize_kernel(const float* part, int n_chunks,
-                                                             int h_kv, int slot_rows,
+                                                             int h_kv, int parts, int slot_rows,
                                                              float* key_score) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)n_chunks * slot_rows) return;
   const int64_t c = idx / slot_rows, j = idx - c * slot_rows;
+  const float* pc = part + c * h_kv * parts * slot_rows + j;
   float s = 0.f;
-  for (int g = 0; g < h_kv; ++g) s += part[(c * h_kv + g) * slot_rows + j];
+  for (int q = 0; q < h_kv * parts; ++q) s += pc[(int64_t)q * slot_rows];
   key_score[idx] = s;
 }
 
@@ -322,7 +335,8 @@ int launch_score_finalize(const PrefillArgs& a, void* stream) {
   const int64_t n = (int64_t)a.n_chunks * a.slot_rows;
   if (n == 0) return (int)hipSuccess;
   hipLaunchKernelGGL(score_finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, a.part_score, a.n_chunks, a.h_kv, a.slot_rows, a.key_score);
+                     (hipStream_t)stream, a.part_score, a.n_chunks, a.h_kv, a.parts, a.slot_rows,
+                     a.key_score);
   return (int)hipGetLastError();
 }
 

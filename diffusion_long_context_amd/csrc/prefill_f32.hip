@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
     }
   }
   __syncthreads();
-  float* part = a.part_score + ((int64_t)c * a.h_kv + g) * R;
+  float* part = a.part_score + ((int64_t)c * a.h_kv + g) * a.parts * R;   // parts == 1
   for (int j = tid; j < R; j += kThreads) part[j] = colsum[j];
 }
 
