@@ -106,6 +106,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const uint16_t* rk = static_cast<const uint16_t*>(a.k_resp);
   const uint16_t* rv = static_cast<const uint16_t*>(a.v_resp);
 
+  // ---- queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc
+  // + 8 lj ..); rows past the end read the last row (never stored).  Issued
+  // first, so they arrive while the row table is built.
+  bf16x8 qf[DC];
+  const int qrow = qt * kRows + wave * 32 + lc;
+  {
+    const int qr = min(qrow, rows_total - 1);
+    const int i = qr / G, h = g * G + (qr - i * G);
+    load_q<DC, 16>(qf, static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
+  }
+
   // ---- row-pointer table for tiles [tw, tw + kTableTiles); rows past n_kv
   // point at the sequence's first response row (finite data, masked scores)
   auto build_table = [&](int tw) {
@@ -121,16 +132,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   };
   int tw = t_begin;
   build_table(tw);
-
-  // ---- queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc + 8 lj ..)
-  bf16x8 qf[DC];
-  const int qrow = qt * kRows + wave * 32 + lc;
-  if (qrow < rows_total) {
-    const int i = qrow / G, h = g * G + (qrow - i * G);
-    load_q<DC, 16>(qf, static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
-  } else {
-    zero_q<DC>(qf);
-  }
 
   // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values of
   // a tile.  K runs one tile ahead of V: load unit a carries K of tile a and
@@ -185,11 +186,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   __syncthreads();                         // row table ready
   fetch_ptrs(0, 0);
   load_unit(0);
-  store_k(0, 0);
-  store_v(0, 0);
-  fetch_ptrs(1, 1);
-  load_unit(0);
-  store_k(1, 0);
+  if constexpr (STAGES == 2) {             // tiles 0 and 1 in one memory round trip
+    fetch_ptrs(1, 1);
+    load_unit(1);
+    store_k(0, 0);
+    store_v(0, 0);
+    store_k(1, 1);
+  } else {
+    store_k(0, 0);
+    store_v(0, 0);
+    fetch_ptrs(1, 1);
+    load_unit(0);
+    store_k(1, 0);
+  }
 #pragma unroll
   for (int i = 0; i < STAGES; ++i) {
     fetch_ptrs(2 + i, 1 + i);
@@ -256,31 +265,49 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
                        at.acc, inv);
       if (a.lse != nullptr && lj == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
     } else {
-      store_o_f32<DB>(a.part_o + a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 4 * lj,
-                      at.acc, inv);
+      store_o_bf16<DB>(static_cast<uint16_t*>(a.part_o) + a.seq[si].part_off +
+                           (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 8 * lj,
+                       at.acc, inv);
       if (lj == 0) a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;
     }
   }
 }
 
 // LSE merge of the per-split partials ("Attention kernel optimization"):
-// lse = M + ln sum_j exp(lse_j - M), o = sum_j exp(lse_j - lse) o_j, rounded
-// once to the output type.  One thread per 4 output values of a row.
+// lse = M + ln sum_j exp(lse_j - M), o = sum_j exp(lse_j - lse) o_j, summed
+// in float32 and rounded once to the output type.  With BF16 the partial
+// outputs are bf16 (the bf16 decode kernel writes them so) and each thread
+// takes 8 values of a row, otherwise float32 and 4 values.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
+  constexpr int EPT = BF16 ? 8 : 4;        // values per thread (16 bytes of partial)
+  constexpr int TPR = D / EPT;
+  constexpr int RPB = 256 / TPR;
   const int si = blockIdx.y;
   if (si >= a.n_seq_launch) return;
   const int n_splits = a.seq[si].n_splits;
   if (n_splits <= 1) return;
-  constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
   const int rows = a.l_d * a.h_q;
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
-  const int e0 = 4 * (threadIdx.x % TPR);
+  const int e0 = EPT * (threadIdx.x % TPR);
   const float* pl = a.part_lse + a.seq[si].lse_off + row;
-  const float* po = a.part_o + a.seq[si].part_off + (int64_t)row * D + e0;
+  const int64_t po = a.seq[si].part_off + (int64_t)row * D + e0;   // element offset
   const int64_t sl = rows, so = (int64_t)rows * D;
+  auto load = [&](int j, float (&x)[EPT]) {
+    if constexpr (BF16) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + po + j * so);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+        x[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+      }
+    } else {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + po + j * so);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = w[q];
+    }
+  };
   // splits are visited in groups of kBatch so that the group's loads are in
   // flight together
   constexpr int kBatch = 8;
@@ -293,39 +320,44 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
     for (int u = 0; u < kBatch; ++u) mx = fmaxf(mx, t[u]);
   }
   float tot = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float o[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) o[e] = 0.f;
   for (int j0 = 0; j0 < n_splits; j0 += kBatch) {
     float t[kBatch];
-    f32x4 x[kBatch];
+    float x[kBatch][EPT];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const bool in = j0 + u < n_splits;
-      t[u] = in ? pl[(j0 + u) * sl] : -INFINITY;
-      x[u] = in ? *reinterpret_cast<const f32x4*>(po + (j0 + u) * so) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int j = min(j0 + u, n_splits - 1);   // past the end: a valid split, weight 0
+      t[u] = j0 + u < n_splits ? pl[j * sl] : -INFINITY;
+      load(j, x[u]);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float w = expf(t[u] - mx);    // 0 for an empty split (lse = -inf)
+      const float w = expf(t[u] - mx);    // 0 for an empty split (lse = -inf) and past the end
       tot += w;
-      o += w * x[u];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) o[e] += w * x[u][e];
     }
   }
-  o *= 1.f / tot;
+  const float inv = 1.f / tot;
   const int s = a.seq0 + si;
   const int i = row / a.h_q, h = row - i * a.h_q;
   const int64_t out = ((int64_t)s * rows + row) * D + e0;
   if constexpr (BF16) {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + out) =
-        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + out) =
+        u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+              pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + out) = o;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + out) =
+        f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   }
   if (a.lse != nullptr && e0 == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = mx + logf(tot);
 }
 
 template <int D, bool BF16>
 int merge_launch(const DecodeArgs& a, void* stream) {
-  constexpr int RPB = 256 / (D / 4);
+  constexpr int RPB = 256 / (D / (BF16 ? 8 : 4));
   const int rows = a.l_d * a.h_q;
   dim3 grid((rows + RPB - 1) / RPB, a.n_seq_launch);
   hipLaunchKernelGGL((lse_merge_kernel<D, BF16>), grid, dim3(256), 0, (hipStream_t)stream, a);

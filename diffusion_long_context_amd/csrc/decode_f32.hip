@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeArgs a) {
     for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
     if (a.lse != nullptr) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
   } else {
-    float* pp = a.part_o + a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D;
+    float* pp = static_cast<float*>(a.part_o) + a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D;
 #pragma unroll
     for (int e = 0; e < D; ++e) pp[e] = acc[e] * inv;
     a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;

@@ -334,8 +334,8 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
   pdllm::DecodeArgs a = base_decode_args(pool, pt, q, k_resp, v_resp, l_d, h_q, scale, o, lse);
   a.q_tiles = plan.q_tiles;
   if (plan.workspace_bytes > 0) {
-    a.part_o = static_cast<float*>(workspace);
-    const int64_t part_bytes = (plan.part_floats * 4 + 255) / 256 * 256;
+    a.part_o = workspace;
+    const int64_t part_bytes = (plan.part_floats * plan.part_elem_bytes + 255) / 256 * 256;
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
   }
   for (int s0 = 0; s0 < n_seq; s0 += pdllm::kMaxSeqPerLaunch) {

@@ -25,8 +25,9 @@ struct DecodePlan {
   int q_rows_per_wg = 0;   // query rows per workgroup
   int q_tiles = 0;         // workgroups along the query rows of one (seq, kv head)
   std::vector<int> k_s, n_kv, n_tiles, splits, tiles_per_split;
-  std::vector<int64_t> part_off, lse_off;   // float offsets into the workspace
-  int64_t part_floats = 0, lse_floats = 0;
+  std::vector<int64_t> part_off, lse_off;   // element offsets into the workspace
+  int64_t part_floats = 0, lse_floats = 0;  // element counts (partial O, partial lse)
+  int part_elem_bytes = 4;                  // partial O element: bf16 (2) or float32 (4)
   int64_t workspace_bytes = 0;
   int64_t total_workgroups = 0;
 };
@@ -44,7 +45,7 @@ struct DecodeSeq {
   int32_t tiles_per_split;
   int32_t wg_begin;         // first workgroup of this sequence in the launch
   int32_t pad_;
-  int64_t part_off;         // float offset of its partial outputs
+  int64_t part_off;         // element offset of its partial outputs
   int64_t lse_off;          // float offset of its partial lse values
 };
 
@@ -60,7 +61,7 @@ struct DecodeArgs {
   const void* v_resp;
   void* o;
   float* lse;
-  float* part_o;
+  void* part_o;             // bf16 partials (bf16 kernel) or float32 (f32 kernel)
   float* part_lse;
   int32_t n_chunks_per_seq, k_max, b;
   int32_t l_d, h_q, h_kv, group;

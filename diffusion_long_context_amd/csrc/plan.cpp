@@ -135,7 +135,8 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
   }
   p.part_floats = part;
   p.lse_floats = lse;
-  p.workspace_bytes = part ? align256(part * 4) + align256(lse * 4) : 0;
+  p.part_elem_bytes = dtype == 1 ? 2 : 4;   // bf16 partial outputs for bf16 inputs
+  p.workspace_bytes = part ? align256(part * p.part_elem_bytes) + align256(lse * 4) : 0;
   *plan = std::move(p);
   return true;
 }

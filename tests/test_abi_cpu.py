@@ -153,8 +153,8 @@ def test_plan_properties(ks, b, l_d, g, dtype):
             assert (splits[s] - 1) * tps[s] < n_tiles <= splits[s] * tps[s]
             if num_splits:
                 assert splits[s] <= min(num_splits, n_tiles)
-            if splits[s] > 1:
-                need += splits[s] * l_d * h_q * (d + 1) * 4
+            if splits[s] > 1:   # partial O (bf16 for bf16 inputs, else float32) + float32 lse
+                need += splits[s] * l_d * h_q * (d * (2 if dtype else 4) + 4)
         assert (ws == 0) == (need == 0) and ws >= need
 
 
