@@ -176,13 +176,17 @@ struct WaveAttn {
   }
 
   // (3) O^T += V^T P^T.  v_lane = V + v_lane_offset(lane, VP) (row-major V,
-  // pitch VP).
+  // pitch VP).  Only the first n16 16-row pieces are accumulated: the caller
+  // passes fewer when the rest hold only masked rows (p = 0 against zero V
+  // rows, so skipping them changes nothing).
   template <int NK>
-  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2 * NK], const uint16_t* __restrict__ v_lane) {
+  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2 * NK], const uint16_t* __restrict__ v_lane,
+                                     int n16 = 2 * NK) {
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        if (2 * kb + h >= n16) break;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const uint16_t* vp = v_lane + (32 * kb + 16 * h) * VP + 32 * db;
@@ -205,7 +209,7 @@ struct WaveAttn {
     qk<NK>(sc, k_lane, qf);
     prep<NK>(sc, sl2, valid_hi, j, valid_lo);
     exp_qk<NK, false>(sc, pf, sc, nullptr, qf, sl2);
-    pv<NK>(pf, v_lane);
+    pv<NK>(pf, v_lane, min(2 * NK, (valid_hi + 15) >> 4));
   }
 
   // Full row sum (both kv halves) and natural-log normaliser.

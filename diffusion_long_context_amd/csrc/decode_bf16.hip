@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
     else
       at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
-    at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP));
+    at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
     __syncthreads();
   };
   {

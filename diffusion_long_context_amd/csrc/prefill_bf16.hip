@@ -298,8 +298,18 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(const float* part, 
   if (idx >= (int64_t)n_chunks * slot_rows) return;
   const int64_t c = idx / slot_rows, j = idx - c * slot_rows;
   const float* pc = part + c * h_kv * parts * slot_rows + j;
+  const int n = h_kv * parts;
+  // loads in groups of 16 (all in flight together), added in index order
+  constexpr int kGroup = 16;
   float s = 0.f;
-  for (int q = 0; q < h_kv * parts; ++q) s += pc[(int64_t)q * slot_rows];
+  for (int q0 = 0; q0 < n; q0 += kGroup) {
+    float x[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) x[u] = q0 + u < n ? pc[(int64_t)(q0 + u) * slot_rows] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+      if (q0 + u < n) s += x[u];
+  }
   key_score[idx] = s;
 }
 
