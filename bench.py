@@ -65,12 +65,12 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "c1760fe69320021e",
+    "sources_sha": "6b0d0b4e1562772a",
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149118.97, "write_kib": 233352.44},
-        "score_finalize_kernel": {"fetch_kib": 326.19, "write_kib": 128.5},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149199.56, "write_kib": 235000.80},
+        "score_finalize_kernel": {"fetch_kib": 2551.44, "write_kib": 128.5},
     },
-    "copy_fetch_kib": 524301.26,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.21,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 
