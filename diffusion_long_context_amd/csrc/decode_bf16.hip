@@ -32,13 +32,16 @@ namespace pdllm {
 namespace {
 
 constexpr int kTile = kDecodeTile;         // kv rows per tile
-constexpr int kTableTiles = 8;             // row-pointer table capacity (tiles)
 
-template <int D>
+// LDS of one workgroup.  The 8-wave variant (one workgroup per CU) uses the
+// V pitch that keeps the transposing reads conflict-free on the 64-bank LDS
+// (4 rows x 64 B per 32 lanes) and an 8-tile row table; the 4-wave variant
+// stays under half of the 160 KiB so two workgroups share a CU.
+template <int D, int WAVES>
 struct Smem {
   static constexpr int KP = D + 8;         // K pitch (elements): 8-row 16-byte reads conflict-free
-  static constexpr int VP = D + 32;        // V pitch (elements): transposing reads conflict-free
-                                           // on the 64-bank LDS (4 rows x 64 B per 32 lanes)
+  static constexpr int VP = WAVES == 8 ? D + 32 : D + 16;   // V pitch (elements)
+  static constexpr int kTableTiles = WAVES == 8 ? 8 : 4;    // row-table capacity (tiles)
   uint16_t k[2][kTile * KP];               // double-buffered tiles, both row-major
   uint16_t v[2][kTile * VP];
   gptr16 kptr[kTableTiles * kTile];        // K / V address of each attended row
@@ -69,8 +72,9 @@ template <int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 32 * WAVES;        // query rows of the workgroup
-  __shared__ Smem<D> sm;
-  constexpr int KP = Smem<D>::KP, VP = Smem<D>::VP;
+  __shared__ Smem<D, WAVES> sm;
+  constexpr int KP = Smem<D, WAVES>::KP, VP = Smem<D, WAVES>::VP;
+  constexpr int kTableTiles = Smem<D, WAVES>::kTableTiles;
   using Attn = WaveAttn<D, KP, VP>;
   constexpr int DC = Attn::DC, DB = Attn::DB;
   constexpr int TPR = D / 8;               // loader threads per kv row (16 B each)
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
   };
   // splits are visited in groups of kBatch so that the group's loads are in
   // flight together
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   float mx = -INFINITY;
   for (int j0 = 0; j0 < n_splits; j0 += kBatch) {
     float t[kBatch];
