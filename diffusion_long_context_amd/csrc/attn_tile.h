@@ -43,7 +43,7 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 // lane-wise combines each lane with its partner (a VALU op, no LDS trip).
 __device__ __forceinline__ float max_halves(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -116,11 +116,11 @@ struct WaveAttn {
           if ((unsigned)(r - valid_lo) >= span) sc[kb][i] = -INFINITY;
         }
     }
-    float mx = fmaxf(sc[0][0], sc[0][1]);
+    float mx = max_f(sc[0][0], sc[0][1]);
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-      for (int i = kb ? 0 : 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[kb][i]), sc[kb][i + 1]);
+      for (int i = kb ? 0 : 2; i < 16; i += 2) mx = max_f(max_f(mx, sc[kb][i]), sc[kb][i + 1]);
     mx = max_halves(mx);
     const float ms = mx * sl2;
     const bool need = ms > m_run + kRescaleLog2;

@@ -312,18 +312,12 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
       for (int q = 0; q < 4; ++q) x[q] = w[q];
     }
   };
-  // splits are visited in groups of kBatch so that the group's loads are in
-  // flight together
+  // Splits are visited in groups of kBatch whose lse and partial loads are
+  // all in flight together (one memory round trip per group; the S32 plans
+  // have one group).  The weights of a group are taken against the running
+  // maximum, and the sums of earlier groups are rescaled when it grows.
   constexpr int kBatch = 16;
-  float mx = -INFINITY;
-  for (int j0 = 0; j0 < n_splits; j0 += kBatch) {
-    float t[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) t[u] = j0 + u < n_splits ? pl[(j0 + u) * sl] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) mx = fmaxf(mx, t[u]);
-  }
-  float tot = 0.f;
+  float mx = -INFINITY, tot = 0.f;
   float o[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) o[e] = 0.f;
@@ -336,13 +330,23 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
       t[u] = j0 + u < n_splits ? pl[j * sl] : -INFINITY;
       load(j, x[u]);
     }
+    float m_new = mx;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) m_new = fmaxf(m_new, t[u]);
+    // every split so far empty (lse = -inf): weigh against 0, all weights are 0
+    const float ref = m_new == -INFINITY ? 0.f : m_new;
+    const float c = expf(mx - ref);            // 0 on the first group
+    tot *= c;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) o[e] *= c;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float w = expf(t[u] - mx);    // 0 for an empty split (lse = -inf) and past the end
+      const float w = expf(t[u] - ref);        // 0 for an empty split and past the end
       tot += w;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) o[e] += w * x[u][e];
     }
+    mx = m_new;
   }
   const float inv = 1.f / tot;
   const int s = a.seq0 + si;

@@ -39,11 +39,41 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// max(a, b) as v_maximum3_f32.  fmaxf (IEEE maxNum) makes the compiler
+// quiet each operand it cannot prove canonical first -- every MFMA result
+// and every lane-permuted value -- with one extra VALU op per operand; the
+// IEEE 754-2019 maximum needs none.  The two differ only on NaN operands
+// (maximum returns the NaN), which the softmax inputs never hold.
+__device__ __forceinline__ float max_f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+  return max_f(v, __shfl_xor(v, mask, 64));
 }
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
+}
+
+// Lane v of the same 16-lane DPP row picked by CTRL (quad_perm, row mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+// Butterfly over the 16 lanes of a DPP row: xor 1, xor 2 (quad permutes),
+// then lane i with 7 - i (half mirror) and with 15 - i (mirror).  Each step
+// pairs lanes that already hold equal partial results, so every lane of the
+// row ends with the same bits.
+__device__ __forceinline__ float row16_max(float v) {
+  v = max_f(v, dpp_row<0xB1>(v));
+  v = max_f(v, dpp_row<0x4E>(v));
+  v = max_f(v, dpp_row<0x141>(v));
+  return max_f(v, dpp_row<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_row<0xB1>(v);
+  v += dpp_row<0x4E>(v);
+  v += dpp_row<0x141>(v);
+  return v + dpp_row<0x140>(v);
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id % 8).  Remap

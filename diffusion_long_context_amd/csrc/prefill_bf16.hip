@@ -64,6 +64,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int lr = lane & 15, lj = lane >> 4;  // 16x16 layout (window items)
   const int G = a.group;
   const float sl2 = a.scale_log2;
+  const int n_rows_w = a.w * G;
+  const int n_wb = (n_rows_w + 31) / 32;
+  const uint16_t* qw = static_cast<const uint16_t*>(a.q_win) +
+                       (int64_t)(c / a.chunks_per_win) * a.w * a.h_q * D;
+  // Window items are 32 (window row, grouped head) pairs, wave w taking
+  // w, w + 8, ...; rows past the end clamp to the last row (their weight is
+  // zero), so every fetch is unconditional and the memory waits stay exact.
+  auto fetch_w = [&](int witem, bf16x8 (&qf)[2][DC]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int x = min(witem * 32 + 16 * b + lr, n_rows_w - 1);
+      const int r = x / G, h = g * G + (x - r * G);
+      load_q<DC, 32>(qf[b], qw + ((int64_t)r * a.h_q + h) * D + 8 * lj);
+    }
+  };
+  // the first window item's queries load together with the staging
+  bf16x8 qw_cur[2][DC];
+  if (n_wb > 0) fetch_w(min(wave, n_wb - 1), qw_cur);
 
   // ---- stage the chunk's K and V (rows >= R are zero); every load is issued
   // before the first LDS store so the staging costs one memory round trip
@@ -105,12 +123,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 
   const int n_rows_c = R * G;
   const int n_cb = (n_rows_c + 31) / 32;
-  const int n_rows_w = a.w * G;
-  const int n_wb = (n_rows_w + 31) / 32;
-  const int n_items = n_cb + n_wb;
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_chunk) + (int64_t)c * R * a.h_q * D;
-  const uint16_t* qw = static_cast<const uint16_t*>(a.q_win) +
-                       (int64_t)(c / a.chunks_per_win) * a.w * a.h_q * D;
   uint16_t* oc = static_cast<uint16_t*>(a.o_chunk) + (int64_t)c * R * a.h_q * D;
   using Attn = WaveAttn<D, KP, VP>;
   constexpr int DC32 = Attn::DC;            // 16-wide d chunks (32x32x16 MFMA)
@@ -158,19 +171,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) colsum[kb] = 0.f;
   const uint16_t* k16 = &sm.k[lr * KP + 8 * lj];
-  for (int item = n_cb + wave; item < n_items; item += kWaves) {
-    const int first = (item - n_cb) * 32;
+  for (int witem = wave; witem < n_wb; witem += kWaves) {
+    const int first = witem * 32;
     bf16x8 qf[2][DC];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int x = first + 16 * b + lr;
-      if (x < n_rows_w) {
-        const int r = x / G, h = g * G + (x - r * G);
-        load_q<DC, 32>(qf[b], qw + ((int64_t)r * a.h_q + h) * D + 8 * lj);
-      } else {
-        zero_q<DC>(qf[b]);
-      }
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) qf[b][dc] = qw_cur[b][dc];
+    // the next item's queries (this one's again on the last pass) load
+    // while this one computes
+    fetch_w(min(witem + kWaves, n_wb - 1), qw_cur);
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -201,14 +211,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       float mx[4], sum[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float m = fmaxf(sw[0][e], sw[1][e]);
+        float m = max_f(sw[0][e], sw[1][e]);
 #pragma unroll
-        for (int kb = 2; kb < NKB; kb += 2) m = fmaxf(fmaxf(m, sw[kb][e]), sw[kb + 1][e]);
-        m = wave_xor_max(m, 1);
-        m = wave_xor_max(m, 2);
-        m = wave_xor_max(m, 4);
-        m = wave_xor_max(m, 8);
-        mx[e] = -m * sl2;
+        for (int kb = 2; kb < NKB; kb += 2) m = max_f(max_f(m, sw[kb][e]), sw[kb + 1][e]);
+        mx[e] = -row16_max(m) * sl2;
         sum[e] = 0.f;
       }
 #pragma unroll
@@ -222,12 +228,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       float wgt[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float t = sum[e];
-        t = wave_xor_sum(t, 1);
-        t = wave_xor_sum(t, 2);
-        t = wave_xor_sum(t, 4);
-        t = wave_xor_sum(t, 8);
-        wgt[e] = first + 16 * b + 4 * lj + e < n_rows_w ? 1.f / t : 0.f;
+        const float t = row16_sum(sum[e]);
+        wgt[e] = first + 16 * b + 4 * lj + e < n_rows_w ? __builtin_amdgcn_rcpf(t) : 0.f;
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
