@@ -110,17 +110,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const uint16_t* rk = static_cast<const uint16_t*>(a.k_resp);
   const uint16_t* rv = static_cast<const uint16_t*>(a.v_resp);
 
-  // ---- queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc
-  // + 8 lj ..); rows past the end read the last row (never stored).  Issued
-  // first, so they arrive while the row table is built.
-  bf16x8 qf[DC];
-  const int qrow = qt * kRows + wave * 32 + lc;
-  {
-    const int qr = min(qrow, rows_total - 1);
-    const int i = qr / G, h = g * G + (qr - i * G);
-    load_q<DC, 16>(qf, static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
-  }
-
   // ---- row-pointer table for tiles [tw, tw + kTableTiles); rows past n_kv
   // point at the sequence's first response row (finite data, masked scores)
   auto build_table = [&](int tw) {
@@ -135,7 +124,44 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     }
   };
   int tw = t_begin;
-  build_table(tw);
+
+  // ---- first fill of the row table, and the queries.  Each thread resolves
+  // at most one row.  Its two dependent index loads (sel_chunk, then
+  // chunk_slot and keep_rows) read clamped, always valid addresses, so they
+  // are unconditional; the query loads are issued after the second pair.
+  // Loads retire in issue order, so the wait for the indices does not
+  // include the queries, which arrive while the table is written and the
+  // first tiles are fetched.
+  bf16x8 qf[DC];
+  const int qrow = qt * kRows + wave * 32 + lc;
+  {
+    static_assert(kTableTiles * kTile == kThreads, "one table row per thread");
+    typedef __attribute__((address_space(1))) const int32_t* gptr32;
+    const int nrow = (min(tw + kTableTiles, t_end) - tw) * kTile;
+    const int per = a.b + 1;
+    const int v = max(0, min(tw * kTile + min(tid, nrow - 1), n_kv - 1));
+    const int kk = min(v / per, max(k_s - 1, 0));
+    const int r = min(v - kk * per, per - 1);   // BOS row 0, then kept rows 1..b
+    const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : a.chunk_slot);
+    const int cg = s * a.n_chunks_per_seq + min(max(c0, 0), a.n_chunks_per_seq - 1);
+    const int slot = *(gptr32)(a.chunk_slot + cg);
+    const int krow = *(gptr32)(a.b > 0 ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0) : a.chunk_slot);
+    __builtin_amdgcn_sched_barrier(0);     // the index loads go out before the queries
+    // queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc
+    // + 8 lj ..); rows past the end read the last row (never stored)
+    {
+      const int qr = min(qrow, rows_total - 1);
+      const int i = qr / G, h = g * G + (qr - i * G);
+      load_q<DC, 16>(qf, static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
+    }
+    // every entry is written (those past nrow hold a valid clamped row and are
+    // never read), so the index values have one unconditional use
+    const bool pool = v < k_s * per;
+    const int64_t e = pool ? (int64_t)slot * a.ps_slot + (int64_t)(r ? krow : 0) * a.ps_row + (int64_t)g * a.ps_head
+                           : (((int64_t)s * a.l_d + (v - k_s * per)) * a.h_kv + g) * D;
+    sm.kptr[tid] = (gptr16)((pool ? pk : rk) + e);
+    sm.vptr[tid] = (gptr16)((pool ? pv : rv) + e);
+  }
 
   // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values of
   // a tile.  K runs one tile ahead of V: load unit a carries K of tile a and
