@@ -65,12 +65,12 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "6b0d0b4e1562772a",
+    "sources_sha": "f055f4d8bdb5b1ad",
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149199.56, "write_kib": 235000.80},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149195.92, "write_kib": 234576.71},
         "score_finalize_kernel": {"fetch_kib": 2551.44, "write_kib": 128.5},
     },
-    "copy_fetch_kib": 524301.21,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.29,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 

@@ -80,7 +80,7 @@ def test_small_shapes(device, name, kw):
             _compare(o, lse, ro, rlse, cfg, f"{name} seed {seed} splits {ns}")
 
 
-@pytest.mark.parametrize("name", ["s8", "s32"])
+@pytest.mark.parametrize("name", ["s8", "s32", "f32"])
 def test_full_size_single_sequence(device, name):
     cfg = synth.config(name)
     inp = synth.generate(cfg, 0)
