@@ -86,6 +86,9 @@ def parse():
                    help="run only a plain device copy of COPY_BYTES (byte-counter scale)")
     p.add_argument("--decode-only", action="store_true",
                    help="time only the decode call (diagnostic; not the headline step)")
+    p.add_argument("--chunk", type=int, default=0,
+                   help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
+                        "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
     return p.parse_args()
 
 
@@ -175,6 +178,56 @@ def cpu_baseline(cfg, inp, min_seconds=10.0):
             "seconds": dt}
 
 
+def chunk_variant(args):
+    """Prefill side of a 32K prefix at another chunk size: one JSON line with
+    the stage time and its algorithmic TFLOP/s and GB/s (diagnostic)."""
+    import torch
+    import synth
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    c = args.chunk
+    if c < 1 or 32768 % c:
+        sys.exit("--chunk must divide 32768")
+    cfg = synth.config("s32", chunk=c, n_chunks=32768 // c, b=min(256, c))
+    inp = synth.generate(cfg, args.seed, with_q_chunk=True)
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    pool_k, pool_v, chunk_slot = to_dev(inp.pool_k), to_dev(inp.pool_v), to_dev(inp.chunk_slot)
+    q_chunk, q_win = to_dev(inp.q_chunk), to_dev(inp.q_win)
+    o_chunk = torch.empty_like(q_chunk)
+    key_score = torch.empty((cfg.n_slots, cfg.rows), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.lib.pdllm_prefill_score_workspace(cfg.n_slots, cfg.h_q, cfg.h_kv, cfg.rows, cfg.w),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        L.chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, cfg.n_chunks, cfg.scale,
+                              o_chunk=o_chunk, key_score=key_score, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / args.steps
+    flops, bytes_ = workload_counts(cfg)
+    print(json.dumps({"diagnostic": f"prefill side, 32K prefix in chunks of {c} (+BOS), 28/4 heads, d=128, "
+                                    f"window 64", "path": "one pass" if cfg.rows <= 288 else "streamed",
+                      "us": t * 1e6, "tflops": flops["prefill"] / t / 1e12,
+                      "gbs": bytes_["prefill"] / t / 1e9,
+                      "mfma_frac": flops["prefill"] / t / 1e12 / BF16_PEAK_TFLOPS,
+                      "hbm_frac": bytes_["prefill"] / t / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_flops": flops["prefill"], "algorithmic_bytes": bytes_["prefill"],
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,6 +238,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.chunk:
+        chunk_variant(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L
@@ -205,7 +261,7 @@ def main():
     q, k_resp, v_resp = to_dev(inp.q), to_dev(inp.k_resp), to_dev(inp.v_resp)
     o_chunk = torch.empty_like(q_chunk)
     key_score = torch.empty((cfg.n_slots, cfg.rows), dtype=torch.float32, device=dev)
-    ws_prefill = torch.empty(L.lib.pdllm_prefill_score_workspace(cfg.n_slots, cfg.h_kv, cfg.rows),
+    ws_prefill = torch.empty(L.lib.pdllm_prefill_score_workspace(cfg.n_slots, cfg.h_q, cfg.h_kv, cfg.rows, cfg.w),
                              dtype=torch.uint8, device=dev)
     keep = torch.empty((cfg.n_slots, cfg.b), dtype=torch.int32, device=dev)
     sel = torch.empty((cfg.n_seq, cfg.k_max), dtype=torch.int32, device=dev)

@@ -52,7 +52,7 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_abi_version.restype = ctypes.c_int
     lib.pdllm_last_error.restype = ctypes.c_char_p
     lib.pdllm_prefill_score_workspace.restype = sz
-    lib.pdllm_prefill_score_workspace.argtypes = [i32, i32, i32]
+    lib.pdllm_prefill_score_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.pdllm_chunk_prefill_score.restype = ctypes.c_int
     lib.pdllm_chunk_prefill_score.argtypes = [P(Pool), vp, i32, vp, i32, vp, i32, i32, f32, vp, vp,
                                               vp, sz, vp]
@@ -72,7 +72,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-ABI_VERSION = 1
+ABI_VERSION = 2
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -141,7 +141,7 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
         o_chunk = torch.empty_like(q_chunk)
     if key_score is None:
         key_score = torch.empty((n_chunks, rows), dtype=torch.float32, device=dev)
-    need = lib.pdllm_prefill_score_workspace(n_chunks, pool.h_kv, rows)
+    need = lib.pdllm_prefill_score_workspace(n_chunks, h_q, pool.h_kv, rows, w)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(lib.pdllm_chunk_prefill_score(ctypes.byref(pool), chunk_slot.data_ptr(), n_chunks,

@@ -165,10 +165,16 @@ int pdllm_abi_version(void) { return PDLLM_ABI_VERSION; }
 
 const char* pdllm_last_error(void) { return g_last_error.c_str(); }
 
-size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slot_rows) {
-  if (n_chunks < 0 || h_kv < 1 || slot_rows < 1) return 0;
-  const int64_t bytes = (int64_t)n_chunks * h_kv * pdllm::kPrefillParts * slot_rows * 4;
-  return (size_t)((bytes + 255) / 256 * 256);
+size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_q, int32_t h_kv, int32_t slot_rows,
+                                     int32_t w) {
+  if (n_chunks < 0 || h_kv < 1 || h_q < 1 || h_q % h_kv != 0 || slot_rows < 1 || w < 1) return 0;
+  const auto align = [](int64_t b) { return (b + 255) / 256 * 256; };
+  if (slot_rows <= pdllm::kPrefillMaxRows)   // resident kernel: per-wave partial key scores
+    return (size_t)align((int64_t)n_chunks * h_kv * pdllm::kPrefillParts * slot_rows * 4);
+  // streamed chunks: one partial row per (chunk, kv head), then the window
+  // rows' normalisers (w * group rows, padded to 32)
+  const int64_t rows_w = ((int64_t)w * (h_q / h_kv) + 31) / 32 * 32;
+  return (size_t)(align((int64_t)n_chunks * h_kv * slot_rows * 4) + align((int64_t)n_chunks * h_kv * rows_w * 4));
 }
 
 pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* chunk_slot,
@@ -184,17 +190,15 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
   if (w < 1 || chunks_per_win < 1)
     return fail(PDLLM_ERR_INVALID_ARG, "w and chunks_per_win must be >= 1 (got %d, %d)", w, chunks_per_win);
   if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
-  const int max_rows = pool->dtype == PDLLM_BF16 ? 257 : 4097;
-  if (pool->slot_rows > max_rows)
-    return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > %d is not supported for this dtype",
-                pool->slot_rows, max_rows);
+  if (pool->slot_rows > 4097)
+    return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > 4097 is not supported", pool->slot_rows);
   if (n_chunks == 0) return ok();
   if (chunk_slot == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot is NULL");
   if ((st = check_tensor(q_chunk, "q_chunk")) != PDLLM_OK) return st;
   if ((st = check_tensor(q_win, "q_win")) != PDLLM_OK) return st;
   if ((st = check_tensor(o_chunk, "o_chunk")) != PDLLM_OK) return st;
   if ((st = check_tensor(key_score, "key_score")) != PDLLM_OK) return st;
-  const size_t need = pdllm_prefill_score_workspace(n_chunks, pool->h_kv, pool->slot_rows);
+  const size_t need = pdllm_prefill_score_workspace(n_chunks, h_q, pool->h_kv, pool->slot_rows, w);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -220,9 +224,15 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
   a.w = w;
   a.chunks_per_win = chunks_per_win;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.parts = pool->dtype == PDLLM_BF16 ? pdllm::kPrefillParts : 1;
-  const int err = pool->dtype == PDLLM_BF16 ? pdllm::launch_prefill_bf16(a, pool->d, stream)
-                                             : pdllm::launch_prefill_f32(a, pool->d, stream);
+  const bool streamed = pool->dtype == PDLLM_BF16 && pool->slot_rows > pdllm::kPrefillMaxRows;
+  a.parts = pool->dtype == PDLLM_BF16 && !streamed ? pdllm::kPrefillParts : 1;
+  if (streamed) {
+    const int64_t part_bytes = ((int64_t)n_chunks * pool->h_kv * pool->slot_rows * 4 + 255) / 256 * 256;
+    a.win_norm = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
+  }
+  const int err = pool->dtype == PDLLM_F32 ? pdllm::launch_prefill_f32(a, pool->d, stream)
+                  : streamed               ? pdllm::launch_prefill_stream(a, pool->d, stream)
+                                           : pdllm::launch_prefill_bf16(a, pool->d, stream);
   if ((st = hip_status(err, "chunk prefill launch")) != PDLLM_OK) return st;
   if ((st = hip_status(pdllm::launch_score_finalize(a, stream), "score finalize launch")) != PDLLM_OK)
     return st;

@@ -89,6 +89,7 @@ struct PrefillArgs {
   void* o_chunk;
   float* key_score;
   float* part_score;        // workspace [n_chunks][h_kv][parts][slot_rows]
+  float* win_norm;          // streaming path: workspace [n_chunks][h_kv][w * group padded to 32]
   int32_t n_chunks, slot_rows, h_q, h_kv, group, w, chunks_per_win;
   int32_t parts;            // partial key-score rows per (chunk, kv head)
   float scale_log2;
@@ -99,6 +100,9 @@ struct PrefillArgs {
 constexpr int kPrefillParts = 8;
 int launch_prefill_bf16(const PrefillArgs& a, int d, void* stream);
 int launch_prefill_f32(const PrefillArgs& a, int d, void* stream);
+// bf16 chunks longer than the on-chip limit (kPrefillMaxRows), streamed
+int launch_prefill_stream(const PrefillArgs& a, int d, void* stream);
+constexpr int kPrefillMaxRows = 288;     // bf16 rows the resident kernel holds in LDS
 int launch_score_finalize(const PrefillArgs& a, void* stream);
 
 // ---------------------------------------------------------------- select

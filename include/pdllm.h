@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 1
+#define PDLLM_ABI_VERSION 2
 
 typedef enum {
   PDLLM_OK = 0,
@@ -104,9 +104,11 @@ typedef struct {
  * Prefill side                                                              *
  * ------------------------------------------------------------------------ */
 
-/* Bytes of workspace pdllm_chunk_prefill_score needs (0 when the arguments
+/* Bytes of workspace pdllm_chunk_prefill_score needs for the same n_chunks,
+ * h_q, h_kv (the pool's), slot_rows (the pool's) and w (0 when the arguments
  * are invalid).  Pure host function. */
-size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slot_rows);
+size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_q, int32_t h_kv, int32_t slot_rows,
+                                     int32_t w);
 
 /*
  * Chunk-local bidirectional attention with fused per-key scoring
@@ -125,10 +127,13 @@ size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_kv, int32_t slo
  *              key_score[c,j] = sum_h sum_w softmax_j(scale <q_win[.,w,h], K[s,j,g]>)
  *              (the window rows' softmax runs over the chunk's own rows only)
  *   chunk_slot device [n_chunks]
- *   workspace  device, >= pdllm_prefill_score_workspace(n_chunks, h_kv, slot_rows)
- * Supported: f32 with d in {16, 32, 64, 128} and slot_rows <= 4097; bf16
- * with d in {64, 128} and slot_rows <= 257 (the chunk's K and V are held on
- * chip).
+ *   workspace  device, >= pdllm_prefill_score_workspace(n_chunks, h_q, h_kv, slot_rows, w),
+ *              16-byte aligned
+ * Supported: slot_rows <= 4097 (chunk sizes up to 4096 plus BOS); f32 with d
+ * in {16, 32, 64, 128}; bf16 with d in {64, 128}.  For bf16, a chunk of up
+ * to 288 rows is held on chip in one pass; longer chunks stream their K and
+ * V through on-chip tiles, and their window rows make a second pass (their
+ * softmax normalisers first, then the per-key weights) -- the same results.
  * The per-key sums are reduced in a fixed order: results are bitwise
  * reproducible run to run.
  */

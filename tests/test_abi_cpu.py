@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 1
+    assert L.lib.pdllm_abi_version() == 2
 
 
 def _pool(**kw):
@@ -114,9 +114,16 @@ def test_prefill_validation():
     assert f(*args(w=0)) == INVALID
     assert f(*args(cpw=0)) == INVALID
     assert f(*args()) == WS_SMALL
-    need = L.lib.pdllm_prefill_score_workspace(128, 4, 257)
-    assert need >= 128 * 4 * 257 * 4
-    assert f(*args(pool=_pool(slot_rows=300, stride_slot=300 * 512))) == UNSUPPORTED
+    ws = L.lib.pdllm_prefill_score_workspace
+    need = ws(128, 28, 4, 257, 64)
+    assert need >= 128 * 4 * 8 * 257 * 4                      # per-wave partial rows
+    # streamed chunks: one partial row per (chunk, kv head) + the window normalisers
+    need_s = ws(8, 28, 4, 4097, 64)
+    assert need_s >= 8 * 4 * 4097 * 4 + 8 * 4 * 448 * 4
+    assert ws(8, 28, 4, 4097, 0) == 0 and ws(8, 30, 4, 4097, 64) == 0
+    assert f(*args(pool=_pool(slot_rows=1025, stride_slot=1025 * 512), ws=0x100000,
+                   ws_bytes=ws(128, 28, 4, 1025, 64) - 1)) == WS_SMALL
+    assert f(*args(pool=_pool(slot_rows=4098, stride_slot=4098 * 512))) == UNSUPPORTED
     assert f(*args(n=0)) == OK                       # nothing to do, nothing enqueued
 
 

@@ -64,6 +64,47 @@ def test_small_shapes(device, name, kw):
     _check_prefill(inp, cfg, what=name)
 
 
+# Chunks longer than the 288 rows the one-pass kernel holds on chip stream
+# their K and V instead: one row past that limit, the chunk sizes of the
+# method's trade-off study (512 .. 4096), d = 64, window row counts that are
+# not a multiple of 32, and a single window row.
+STREAMED = [
+    ("c288", dict(h_q=7, h_kv=1, d=128, n_chunks=2, chunk=288, w=64)),
+    ("c512_g2", dict(h_q=4, h_kv=2, d=128, n_chunks=3, chunk=512, w=16)),
+    ("c1024_g7", dict(h_q=7, h_kv=1, d=128, n_chunks=2, chunk=1024, w=64)),
+    ("c2048_d64", dict(h_q=4, h_kv=2, d=64, n_chunks=2, chunk=2048, w=9)),
+    ("c4096", dict(h_q=2, h_kv=1, d=128, n_chunks=2, chunk=4096, w=40)),
+    ("c700_w1", dict(h_q=3, h_kv=3, d=128, n_chunks=2, chunk=700, w=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw", STREAMED, ids=[s[0] for s in STREAMED])
+def test_streamed_chunks(device, name, kw):
+    base = dict(name=name, dtype="bf16", k_per_seq=(1,), b=1, l_d=max(kw.get("w", 4), 4), n_seq=1)
+    base.update(kw)
+    cfg = synth.Config(**base)
+    inp = synth.generate(cfg, 11, with_q_chunk=True)
+    say(f"streamed prefill {name} (slot rows {cfg.rows})")
+    o, ks = _check_prefill(inp, cfg, what=name)
+    o2, ks2 = _prefill_gpu(inp, cfg)
+    assert np.array_equal(host(o), host(o2)) and np.array_equal(host(ks), host(ks2)), "not reproducible"
+
+
+def test_streamed_identical_keys(device):
+    """All keys equal: every window weight is 1/R, so every score is W h_q / R,
+    and every chunk row's output is the mean of the slot's V rows."""
+    cfg = synth.Config("same_long", 7, 1, 128, "bf16", 2, 600, (1,), 1, 24, 24)
+    inp = synth.generate(cfg, 2, with_q_chunk=True)
+    inp.pool_k[:] = inp.pool_k[0, 0]
+    o, ks = _prefill_gpu(inp, cfg)
+    assert np.allclose(host(ks), cfg.w * cfg.h_q / cfg.rows, rtol=1e-5, atol=0)
+    vmean = oracle.as_f64(inp.pool_v).mean(axis=1)            # [n_slots][h_kv][d]
+    og = host(o).astype(np.float64)
+    for c in range(cfg.n_chunks):
+        want = vmean[inp.chunk_slot[c], 0]
+        assert np.abs(og[c] - want).max() <= 2e-2, f"chunk {c}"
+
+
 def test_s32_sampled_chunks(device):
     cfg = synth.config("s32")
     say("s32 prefill: generating")
