@@ -86,6 +86,9 @@ def parse():
                    help="run only a plain device copy of COPY_BYTES (byte-counter scale)")
     p.add_argument("--decode-only", action="store_true",
                    help="time only the decode call (diagnostic; not the headline step)")
+    p.add_argument("--full-step", action="store_true",
+                   help="diagnostic: decode side of one denoising step of the 28-layer 32K run "
+                        "(28 decode calls over distinct layer pools, one HIP graph, replayed)")
     p.add_argument("--chunk", type=int, default=0,
                    help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
                         "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
@@ -228,6 +231,66 @@ def chunk_variant(args):
                       "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def full_step(args):
+    """Decode side of the full denoising run at a 32K prefix: every step makes
+    one decode call per layer (28 layers, each with its own pool, queries and
+    response K/V; K = 16, B = 128, L_d = 256).  The 28 calls are captured in one
+    HIP graph, which is replayed once per denoising step (diagnostic line)."""
+    import torch
+    import synth
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    cfg = synth.config("f32")
+    sel_h, keep_h = synth.random_page_table(cfg, args.seed)
+    sel = torch.from_numpy(np.ascontiguousarray(sel_h)).to(dev)
+    keep = torch.from_numpy(np.ascontiguousarray(keep_h)).to(dev)
+    chunk_slot = torch.from_numpy(np.ascontiguousarray(
+        np.random.default_rng(args.seed).permutation(cfg.n_slots).astype(np.int32))).to(dev)
+    gen = torch.Generator(device=dev)
+    calls = []
+    for layer in range(cfg.layers):
+        gen.manual_seed(args.seed * 1000 + layer)
+
+        def rnd(*shape):
+            return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        pool_k = rnd(cfg.n_slots, cfg.rows, cfg.h_kv, cfg.d)
+        pool_v = rnd(cfg.n_slots, cfg.rows, cfg.h_kv, cfg.d)
+        q = rnd(cfg.n_seq, cfg.l_d, cfg.h_q, cfg.d)
+        k_resp = rnd(cfg.n_seq, cfg.l_d, cfg.h_kv, cfg.d)
+        v_resp = rnd(cfg.n_seq, cfg.l_d, cfg.h_kv, cfg.d)
+        calls.append(L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp,
+                              cfg.scale))
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(cfg.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / cfg.steps
+    flops, _ = workload_counts(cfg)
+    step_flops = flops["decode"] * cfg.layers
+    print(json.dumps({"diagnostic": f"decode side of one denoising step: {cfg.layers} layers x one decode call "
+                                    f"(32K prefix, K=16, B=128, L_d=256), one HIP graph per step, "
+                                    f"{cfg.steps} steps replayed", "us_per_step": t * 1e6,
+                      "us_per_layer": t * 1e6 / cfg.layers, "tflops": step_flops / t / 1e12,
+                      "mfma_frac": step_flops / t / 1e12 / BF16_PEAK_TFLOPS,
+                      "us_per_run": t * 1e6 * cfg.steps, "algorithmic_flops_per_step": step_flops}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -241,6 +304,9 @@ def main():
         return
     if args.chunk:
         chunk_variant(args)
+        return
+    if args.full_step:
+        full_step(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L
