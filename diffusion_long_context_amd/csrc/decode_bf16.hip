@@ -7,7 +7,8 @@
 // followed by the sequence's recomputed response rows.  The kv rows are split
 // into runs of 64-row tiles; each workgroup handles one (sequence, kv head,
 // 128 or 256 query rows, split) and emits either the final output (single
-// split) or a float32 partial output and its log-sum-exp for the merge kernel.
+// split) or a partial output (bf16, normalised) and its float32 log-sum-exp
+// for the merge kernel.
 //
 // Design for CDNA4:
 // * Query rows of one kv head are packed as (token, grouped head) pairs, so

@@ -218,8 +218,10 @@ size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_pag
  *   lse      device [n_seq][h_q][l_d] float out, nullable: natural-log
  *            normaliser ln sum_a exp(scale <q, k_a>)
  *   workspace device, >= pdllm_split_attn_decode_workspace(...) for the same
- *            arguments (holds per-split partial outputs, float32)
- * The result does not depend on num_splits beyond float32 rounding.
+ *            arguments (holds the per-split partial outputs -- in the pool dtype, each
+ *            normalised by its own softmax sum -- and their float32 log-sum-exps)
+ * The result does not depend on num_splits beyond rounding: with bf16 the
+ * partials are rounded once to bf16 before the merge.
  * Supported: f32 with d in {16, 32, 64, 128}; bf16 with d in {64, 128}.
  */
 pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
