@@ -29,6 +29,10 @@ summary:
   the KV dimension into independent parts that are merged by a log-sum-exp
   reduction (``lse_merge`` below is that merge, used to pin split
   invariance).
+* Methodology 1, predictive scoring: each chunk is scored by the negative
+  log-likelihood of the query window given the chunk (s_I) and by the
+  likelihood of the pseudo-labels given the chunk and the query (s_P), and
+  s = s_I + s_P feeds the top-K (``chunk_scores``).
 
 Readings where the pages are silent (each is listed with its support in the
 design notes):
@@ -43,6 +47,10 @@ design notes):
   * Selection order: larger score first, ties to the lower index, -0 == +0,
     NaN after every number; the kept indices are returned in ascending order.
   * lse is the natural logarithm of the softmax normaliser (with max).
+  * s_P's "likelihood" is read as a log-likelihood (a sum of per-token
+    log-probabilities), the only reading that can be added to the
+    negative log-likelihood s_I; both are natural-log sums over the
+    vocabulary-wide softmax of each scored row.
 """
 from __future__ import annotations
 
@@ -274,3 +282,40 @@ def attention_over_parts(q_rows: np.ndarray, k_rows: np.ndarray, v_rows: np.ndar
         o_parts[i] = p @ v_rows[idx]
         lse_parts[i] = m + np.log(l)
     return lse_merge(o_parts, lse_parts)
+
+
+# --------------------------------------------------------------------------
+# chunk scores from per-token log-probabilities
+# --------------------------------------------------------------------------
+def token_log_probs(logits: np.ndarray, target: np.ndarray) -> np.ndarray:
+    """Log-probability of each row's target token: logits [n][V] (bf16 bits or
+    float32), target [n] ids in [0, V) -> [n] float64, with
+    log p = z[target] - ln sum_v exp(z[v])  (the row's log-softmax at the
+    target; the sum is taken against the row maximum)."""
+    z = as_f64(logits).reshape(-1, logits.shape[-1])
+    t = np.asarray(target).reshape(-1)
+    m = z.max(axis=1)
+    lse = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return z[np.arange(z.shape[0]), t] - lse
+
+
+def chunk_scores(logits: np.ndarray, target: np.ndarray, n_query: int, n_pseudo: int):
+    """Predictive chunk scores (Methodology 1, predictive scoring), from the
+    model's logits at each chunk's scored positions:
+
+    logits [n_chunks][n_query + n_pseudo][V]: rows 0..n_query-1 predict the
+    query window's tokens, the next n_pseudo rows the pseudo-label tokens;
+    target [n_chunks][n_query + n_pseudo] holds those token ids.
+
+    s_I = -sum over the query rows of log p   (negative log-likelihood of the
+          query window given the chunk)
+    s_P =  sum over the pseudo-label rows of log p   (log-likelihood of the
+          pseudo-labels given the chunk and the query)
+    s   = s_I + s_P
+    Returns (s_i, s_p, s), each float64 [n_chunks]; rows summed in order.
+    """
+    n_chunks = logits.shape[0]
+    lp = token_log_probs(logits, target).reshape(n_chunks, n_query + n_pseudo)
+    s_i = -lp[:, :n_query].sum(axis=1)
+    s_p = lp[:, n_query:].sum(axis=1)
+    return s_i, s_p, s_i + s_p

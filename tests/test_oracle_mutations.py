@@ -74,3 +74,37 @@ def test_wrong_tie_rule_is_caught(monkeypatch):
     monkeypatch.setattr(ref, "_rank_key", bad)
     _fails(sp.test_topb_special_values)
     _fails(sp.test_topb_matches_lexsort, 0)
+
+
+import test_oracle_chunk_score_pins as cp
+
+
+def test_wrong_log_softmax_axis_is_caught(monkeypatch):
+    def bad(logits, target):
+        z = oracle.as_f64(logits).reshape(-1, logits.shape[-1])
+        t = np.asarray(target).reshape(-1)
+        m = z.max(axis=0)                              # over rows, not the vocabulary
+        lse = m + np.log(np.exp(z - m[None, :]).sum(axis=0))
+        return z[np.arange(z.shape[0]), t] - lse[t]
+    monkeypatch.setattr(ref, "token_log_probs", bad)
+    _fails(cp.test_chunk_score_is_sum_of_row_log_probs, 3, 6)
+
+
+def test_target_off_by_one_is_caught(monkeypatch):
+    orig = ref.token_log_probs
+    monkeypatch.setattr(ref, "token_log_probs",
+                        lambda z, t: orig(z, np.minimum(np.asarray(t) + 1, z.shape[-1] - 1)))
+    monkeypatch.setattr(oracle, "token_log_probs", ref.token_log_probs)
+    _fails(cp.test_two_token_closed_form)
+    _fails(cp.test_chunk_score_signs_and_rows)
+
+
+def test_flipped_or_swapped_score_parts_are_caught(monkeypatch):
+    orig = ref.chunk_scores
+    monkeypatch.setattr(ref, "chunk_scores", lambda *a: (lambda r: (-r[0], r[1], r[1] - r[0]))(orig(*a)))
+    monkeypatch.setattr(oracle, "chunk_scores", ref.chunk_scores)
+    _fails(cp.test_chunk_score_signs_and_rows)
+    monkeypatch.setattr(ref, "chunk_scores",
+                        lambda z, t, nq, npp: orig(z[:, ::-1], t[:, ::-1], nq, npp))
+    monkeypatch.setattr(oracle, "chunk_scores", ref.chunk_scores)
+    _fails(cp.test_chunk_score_signs_and_rows)
