@@ -89,6 +89,9 @@ def parse():
     p.add_argument("--full-step", action="store_true",
                    help="diagnostic: decode side of one denoising step of the 28-layer 32K run "
                         "(28 decode calls over distinct layer pools, one HIP graph, replayed)")
+    p.add_argument("--chunk-score", action="store_true",
+                   help="diagnostic: chunk scores of a 32K prefix (128 chunks x 64 query + 64 "
+                        "pseudo-label rows of 152064 bf16 logits) through pdllm_chunk_score")
     p.add_argument("--chunk", type=int, default=0,
                    help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
                         "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
@@ -291,6 +294,39 @@ def full_step(args):
                       "us_per_run": t * 1e6 * cfg.steps, "algorithmic_flops_per_step": step_flops}), flush=True)
 
 
+def chunk_score_run(args):
+    """Predictive chunk scores for a 32K prefix: 128 chunks, each with 64
+    query-window rows and 64 pseudo-label rows of logits over a 152,064-token
+    vocabulary (Dream-7B's), bf16, 5.0 GB read once (diagnostic line)."""
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    n_c, n_q, n_p, vocab = 128, 64, 64, 152064
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    logits = torch.empty((n_c, n_q + n_p, vocab), dtype=torch.bfloat16, device=dev)
+    for c in range(n_c):                       # one chunk at a time keeps the float32 draw small
+        logits[c] = (torch.randn((n_q + n_p, vocab), generator=gen, device=dev) * 2.5).to(torch.bfloat16)
+    target = torch.randint(0, vocab, (n_c, n_q + n_p), generator=gen, device=dev, dtype=torch.int32)
+    out = tuple(torch.empty(n_c, dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(L.lib.pdllm_chunk_score_workspace(n_c, n_q, n_p), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        L.chunk_score(logits, target, n_q, n_p, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        L.chunk_score(logits, target, n_q, n_p, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / args.steps
+    nbytes = logits.numel() * 2 + target.numel() * 4 + 3 * n_c * 4
+    print(json.dumps({"diagnostic": f"chunk scores: {n_c} chunks x ({n_q} query + {n_p} pseudo-label rows) x "
+                                    f"{vocab} bf16 logits, read once", "us": t * 1e6,
+                      "gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_bytes": nbytes, "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -307,6 +343,9 @@ def main():
         return
     if args.full_step:
         full_step(args)
+        return
+    if args.chunk_score:
+        chunk_score_run(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L

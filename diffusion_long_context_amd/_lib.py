@@ -38,7 +38,8 @@ class PageTable(ctypes.Structure):
 
 EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_select_topB",
            "pdllm_select_topK", "pdllm_decode_plan", "pdllm_split_attn_decode_workspace",
-           "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version")
+           "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
+           "pdllm_chunk_score_workspace", "pdllm_chunk_score")
 
 
 def _load() -> ctypes.CDLL:
@@ -68,11 +69,15 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_split_attn_decode.restype = ctypes.c_int
     lib.pdllm_split_attn_decode.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32,
                                             i32, vp, vp, vp, sz, vp]
+    lib.pdllm_chunk_score_workspace.restype = sz
+    lib.pdllm_chunk_score_workspace.argtypes = [i32, i32, i32]
+    lib.pdllm_chunk_score.restype = ctypes.c_int
+    lib.pdllm_chunk_score.argtypes = [vp, i32, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     return lib
 
 
 lib = _load()
-ABI_VERSION = 2
+ABI_VERSION = 3
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -174,6 +179,36 @@ def select_topk(chunk_score: torch.Tensor, k_per_seq: Sequence[int], k_max: int,
     _check(lib.pdllm_select_topK(chunk_score.data_ptr(), n_seq, n, ks, k_max, sel_chunk.data_ptr(),
                                  _stream(chunk_score.device)), "pdllm_select_topK")
     return sel_chunk
+
+
+def chunk_score(logits: torch.Tensor, target: torch.Tensor, n_query: int, n_pseudo: int,
+                out=None, workspace=None):
+    """pdllm_chunk_score: logits [n_chunks][n_query + n_pseudo][vocab] (bf16 or
+    float32; the last dimension may be padded, rows 16-byte aligned), target
+    [n_chunks][n_query + n_pseudo] int32 -> (s_i, s_p, s), each [n_chunks]
+    float32."""
+    if logits.dim() != 3 or (logits.numel() > 0 and (
+            logits.stride(2) != 1 or logits.stride(0) != logits.shape[1] * logits.stride(1))):
+        raise ValueError("logits must be [n_chunks][rows][vocab] with rows evenly spaced")
+    if not logits.is_cuda:
+        raise ValueError("logits must be a GPU tensor")
+    dtype = {torch.float32: 0, torch.bfloat16: 1}.get(logits.dtype)
+    if dtype is None:
+        raise ValueError("logits must be float32 or bfloat16")
+    _dense(target, "target", torch.int32)
+    n_chunks, rows, vocab = logits.shape
+    if rows != n_query + n_pseudo or target.shape != (n_chunks, rows):
+        raise ValueError("logits / target shapes do not match n_query + n_pseudo")
+    dev = logits.device
+    if out is None:
+        out = tuple(torch.empty(n_chunks, dtype=torch.float32, device=dev) for _ in range(3))
+    need = lib.pdllm_chunk_score_workspace(n_chunks, n_query, n_pseudo)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib.pdllm_chunk_score(logits.data_ptr(), dtype, logits.stride(1), vocab, target.data_ptr(),
+                                 n_chunks, n_query, n_pseudo, _ptr(out[0]), _ptr(out[1]), out[2].data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream(dev)), "pdllm_chunk_score")
+    return out
 
 
 def decode_plan(k_per_seq, b, l_d, h_q, h_kv, d, dtype, num_splits=0, n_cu=256, with_rows=False):

@@ -284,6 +284,52 @@ pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t 
   return ok();
 }
 
+size_t pdllm_chunk_score_workspace(int32_t n_chunks, int32_t n_query, int32_t n_pseudo) {
+  if (n_chunks < 0 || n_query < 0 || n_pseudo < 0) return 0;
+  return (size_t)(((int64_t)n_chunks * (n_query + n_pseudo) * 4 + 255) / 256 * 256);
+}
+
+pdllm_status pdllm_chunk_score(const void* logits, int32_t dtype, int64_t row_stride, int32_t vocab,
+                               const int32_t* target, int32_t n_chunks, int32_t n_query, int32_t n_pseudo,
+                               float* s_i, float* s_p, float* s, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (dtype != PDLLM_F32 && dtype != PDLLM_BF16) return fail(PDLLM_ERR_INVALID_ARG, "dtype %d is unknown", dtype);
+  if (vocab < 1) return fail(PDLLM_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (row_stride < vocab) return fail(PDLLM_ERR_INVALID_ARG, "row_stride %lld < vocab %d", (long long)row_stride, vocab);
+  if (n_chunks < 0 || n_query < 0 || n_pseudo < 0)
+    return fail(PDLLM_ERR_INVALID_ARG, "n_chunks, n_query and n_pseudo must be >= 0");
+  const int64_t rows = (int64_t)n_chunks * (n_query + n_pseudo);
+  if (rows > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "too many scored rows (%lld)", (long long)rows);
+  if (n_chunks == 0) return ok();
+  if (s == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "s is NULL");
+  if (rows > 0) {
+    pdllm_status st;
+    if ((st = check_tensor(logits, "logits")) != PDLLM_OK) return st;
+    if (target == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "target is NULL");
+    const int64_t es = dtype == PDLLM_BF16 ? 2 : 4;
+    if ((row_stride * es) % 16 != 0)
+      return fail(PDLLM_ERR_INVALID_ARG, "row_stride * element size must be a multiple of 16 bytes");
+  }
+  const size_t need = pdllm_chunk_score_workspace(n_chunks, n_query, n_pseudo);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  pdllm::ChunkScoreArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.target = target;
+  a.logp = static_cast<float*>(workspace);
+  a.s_i = s_i;
+  a.s_p = s_p;
+  a.s = s;
+  a.vocab = vocab;
+  a.n_chunks = n_chunks;
+  a.n_query = n_query;
+  a.n_pseudo = n_pseudo;
+  a.bf16 = dtype == PDLLM_BF16;
+  return hip_status(pdllm::launch_chunk_score(a, stream), "chunk score launch");
+}
+
 pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t b, int32_t l_d,
                                int32_t h_q, int32_t h_kv, int32_t d, int32_t dtype,
                                int32_t num_splits, int32_t n_cu, int32_t* splits_per_seq,

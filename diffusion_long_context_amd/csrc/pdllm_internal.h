@@ -117,4 +117,18 @@ struct TopkArgs {
 };
 int launch_select_topk(const TopkArgs& a, void* stream);
 
+// ---------------------------------------------------------------- chunk scores
+struct ChunkScoreArgs {
+  const void* logits;       // [n_chunks][n_query + n_pseudo] rows of `vocab` logits
+  int64_t row_stride;       // elements between rows
+  const int32_t* target;    // [n_chunks][n_query + n_pseudo]
+  float* logp;              // workspace [n_chunks][n_query + n_pseudo]
+  float* s_i;               // nullable
+  float* s_p;               // nullable
+  float* s;
+  int32_t vocab, n_chunks, n_query, n_pseudo;
+  bool bf16;
+};
+int launch_chunk_score(const ChunkScoreArgs& a, void* stream);
+
 }  // namespace pdllm

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 2
+#define PDLLM_ABI_VERSION 3
 
 typedef enum {
   PDLLM_OK = 0,
@@ -169,6 +169,40 @@ pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t
  */
 pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t n_chunks,
                                const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
+                               void* stream);
+
+/* Bytes of workspace pdllm_chunk_score needs (0 when the arguments are
+ * invalid).  Pure host function. */
+size_t pdllm_chunk_score_workspace(int32_t n_chunks, int32_t n_query, int32_t n_pseudo);
+
+/*
+ * Predictive chunk scores from the model's logits (Methodology 1, predictive
+ * scoring: each chunk is scored by the negative log-likelihood of the query
+ * window given the chunk, s_I, and by the likelihood of the pseudo-labels
+ * given the chunk and the query, s_P -- read as a log-likelihood -- and the
+ * top-K chunks by s = s_I + s_P are selected; its output feeds
+ * pdllm_select_topK).  For each scored row r, with z the row's logits:
+ *   log p[r] = z[target[r]] - ln sum_v exp(z[v])
+ *
+ *   logits     device, row r = c (n_query + n_pseudo) + t at logits + r row_stride
+ *              (elements of dtype PDLLM_F32 or PDLLM_BF16), vocab logits per row;
+ *              16-byte aligned, row_stride * element size a multiple of 16 bytes.
+ *              Rows t < n_query predict the chunk's query-window tokens, the
+ *              next n_pseudo rows its pseudo-label tokens.  Logits are finite
+ *              or -inf; a row of all -inf has no defined result.
+ *   target     device [n_chunks][n_query + n_pseudo] int32 token ids; ids
+ *              outside [0, vocab) are clamped into it
+ *   s_i        device [n_chunks] float out, nullable: -sum_{t < n_query} log p
+ *   s_p        device [n_chunks] float out, nullable: sum_{t >= n_query} log p
+ *   s          device [n_chunks] float out: s_i + s_p
+ *   workspace  device, >= pdllm_chunk_score_workspace(n_chunks, n_query, n_pseudo)
+ *              (the per-row log-probabilities)
+ * Each row's sum over the vocabulary and each chunk's sum over its rows are
+ * taken in a fixed order: results are bitwise reproducible run to run.
+ */
+pdllm_status pdllm_chunk_score(const void* logits, int32_t dtype, int64_t row_stride, int32_t vocab,
+                               const int32_t* target, int32_t n_chunks, int32_t n_query, int32_t n_pseudo,
+                               float* s_i, float* s_p, float* s, void* workspace, size_t workspace_bytes,
                                void* stream);
 
 /* ------------------------------------------------------------------------ *

@@ -211,5 +211,28 @@ def random_page_table(cfg: Config, seed: int = 0):
     return sel, keep
 
 
+def chunk_logits(n_chunks: int, n_query: int, n_pseudo: int, vocab: int, seed: int = 0,
+                 dtype: str = "bf16", std: float = 2.5, stride: int = 0):
+    """Seeded stand-in for the model's logits at each chunk's scored rows.
+
+    Returns ``(logits [n_chunks][n_query + n_pseudo][stride or vocab], target
+    [n_chunks][n_query + n_pseudo] int32)``: logits ~ N(0, std) drawn in
+    float32 (rounded once to bf16 bits for ``dtype="bf16"``), padding columns
+    past ``vocab`` set to 0; targets uniform over the vocabulary.  Half of the
+    rows get their target logit raised by 2 std, so that the log-probabilities
+    spread the way a model's do.
+    """
+    rng = np.random.default_rng(2_000_003 + seed)
+    rows = n_query + n_pseudo
+    width = max(stride, vocab)
+    z = np.zeros((n_chunks, rows, width), dtype=np.float32)
+    z[..., :vocab] = rng.normal(0.0, std, size=(n_chunks, rows, vocab)).astype(np.float32)
+    target = rng.integers(0, vocab, size=(n_chunks, rows)).astype(np.int32)
+    lift = rng.random((n_chunks, rows)) < 0.5
+    ci, ri = np.nonzero(lift)
+    z[ci, ri, target[ci, ri]] += np.float32(2.0 * std)
+    return _finish(z, dtype), target
+
+
 __all__ = ["Config", "CONFIGS", "config", "Inputs", "generate",
-           "random_page_table", "f32_to_bf16_bits"]
+           "random_page_table", "f32_to_bf16_bits", "chunk_logits"]

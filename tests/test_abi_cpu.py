@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 2
+    assert L.lib.pdllm_abi_version() == 3
 
 
 def _pool(**kw):
@@ -170,3 +170,23 @@ def test_plan_rejects_bad_sizes():
         L.decode_plan([4], 8, 16, 6, 4, 128, 1)
     with pytest.raises(L.PdllmError):
         L.decode_plan([-1], 8, 16, 8, 4, 128, 1)
+
+
+def test_chunk_score_validation():
+    f = L.lib.pdllm_chunk_score
+    ws = L.lib.pdllm_chunk_score_workspace
+    assert ws(128, 64, 64) == 128 * 128 * 4
+    assert ws(-1, 64, 64) == 0
+    need = ws(4, 3, 5)
+    args = lambda **kw: [kw.get("logits", 0x100000), kw.get("dtype", 1), kw.get("stride", 152064),
+                         kw.get("vocab", 152064), 0x200000, kw.get("n", 4), kw.get("nq", 3), kw.get("np_", 5),
+                         None, None, kw.get("s", 0x300000), kw.get("ws", 0x400000), kw.get("ws_bytes", need), None]
+    assert f(*args(dtype=7)) == INVALID
+    assert f(*args(vocab=0)) == INVALID
+    assert f(*args(stride=100, vocab=101)) == INVALID
+    assert f(*args(stride=152065)) == INVALID                     # rows not 16-byte aligned
+    assert f(*args(logits=0x100002)) == INVALID                   # base not 16-byte aligned
+    assert f(*args(s=None)) == INVALID
+    assert f(*args(nq=-1)) == INVALID
+    assert f(*args(ws_bytes=need - 1)) == WS_SMALL
+    assert f(*args(n=0)) == OK                                      # nothing to do, nothing enqueued
