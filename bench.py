@@ -65,9 +65,9 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "4b7a80c31af23058",
+    "sources_sha": "f5b7fb1869271615",
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149196.48, "write_kib": 234558.02},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149196.34, "write_kib": 234575.95},
         "score_finalize_kernel": {"fetch_kib": 2551.44, "write_kib": 128.5},
     },
     "copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
