@@ -152,6 +152,52 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
 
 
+def measured_peaks():
+    """Ceilings this GPU reaches in practice (libpdllm_calib.so): dense bf16
+    MFMA on full-entropy operands, and HBM read and copy over 4 GiB (past the
+    Infinity Cache).  Best of three timed runs each."""
+    import ctypes
+    import torch
+    here = os.path.join(ROOT, "diffusion_long_context_amd", "libpdllm_calib.so")
+    lib = ctypes.CDLL(here)
+    lib.pdllm_calib_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pdllm_calib_mfma_bf16_flops.restype = ctypes.c_int64
+    lib.pdllm_calib_mfma_bf16_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    lib.pdllm_calib_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.pdllm_calib_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev).cuda_stream
+    n_wg = 16384                                  # 256 KiB per workgroup
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev).fill_(1)
+
+    def best(fn):
+        ts = []
+        for k in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            assert rc == 0, rc
+            if k:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    iters, mfma_wg = 20000, 512
+    t_mfma = best(lambda: lib.pdllm_calib_mfma_bf16(iters, mfma_wg, sink.data_ptr(), st))
+    t_read = best(lambda: lib.pdllm_calib_hbm_read(buf.data_ptr(), buf.numel(), n_wg, sink.data_ptr(), st))
+    half = buf.numel() // 2
+    t_copy = best(lambda: lib.pdllm_calib_hbm_copy(buf.data_ptr(), buf.data_ptr() + half, half, n_wg, st))
+    del buf
+    return {"mfma_bf16_tflops": lib.pdllm_calib_mfma_bf16_flops(iters, mfma_wg) / t_mfma / 1e12,
+            "hbm_read_gbs": (4 << 30) / t_read / 1e9, "hbm_copy_gbs": 2 * half / t_copy / 1e9,
+            "source": "libpdllm_calib.so: 32x32x16 bf16 MFMA chains on full-entropy operands; "
+                      "16-byte streaming read and copy of 4 GiB in 256 KiB blocks"}
+
+
 def cpu_baseline(cfg, inp, min_seconds=10.0):
     """The fp64 oracle, as it stands, timed on the host over whole steps of
     the workload (chunk prefill + scoring of all chunks, top-B, top-K,
@@ -410,7 +456,19 @@ def main():
 
     traffic = {"prefill": prefill_traffic()}
 
+    peaks = measured_peaks()
+
     def roof(name):
+        r = roof_vendor(name)
+        if r["unit"] == "GB/s":
+            # the stage reads and writes: its ceiling is the copy rate
+            r["measured_peak"], r["measured_peak_kind"] = peaks["hbm_copy_gbs"], "hbm copy"
+        else:
+            r["measured_peak"], r["measured_peak_kind"] = peaks["mfma_bf16_tflops"], "bf16 mfma"
+        r["frac_measured"] = r["achieved"] / r["measured_peak"]
+        return r
+
+    def roof_vendor(name):
         t = stage_ms[name] * 1e-3
         ai = flops[name] / max(bytes_[name], 1.0)
         hbm_bound = ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -436,6 +494,7 @@ def main():
         "stage_us": {n: stage_ms[n] * 1e3 for n in names},
         "roofline": roof(dominant),
         "rooflines": {n: roof(n) for n in names if flops[n] > 0},
+        "measured_peaks": peaks,
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:

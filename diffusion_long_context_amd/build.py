@@ -19,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpdllm.so")
+CALIB = os.path.join(HERE, "calib")
+CALIB_LIB = os.path.join(HERE, "libpdllm_calib.so")   # peak calibration, measurement only
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 instructions
@@ -43,20 +45,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    """Compile every source and link the shared libraries (the path's
+    libpdllm.so and the calibration libpdllm_calib.so); returns the path of
+    libpdllm.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    calib = sorted(glob.glob(os.path.join(CALIB, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, sources + calib))
+    _link(objs[:len(sources)], LIB)
+    _link(objs[len(sources):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB} from {len(sources)} sources")
+        print(f"built {LIB} from {len(sources)} sources and {CALIB_LIB} from {len(calib)}")
     return LIB
 
 

@@ -14,21 +14,35 @@ L = pytest.importorskip("diffusion_long_context_amd._lib")
 OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
 
 
-def _declared():
-    names = set()
-    for fn in os.listdir(os.path.join(ROOT, "include")):
-        if fn.endswith(".h"):
-            text = open(os.path.join(ROOT, "include", fn)).read()
-            names |= set(re.findall(r"\b(pdllm_[a-zA-Z_]+)\s*\(", text))
-    return names
+def _declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    return set(re.findall(r"\b(pdllm_[a-zA-Z_0-9]+)\s*\(", text))
 
 
 def test_every_declared_symbol_is_exported():
-    names = _declared()
+    names = _declared("pdllm.h")
     assert len(names) >= 9
     for n in names:
-        assert hasattr(L.lib, n), f"{n} declared in include/ but not exported"
+        assert hasattr(L.lib, n), f"{n} declared in include/pdllm.h but not exported"
     assert set(L.EXPORTS) <= names
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        ["pdllm.h", "pdllm_calib.h"]
+
+
+def test_calibration_library_exports_its_header():
+    """The peak-calibration library (measurement only) loads on the CPU and
+    exports what include/pdllm_calib.h declares; the path library does not
+    carry those symbols."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "diffusion_long_context_amd", "libpdllm_calib.so"))
+    names = _declared("pdllm_calib.h")
+    assert len(names) == 4
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/pdllm_calib.h but not exported"
+        assert not hasattr(L.lib, n)
+    lib.pdllm_calib_mfma_bf16_flops.restype = ctypes.c_int64
+    lib.pdllm_calib_mfma_bf16_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    assert lib.pdllm_calib_mfma_bf16_flops(3, 5) == 5 * 4 * 3 * 4 * 32 * 32 * 16 * 2
 
 
 def test_abi_version():
