@@ -218,21 +218,15 @@ struct WaveAttn {
 };
 
 // Query fragments (B operand of S^T): lane column c, d = 16 dc + 8 j ...
-template <int DC>
-__device__ __forceinline__ void zero_q(bf16x8 (&qf)[DC]) {
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc) qf[dc] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-}
-
 template <int DC, int STRIDE>
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[DC], const uint16_t* row_plus_8j) {
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(row_plus_8j + STRIDE * dc);
 }
 
-// Store a wavefront's O^T columns as bf16 rows, 16 bytes per lane and
-// store: for accumulator block db and m-pair p, lane (c, j) holds d =
-// 32 db + 16 p + 8 m' + 4 j + t (m' = 0, 1).  One v_permlane32_swap of the
+// Store a wavefront's O^T columns (times inv) as bf16 rows, 16 bytes per
+// lane and store.  For accumulator block db and m-pair p, lane (c, j) holds
+// d = 32 db + 16 p + 8 m' + 4 j + t (m' = 0, 1).  One v_permlane32_swap of the
 // m' = 0 values (X) with the m' = 1 values (Y) leaves lane c with X of lanes
 // c and c + 32 (d = 32 db + 16 p + 0..7) and lane c + 32 with Y of both
 // (d = 32 db + 16 p + 8..15).  row_plus_8j = &O[row][8 j]; lanes c and c + 32
@@ -253,16 +247,6 @@ __device__ __forceinline__ void store_o_bf16(uint16_t* row_plus_8j, const f32x16
       const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
       *reinterpret_cast<u32x4*>(row_plus_8j + 32 * db + 16 * p) = u32x4{s0[0], s1[0], s0[1], s1[1]};
     }
-}
-
-template <int DB>
-__device__ __forceinline__ void store_o_f32(float* row_plus_4j, const f32x16 (&acc)[DB], float inv) {
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<f32x4*>(row_plus_4j + 32 * db + 8 * m) =
-          f32x4{acc[db][4 * m], acc[db][4 * m + 1], acc[db][4 * m + 2], acc[db][4 * m + 3]} * inv;
 }
 
 }  // namespace pdllm

@@ -46,9 +46,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // (maximum returns the NaN), which the softmax inputs never hold.
 __device__ __forceinline__ float max_f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-__device__ __forceinline__ float wave_xor_max(float v, int mask) {
-  return max_f(v, __shfl_xor(v, mask, 64));
-}
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
