@@ -92,6 +92,9 @@ def parse():
     p.add_argument("--chunk-score", action="store_true",
                    help="diagnostic: chunk scores of a 32K prefix (128 chunks x 64 query + 64 "
                         "pseudo-label rows of 152064 bf16 logits) through pdllm_chunk_score")
+    p.add_argument("--compact", action="store_true",
+                   help="diagnostic: kept-row compaction of a 32K prefix (128 chunks, B = 128) and the "
+                        "decode over the compacted slots against the decode through keep_rows")
     p.add_argument("--chunk", type=int, default=0,
                    help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
                         "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
@@ -373,6 +376,73 @@ def chunk_score_run(args):
                       "algorithmic_bytes": nbytes, "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def compact_run(args):
+    """Kept-row compaction at the 32K prefix with B = 128 (128 chunks x 129
+    rows x 4 KV heads, K and V) and one decode call (K = 16, L_d = 256) over
+    the whole-chunk pool through keep_rows against the same call over the
+    compacted slots; each decode is captured in a HIP graph and replayed
+    (diagnostic line)."""
+    import torch
+    import synth
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    cfg = synth.config("f32")
+    inp = synth.generate(cfg, args.seed)
+    sel_h, keep_h = synth.random_page_table(cfg, args.seed)
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    pool_k, pool_v, chunk_slot = to_dev(inp.pool_k), to_dev(inp.pool_v), to_dev(inp.chunk_slot)
+    sel, keep = to_dev(sel_h), to_dev(keep_h)
+    q, k_resp, v_resp = to_dev(inp.q), to_dev(inp.k_resp), to_dev(inp.v_resp)
+    ck, cv = L.compact_kept_rows(pool_k, pool_v, chunk_slot, keep)
+
+    def timed(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    t_compact = timed(lambda: L.compact_kept_rows(pool_k, pool_v, chunk_slot, keep, ck, cv), args.steps)
+    rest = (cfg.k_per_seq, q, k_resp, v_resp, cfg.scale)
+    calls = {"gather": L.Decode(pool_k, pool_v, chunk_slot, sel, keep, *rest),
+             "compacted": L.Decode(ck, cv, chunk_slot, sel, None, *rest, b=cfg.b)}
+    t_dec = {}
+    for name, call in calls.items():
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        t_dec[name] = timed(graph.replay, args.steps)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(calls["gather"].o, calls["compacted"].o))
+    row_bytes = cfg.h_kv * cfg.d * 2
+    nbytes = 2 * 2 * cfg.n_slots * (cfg.b + 1) * row_bytes + 4 * cfg.n_slots * cfg.b
+    flops, _ = workload_counts(cfg)
+    print(json.dumps({"diagnostic": f"kept-row compaction, 32K prefix: {cfg.n_slots} chunks x {cfg.b + 1} rows "
+                                    f"x {cfg.h_kv} KV heads, K and V (bf16), then one decode call "
+                                    f"(K={cfg.k_per_seq[0]}, B={cfg.b}, L_d={cfg.l_d}) per layout",
+                      "compact_us": t_compact * 1e6, "compact_gbs": nbytes / t_compact / 1e9,
+                      "compact_hbm_frac": nbytes / t_compact / 1e9 / HBM_PEAK_GBS,
+                      "compact_algorithmic_bytes": nbytes,
+                      "decode_us": {k: v * 1e6 for k, v in t_dec.items()},
+                      "decode_tflops": {k: flops["decode"] / v / 1e12 for k, v in t_dec.items()},
+                      "outputs_identical": same, "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -392,6 +462,9 @@ def main():
         return
     if args.chunk_score:
         chunk_score_run(args)
+        return
+    if args.compact:
+        compact_run(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L

@@ -33,13 +33,13 @@ class PageTable(ctypes.Structure):
     _fields_ = [("chunk_slot", ctypes.c_void_p), ("sel_chunk", ctypes.c_void_p),
                 ("keep_rows", ctypes.c_void_p), ("k_per_seq", ctypes.c_void_p),
                 ("n_chunks_per_seq", ctypes.c_int32), ("k_max", ctypes.c_int32),
-                ("b", ctypes.c_int32)]
+                ("b", ctypes.c_int32), ("rows_compacted", ctypes.c_int32)]
 
 
 EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_select_topB",
            "pdllm_select_topK", "pdllm_decode_plan", "pdllm_split_attn_decode_workspace",
            "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
-           "pdllm_chunk_score_workspace", "pdllm_chunk_score")
+           "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows")
 
 
 def _load() -> ctypes.CDLL:
@@ -73,11 +73,13 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_chunk_score_workspace.argtypes = [i32, i32, i32]
     lib.pdllm_chunk_score.restype = ctypes.c_int
     lib.pdllm_chunk_score.argtypes = [vp, i32, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.pdllm_compact_kept_rows.restype = ctypes.c_int
+    lib.pdllm_compact_kept_rows.argtypes = [P(Pool), vp, i32, vp, i32, vp, vp, i64, i64, i64, i32, vp]
     return lib
 
 
 lib = _load()
-ABI_VERSION = 3
+ABI_VERSION = 4
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -211,6 +213,37 @@ def chunk_score(logits: torch.Tensor, target: torch.Tensor, n_query: int, n_pseu
     return out
 
 
+def compact_kept_rows(pool_k, pool_v, chunk_slot, keep_rows, dst_k=None, dst_v=None):
+    """pdllm_compact_kept_rows: for chunk c in slot s = chunk_slot[c], writes
+    the BOS row and the kept rows keep_rows[c] ([n_chunks][b] int32) to rows
+    0..b of slot s of (dst_k, dst_v).  The destination defaults to new
+    [n_slots][b + 1][h_kv][d] tensors (slots of no listed chunk are left
+    uninitialised); returns (dst_k, dst_v)."""
+    pool = make_pool(pool_k, pool_v)
+    _dense(chunk_slot, "chunk_slot", torch.int32)
+    _dense(keep_rows, "keep_rows", torch.int32)
+    if keep_rows.dim() != 2:
+        raise ValueError("keep_rows must be [n_chunks][b]")
+    n_chunks, b = keep_rows.shape
+    if chunk_slot.numel() < n_chunks:
+        raise ValueError("chunk_slot must hold n_chunks entries")
+    if dst_k is None:
+        shape = (pool.n_slots, b + 1, pool.h_kv, pool.d)
+        dst_k = torch.empty(shape, dtype=pool_k.dtype, device=pool_k.device)
+        dst_v = torch.empty(shape, dtype=pool_k.dtype, device=pool_k.device)
+    if dst_k.shape != dst_v.shape or dst_k.stride() != dst_v.stride() or dst_k.dtype != pool_k.dtype:
+        raise ValueError("dst k and v must share shape, strides and the pool dtype")
+    if dst_k.dim() != 4 or dst_k.stride(3) != 1 or dst_k.shape[0] != pool.n_slots or \
+            dst_k.shape[2:] != (pool.h_kv, pool.d):
+        raise ValueError("dst tensors must be [n_slots][rows][h_kv][d] with d contiguous")
+    _check(lib.pdllm_compact_kept_rows(ctypes.byref(pool), chunk_slot.data_ptr(), n_chunks,
+                                       _ptr(keep_rows) if b > 0 else None, b, dst_k.data_ptr(),
+                                       dst_v.data_ptr(), dst_k.stride(0), dst_k.stride(1),
+                                       dst_k.stride(2), dst_k.shape[1], _stream(pool_k.device)),
+           "pdllm_compact_kept_rows")
+    return dst_k, dst_v
+
+
 def decode_plan(k_per_seq, b, l_d, h_q, h_kv, d, dtype, num_splits=0, n_cu=256, with_rows=False):
     """pdllm_decode_plan (host only): returns (splits, tiles_per_split,
     workspace_bytes), and the query rows per workgroup if ``with_rows``."""
@@ -230,11 +263,19 @@ def decode_plan(k_per_seq, b, l_d, h_q, h_kv, d, dtype, num_splits=0, n_cu=256, 
 class Decode:
     """A prepared pdllm_split_attn_decode call: the structs, host K_s array,
     outputs and workspace are built once so repeated calls (timing loops,
-    denoising steps) only cross the boundary."""
+    denoising steps) only cross the boundary.  ``keep_rows`` is the
+    [n_seq * N][b] table over a whole-chunk pool, or None for a pool of
+    compacted slots (pdllm_compact_kept_rows) whose kept rows are rows
+    1..``b``."""
 
     def __init__(self, pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                 v_resp, scale, num_splits=0, want_lse=True, out=None):
+                 v_resp, scale, num_splits=0, want_lse=True, out=None, b=None):
         self.pool = make_pool(pool_k, pool_v)
+        compacted = keep_rows is None
+        if compacted:
+            if b is None:
+                raise ValueError("a compacted pool needs b")
+            keep_rows = torch.empty((chunk_slot.numel(), 0), dtype=torch.int32, device=q.device)
         for t, name in ((chunk_slot, "chunk_slot"), (sel_chunk, "sel_chunk"), (keep_rows, "keep_rows")):
             _dense(t, name, torch.int32)
         _dense(q, "q", pool_k.dtype)
@@ -249,9 +290,11 @@ class Decode:
             raise ValueError("keep_rows must be [n_seq * N][b] and chunk_slot [n_seq * N]")
         self._keep = (chunk_slot, sel_chunk, keep_rows, q, k_resp, v_resp, pool_k, pool_v)
         self.ks = (ctypes.c_int32 * n_seq)(*[int(x) for x in k_per_seq])
-        self.pt = PageTable(chunk_slot.data_ptr(), sel_chunk.data_ptr(), keep_rows.data_ptr(),
+        self.pt = PageTable(chunk_slot.data_ptr(), sel_chunk.data_ptr(),
+                            None if compacted else keep_rows.data_ptr(),
                             ctypes.cast(self.ks, ctypes.c_void_p), chunk_slot.numel() // n_seq,
-                            sel_chunk.shape[1], keep_rows.shape[1])
+                            sel_chunk.shape[1], int(b) if compacted else keep_rows.shape[1],
+                            1 if compacted else 0)
         self.n_seq, self.l_d, self.h_q = n_seq, l_d, h_q
         self.scale = float(scale)
         self.num_splits = int(num_splits)
@@ -274,7 +317,8 @@ class Decode:
 
 
 def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                      v_resp, scale, num_splits=0, want_lse=True):
-    """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None)."""
+                      v_resp, scale, num_splits=0, want_lse=True, b=None):
+    """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None).
+    keep_rows=None with ``b`` decodes over a pool of compacted slots."""
     return Decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp, v_resp,
-                  scale, num_splits, want_lse)()
+                  scale, num_splits, want_lse, b=b)()

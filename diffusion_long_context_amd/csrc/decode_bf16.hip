@@ -52,7 +52,8 @@ struct Smem {
 // Element offset of attended row v of sequence s for kv head g.  Pool rows
 // are >= 0 (relative to pool k/v); response rows are encoded as -1 - offset
 // (relative to k_resp/v_resp).  Chunk k of the sequence contributes rows
-// [k (b+1), (k+1)(b+1)): its BOS row 0, then its kept rows.
+// [k (b+1), (k+1)(b+1)): its BOS row 0, then its kept rows -- looked up in
+// keep_rows, or rows 1..b of the slot when the pool holds compacted slots.
 template <int D>
 __device__ __forceinline__ int64_t resolve_row(const DecodeArgs& a, int s, int g, int k_s,
                                                int v) {
@@ -62,7 +63,7 @@ __device__ __forceinline__ int64_t resolve_row(const DecodeArgs& a, int s, int g
     const int r = v - k * per;
     const int cg = s * a.n_chunks_per_seq + a.sel_chunk[(int64_t)s * a.k_max + k];
     const int slot = a.chunk_slot[cg];
-    const int row = r ? a.keep_rows[(int64_t)cg * a.b + r - 1] : 0;
+    const int row = r == 0 ? 0 : a.compact ? r : a.keep_rows[(int64_t)cg * a.b + r - 1];
     return (int64_t)slot * a.ps_slot + (int64_t)row * a.ps_row + (int64_t)g * a.ps_head;
   }
   const int j = v - k_s * per;
@@ -146,7 +147,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : a.chunk_slot);
     const int cg = s * a.n_chunks_per_seq + min(max(c0, 0), a.n_chunks_per_seq - 1);
     const int slot = *(gptr32)(a.chunk_slot + cg);
-    const int krow = *(gptr32)(a.b > 0 ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0) : a.chunk_slot);
+    const int krow_ld = *(gptr32)(a.b > 0 && !a.compact ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0)
+                                                       : a.chunk_slot);
+    const int krow = a.compact ? r : krow_ld;   // compacted slots: kept row i sits at row 1 + i
     __builtin_amdgcn_sched_barrier(0);     // the index loads go out before the queries
     // queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc
     // + 8 lj ..); rows past the end read the last row (never stored)

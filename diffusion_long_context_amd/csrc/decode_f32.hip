@@ -25,7 +25,7 @@ __device__ __forceinline__ int64_t resolve_row_f32(const DecodeArgs& a, int s, i
     const int r = v - k * per;
     const int cg = s * a.n_chunks_per_seq + a.sel_chunk[(int64_t)s * a.k_max + k];
     const int slot = a.chunk_slot[cg];
-    const int row = r ? a.keep_rows[(int64_t)cg * a.b + r - 1] : 0;
+    const int row = r == 0 ? 0 : a.compact ? r : a.keep_rows[(int64_t)cg * a.b + r - 1];
     return (int64_t)slot * a.ps_slot + (int64_t)row * a.ps_row + (int64_t)g * a.ps_head;
   }
   const int j = v - k_s * per;

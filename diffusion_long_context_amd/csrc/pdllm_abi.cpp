@@ -117,6 +117,7 @@ pdllm::DecodeArgs base_decode_args(const pdllm_pool* pool, const pdllm_page_tabl
   a.n_chunks_per_seq = pt->n_chunks_per_seq;
   a.k_max = pt->k_max;
   a.b = pt->b;
+  a.compact = pt->rows_compacted ? 1 : 0;
   a.l_d = l_d;
   a.h_q = h_q;
   a.h_kv = pool->h_kv;
@@ -142,6 +143,8 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
   if (pt->b < 0 || pt->b > pool->slot_rows - 1)
     return fail(PDLLM_ERR_INVALID_ARG, "b %d outside [0, slot_rows - 1 = %d]", pt->b, pool->slot_rows - 1);
   if (pt->k_per_seq == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq (host) is NULL");
+  if (pt->rows_compacted != 0 && pt->rows_compacted != 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "rows_compacted must be 0 or 1 (got %d)", pt->rows_compacted);
   bool any_chunk = false;
   for (int s = 0; s < n_seq; ++s) {
     const int ks = pt->k_per_seq[s];
@@ -152,7 +155,8 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
   if (any_chunk) {
     if (pt->chunk_slot == nullptr || pt->sel_chunk == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot / sel_chunk is NULL");
-    if (pt->b > 0 && pt->keep_rows == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
+    if (pt->b > 0 && !pt->rows_compacted && pt->keep_rows == nullptr)
+      return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
   }
   return PDLLM_OK;
 }
@@ -282,6 +286,56 @@ pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t 
     if (st != PDLLM_OK) return st;
   }
   return ok();
+}
+
+pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk_slot, int32_t n_chunks,
+                                     const int32_t* keep_rows, int32_t b, void* dst_k, void* dst_v,
+                                     int64_t dst_stride_slot, int64_t dst_stride_row,
+                                     int64_t dst_stride_head, int32_t dst_slot_rows, void* stream) {
+  pdllm_status st = check_pool(src);
+  if (st != PDLLM_OK) return st;
+  if (n_chunks < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 0");
+  if (b < 0 || b > src->slot_rows - 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "b %d outside [0, slot_rows - 1 = %d]", b, src->slot_rows - 1);
+  if (dst_slot_rows < b + 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "dst_slot_rows %d < b + 1 = %d", dst_slot_rows, b + 1);
+  // the destination must pass the same checks as a pool of the same shape
+  pdllm_pool dst = *src;
+  dst.k = dst_k;
+  dst.v = dst_v;
+  dst.stride_slot = dst_stride_slot;
+  dst.stride_row = dst_stride_row;
+  dst.stride_head = dst_stride_head;
+  dst.slot_rows = dst_slot_rows;
+  if ((st = check_pool(&dst)) != PDLLM_OK) return st;
+  if (n_chunks == 0) return ok();
+  if (chunk_slot == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot is NULL");
+  if (b > 0 && keep_rows == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
+  const int64_t es = elem_bytes(src->dtype);
+  pdllm::CompactArgs a{};
+  a.src_k = static_cast<const char*>(src->k);
+  a.src_v = static_cast<const char*>(src->v);
+  a.dst_k = static_cast<char*>(dst_k);
+  a.dst_v = static_cast<char*>(dst_v);
+  a.ss = src->stride_slot * es;
+  a.sr = src->stride_row * es;
+  a.sh = src->stride_head * es;
+  a.ds = dst_stride_slot * es;
+  a.dr = dst_stride_row * es;
+  a.dh = dst_stride_head * es;
+  a.chunk_slot = chunk_slot;
+  a.keep_rows = keep_rows;
+  a.n_chunks = n_chunks;
+  a.b = b;
+  a.h_kv = src->h_kv;
+  a.nvec = (int32_t)(src->d * es / 16);
+  const int64_t total = (int64_t)(b + 1) * src->h_kv * a.nvec;
+  const int64_t per_wg = (int64_t)pdllm::kCompactThreads * pdllm::kCompactVec;
+  a.blocks = (int32_t)((total + per_wg - 1) / per_wg);
+  if (total > INT32_MAX / 2 || (int64_t)n_chunks * 2 * a.blocks > INT32_MAX)
+    return fail(PDLLM_ERR_UNSUPPORTED, "compaction grid too large");
+  st = hip_status(pdllm::launch_compact(a, stream), "compaction launch");
+  return st != PDLLM_OK ? st : ok();
 }
 
 size_t pdllm_chunk_score_workspace(int32_t n_chunks, int32_t n_query, int32_t n_pseudo) {

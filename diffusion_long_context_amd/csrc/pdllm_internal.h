@@ -64,6 +64,7 @@ struct DecodeArgs {
   void* part_o;             // bf16 partials (bf16 kernel) or float32 (f32 kernel)
   float* part_lse;
   int32_t n_chunks_per_seq, k_max, b;
+  int32_t compact;          // 1: a chunk's kept rows are rows 1..b of its slot (keep_rows unused)
   int32_t l_d, h_q, h_kv, group;
   int32_t q_tiles;
   int32_t seq0;             // first sequence of this launch
@@ -130,5 +131,23 @@ struct ChunkScoreArgs {
   bool bf16;
 };
 int launch_chunk_score(const ChunkScoreArgs& a, void* stream);
+
+// ---------------------------------------------------------------- kept-row compaction
+struct CompactArgs {
+  const char* src_k;
+  const char* src_v;
+  char* dst_k;
+  char* dst_v;
+  int64_t ss, sr, sh;       // source slot / row / head strides (bytes)
+  int64_t ds, dr, dh;       // destination strides (bytes)
+  const int32_t* chunk_slot;
+  const int32_t* keep_rows; // [n_chunks][b]
+  int32_t n_chunks, b, h_kv;
+  int32_t nvec;             // 16-byte vectors per (row, head)
+  int32_t blocks;           // workgroups per (chunk, tensor)
+};
+constexpr int kCompactThreads = 256;
+constexpr int kCompactVec = 4;           // 16-byte vectors per thread
+int launch_compact(const CompactArgs& a, void* stream);
 
 }  // namespace pdllm

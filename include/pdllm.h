@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 3
+#define PDLLM_ABI_VERSION 4
 
 typedef enum {
   PDLLM_OK = 0,
@@ -87,6 +87,11 @@ typedef struct {
  *   keep_rows   device [n_seq * n_chunks_per_seq][b]   kept content rows
  *                      (1..C) of every chunk, as written by pdllm_select_topB
  *   k_per_seq   host   [n_seq]   K_s, 0 <= K_s <= k_max
+ *   rows_compacted  0: the pool holds whole chunks and keep_rows names the
+ *                      kept rows;  1: the pool holds compacted slots (the
+ *                      layout pdllm_compact_kept_rows writes), whose kept
+ *                      rows are rows 1..b in order -- keep_rows is not read
+ *                      and may be NULL
  * A selected chunk contributes its BOS row and its b kept rows, in that
  * order; chunks are visited in sel_chunk order.
  */
@@ -98,6 +103,7 @@ typedef struct {
   int32_t n_chunks_per_seq;
   int32_t k_max;
   int32_t b;
+  int32_t rows_compacted;
 } pdllm_page_table;
 
 /* ------------------------------------------------------------------------ *
@@ -170,6 +176,31 @@ pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t
 pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t n_chunks,
                                const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
                                void* stream);
+
+/*
+ * Compacted kept-row cache (Methodology 2: after the intra-chunk selection
+ * only the top-B tokens of a chunk stay in the KV cache).  Chunk c, held in
+ * slot s = chunk_slot[c] of the source pool, is written to slot s of the
+ * destination: its BOS row first, then its b kept rows in keep_rows order,
+ *   dst[s][0] = src[s][0],   dst[s][1 + i] = src[s][keep_rows[c][i]],
+ * for every KV head, in K and in V.  The copy is bit-exact; destination rows
+ * past b and slots of no listed chunk are not written.  A decode over the
+ * destination with rows_compacted = 1 and the same b attends exactly the rows
+ * a decode over the source with keep_rows attends, in the same order.
+ *   src        the whole-chunk pool
+ *   chunk_slot device [n_chunks]
+ *   keep_rows  device [n_chunks][b] rows in 1..src->slot_rows-1 (as written by
+ *              pdllm_select_topB); may be NULL when b = 0
+ *   dst_k, dst_v  device, the source's dtype, h_kv, d and n_slots, with
+ *              dst_slot_rows >= b + 1 rows per slot and element strides
+ *              dst_stride_slot, dst_stride_row, dst_stride_head (d contiguous;
+ *              the same rules as a pdllm_pool's); must not overlap the source
+ * Supported: every dtype and d a pdllm_pool supports; 0 <= b <= slot_rows - 1.
+ */
+pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk_slot, int32_t n_chunks,
+                                     const int32_t* keep_rows, int32_t b, void* dst_k, void* dst_v,
+                                     int64_t dst_stride_slot, int64_t dst_stride_row,
+                                     int64_t dst_stride_head, int32_t dst_slot_rows, void* stream);
 
 /* Bytes of workspace pdllm_chunk_score needs (0 when the arguments are
  * invalid).  Pure host function. */

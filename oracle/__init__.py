@@ -11,10 +11,12 @@ invariants); none is "parity unpinned".
 """
 from .reference import (as_f64, kv_head_of, softmax_rows, chunk_prefill_score,
                         select_topb, select_topk, attended_pool_rows, attended_kv,
+                        compact_kept_rows, all_rows_kept,
                         split_attn_decode, lse_merge, attention_over_parts,
                         token_log_probs, chunk_scores)
 
 __all__ = ["as_f64", "kv_head_of", "softmax_rows", "chunk_prefill_score",
            "select_topb", "select_topk", "attended_pool_rows", "attended_kv",
+           "compact_kept_rows", "all_rows_kept",
            "split_attn_decode", "lse_merge", "attention_over_parts",
            "token_log_probs", "chunk_scores"]

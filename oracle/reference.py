@@ -203,6 +203,37 @@ def attended_pool_rows(chunk_slot, sel_chunk, keep_rows, k_s: int, seq: int,
     return np.asarray(slots, dtype=np.int64), np.asarray(rows, dtype=np.int64)
 
 
+def compact_kept_rows(pool_k, pool_v, chunk_slot, keep_rows, n_chunks: int):
+    """Kept-row cache of the first ``n_chunks`` chunks (Methodology 2: after
+    the intra-chunk selection only a chunk's top-B tokens stay in the KV
+    cache; the BOS anchor stays with them).
+
+    pool_k, pool_v : [n_slots][R][h_kv][d];  keep_rows : [n_chunks][b]
+    Returns (k, v, written): [n_slots][b + 1][h_kv][d] arrays of the pool's
+    dtype where slot s = chunk_slot[c] holds the chunk's BOS row, then its
+    kept rows in keep_rows order; ``written`` [n_slots] flags the slots that
+    hold a chunk (the others are zero).
+    """
+    n_slots, _, h_kv, d = pool_k.shape
+    b = keep_rows.shape[1]
+    k = np.zeros((n_slots, b + 1, h_kv, d), dtype=pool_k.dtype)
+    v = np.zeros_like(k)
+    written = np.zeros(n_slots, dtype=bool)
+    for c in range(n_chunks):
+        slot = int(chunk_slot[c])
+        rows = [0] + [int(x) for x in keep_rows[c]]
+        k[slot] = pool_k[slot, rows]
+        v[slot] = pool_v[slot, rows]
+        written[slot] = True
+    return k, v, written
+
+
+def all_rows_kept(n_chunks: int, b: int) -> np.ndarray:
+    """The keep_rows table of compacted slots: chunk c's kept rows are rows
+    1..b of its slot ([n_chunks][b] int32)."""
+    return np.tile(np.arange(1, b + 1, dtype=np.int32), (n_chunks, 1))
+
+
 def attended_kv(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_s, seq,
                 n_chunks_per_seq, k_resp, v_resp):
     """Dense [N_kv][h_kv][d] float64 keys and values attended by ``seq``:

@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 3
+    assert L.lib.pdllm_abi_version() == 4
 
 
 def _pool(**kw):
@@ -60,10 +60,10 @@ def _pool(**kw):
 def _pt(ks, **kw):
     arr = (ctypes.c_int32 * len(ks))(*ks)
     f = dict(chunk_slot=0x30000, sel_chunk=0x40000, keep_rows=0x50000, n_chunks_per_seq=128,
-             k_max=16, b=256)
+             k_max=16, b=256, rows_compacted=0)
     f.update(kw)
     pt = L.PageTable(f["chunk_slot"], f["sel_chunk"], f["keep_rows"], ctypes.cast(arr, ctypes.c_void_p),
-                     f["n_chunks_per_seq"], f["k_max"], f["b"])
+                     f["n_chunks_per_seq"], f["k_max"], f["b"], f["rows_compacted"])
     return pt, arr
 
 
@@ -96,12 +96,15 @@ def _err():
     (dict(o=0x90004), INVALID, "aligned"),
     (dict(scale=float("nan")), INVALID, "scale"),
     (dict(splits=-1), INVALID, "num_splits"),
+    (dict(keep_rows=None), INVALID, "keep_rows is NULL"),
+    (dict(rows_compacted=2), INVALID, "rows_compacted"),
+    (dict(keep_rows=None, rows_compacted=1), WS_SMALL, "workspace"),   # compacted: keep_rows unread
     (dict(), WS_SMALL, "workspace"),
 ])
 def test_decode_validation(mutate, code, msg):
     pool_kw = {k: mutate[k] for k in ("dtype", "d", "stride_head", "stride_row", "k") if k in mutate}
     pool = None if "pool" in mutate else _pool(**pool_kw)
-    pt_kw = {k: mutate[k] for k in ("b", "k_max") if k in mutate}
+    pt_kw = {k: mutate[k] for k in ("b", "k_max", "keep_rows", "rows_compacted") if k in mutate}
     pt, _keep = _pt(mutate.get("k_per_seq", [16]), **pt_kw)
     call = {k: mutate[k] for k in ("h_q", "l_d", "q", "o", "scale", "splits") if k in mutate}
     st = _decode(pool, pt, **call)
@@ -204,3 +207,27 @@ def test_chunk_score_validation():
     assert f(*args(nq=-1)) == INVALID
     assert f(*args(ws_bytes=need - 1)) == WS_SMALL
     assert f(*args(n=0)) == OK                                      # nothing to do, nothing enqueued
+
+
+def test_compaction_validation():
+    f = L.lib.pdllm_compact_kept_rows
+    pool = _pool()
+    # destination: [128][b + 1 = 129][4][128] dense
+    args = lambda **kw: [ctypes.byref(kw.get("pool", pool)), kw.get("slot", 0x30000), kw.get("n", 128),
+                         kw.get("keep", 0x50000), kw.get("b", 128), kw.get("dk", 0x100000), kw.get("dv", 0x200000),
+                         kw.get("ss", 129 * 512), kw.get("sr", 512), kw.get("sh", 128), kw.get("rows", 129), None]
+    assert f(*args(b=257)) == INVALID                      # b > slot_rows - 1
+    assert "b 257" in _err()
+    assert f(*args(b=-1)) == INVALID
+    assert f(*args(rows=128)) == INVALID                   # dst_slot_rows < b + 1
+    assert "dst_slot_rows" in _err()
+    assert f(*args(ss=128 * 512)) == INVALID               # dst slots overlap
+    assert f(*args(sh=132)) == INVALID                     # dst stride not a multiple of 8
+    assert f(*args(dk=0x100008)) == INVALID                # dst not 16-byte aligned
+    assert f(*args(dv=None)) == INVALID
+    assert f(*args(keep=None)) == INVALID
+    assert "keep_rows is NULL" in _err()
+    assert f(*args(slot=None)) == INVALID
+    assert f(*args(n=-1)) == INVALID
+    assert f(*args(pool=_pool(d=96))) == UNSUPPORTED
+    assert f(*args(n=0)) == OK                              # nothing to do, nothing enqueued

@@ -1,7 +1,8 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the
 pins catch each of them.  This shows the pins are sensitive to a wrong
 head map, a wrong softmax axis, a dropped BOS row, a dropped scale, a wrong
-merge weight and a wrong tie rule -- not only to gross breakage."""
+merge weight, a wrong tie rule, wrong log-softmax terms and a misplaced BOS
+row or slot in the kept-row compaction -- not only to gross breakage."""
 import numpy as np
 import pytest
 
@@ -108,3 +109,37 @@ def test_flipped_or_swapped_score_parts_are_caught(monkeypatch):
                         lambda z, t, nq, npp: orig(z[:, ::-1], t[:, ::-1], nq, npp))
     monkeypatch.setattr(oracle, "chunk_scores", ref.chunk_scores)
     _fails(cp.test_chunk_score_signs_and_rows)
+
+
+def test_compaction_without_bos_is_caught(monkeypatch):
+    import test_oracle_compact_pins as cp
+
+    def no_bos(pool_k, pool_v, chunk_slot, keep_rows, n_chunks):
+        n_slots, _, h_kv, d = pool_k.shape
+        b = keep_rows.shape[1]
+        k = np.zeros((n_slots, b + 1, h_kv, d), dtype=pool_k.dtype)
+        v = np.zeros_like(k)
+        written = np.zeros(n_slots, dtype=bool)
+        for c in range(n_chunks):
+            slot = int(chunk_slot[c])
+            rows = [int(x) for x in keep_rows[c]] + [0]    # BOS moved behind the kept rows
+            k[slot], v[slot] = pool_k[slot, rows], pool_v[slot, rows]
+            written[slot] = True
+        return k, v, written
+    monkeypatch.setattr(oracle, "compact_kept_rows", no_bos)
+    _fails(cp.test_compacted_rows_carry_their_source_coordinates, 5)
+
+
+def test_compaction_into_chunk_index_is_caught(monkeypatch):
+    import test_oracle_compact_pins as cp
+    orig = ref.compact_kept_rows
+
+    def by_chunk(pool_k, pool_v, chunk_slot, keep_rows, n_chunks):
+        # chunk c lands in slot c instead of slot chunk_slot[c]
+        k, v, written = orig(pool_k, pool_v, chunk_slot, keep_rows, n_chunks)
+        perm = np.asarray(chunk_slot[:n_chunks])
+        k2, v2 = np.zeros_like(k), np.zeros_like(v)
+        k2[:n_chunks], v2[:n_chunks] = k[perm], v[perm]
+        return k2, v2, written
+    monkeypatch.setattr(oracle, "compact_kept_rows", by_chunk)
+    _fails(cp.test_compacted_rows_carry_their_source_coordinates, 5)
