@@ -95,6 +95,9 @@ def parse():
     p.add_argument("--compact", action="store_true",
                    help="diagnostic: kept-row compaction of a 32K prefix (128 chunks, B = 128) and the "
                         "decode over the compacted slots against the decode through keep_rows")
+    p.add_argument("--decode-sweep", action="store_true",
+                   help="diagnostic: decode calls at the 32K prefix over K in {4, 8, 16, 32} and "
+                        "L_d in {16, 32, 256}, warm and with the caches flushed, median / p10 / p90")
     p.add_argument("--chunk", type=int, default=0,
                    help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
                         "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
@@ -443,6 +446,88 @@ def compact_run(args):
                       "outputs_identical": same, "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def decode_sweep(args):
+    """Decode calls at the 32K prefix (128 chunks of 256 + BOS, 28/4 heads,
+    d = 128, B = 256) over K in {4, 8, 16, 32} and L_d in {16, 32, 256}: the
+    time should grow linearly in K at fixed L_d, and at small L_d the KV
+    gather is memory-bound (7 L_d FLOP per byte of K/V).  Each point is timed
+    warm (a HIP graph of one call, replayed) and cold (a 512 MB write before
+    each call evicts the L2s and the Infinity Cache); one JSON line per point
+    with the median, p10 and p90 of the per-call times."""
+    import torch
+    import synth
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    base = synth.config("s32")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    pool_k = rnd(base.n_slots, base.rows, base.h_kv, base.d)
+    pool_v = rnd(base.n_slots, base.rows, base.h_kv, base.d)
+    q_all = rnd(1, 256, base.h_q, base.d)
+    kr_all = rnd(1, 256, base.h_kv, base.d)
+    vr_all = rnd(1, 256, base.h_kv, base.d)
+    chunk_slot = torch.from_numpy(np.random.default_rng(args.seed).permutation(base.n_slots)
+                                  .astype(np.int32)).to(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n = max(args.steps, 20)
+
+    def stats(ts):
+        ts = np.asarray(ts) * 1e3            # ms -> us
+        return {"median": float(np.median(ts)), "p10": float(np.percentile(ts, 10)),
+                "p90": float(np.percentile(ts, 90))}
+
+    for l_d in (16, 32, 256):
+        q = q_all[:, :l_d].contiguous()
+        k_resp, v_resp = kr_all[:, :l_d].contiguous(), vr_all[:, :l_d].contiguous()
+        for k in (4, 8, 16, 32):
+            cfg = synth.config("s32", l_d=l_d, k_per_seq=(k,))
+            sel_h, keep_h = synth.random_page_table(cfg, args.seed)
+            sel = torch.from_numpy(np.ascontiguousarray(sel_h)).to(dev)
+            keep = torch.from_numpy(np.ascontiguousarray(keep_h)).to(dev)
+            call = L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp,
+                            cfg.scale)
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.current_stream(dev).wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                call()
+            times = {}
+            for mode in ("warm", "cold"):
+                for _ in range(args.warmup):
+                    graph.replay()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+                for e0, e1 in ev:
+                    if mode == "cold":
+                        flush.fill_(1)
+                    e0.record()
+                    graph.replay()
+                    e1.record()
+                torch.cuda.synchronize()
+                times[mode] = stats([e0.elapsed_time(e1) for e0, e1 in ev])
+            n_kv = k * (cfg.b + 1) + l_d
+            flops = 4.0 * l_d * cfg.h_q * cfg.d * n_kv
+            kv_bytes = 2.0 * n_kv * cfg.h_kv * cfg.d * 2
+            nbytes = kv_bytes + 2.0 * l_d * cfg.h_q * cfg.d * 2          # + q and o
+            rec = {"diagnostic": "decode sweep, 32K prefix, B=256, 28/4 heads, d=128, one call per replay",
+                   "k": k, "l_d": l_d, "n_kv": n_kv, "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                   "kv_gather_bytes": kv_bytes, "flop_per_byte": flops / nbytes}
+            for mode, st in times.items():
+                t = st["median"] * 1e-6
+                rec[mode] = dict(st, tflops=flops / t / 1e12, gbs=nbytes / t / 1e9,
+                                 mfma_frac=flops / t / 1e12 / BF16_PEAK_TFLOPS,
+                                 hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS)
+            print(json.dumps(rec), flush=True)
+            del graph, call
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -465,6 +550,9 @@ def main():
         return
     if args.compact:
         compact_run(args)
+        return
+    if args.decode_sweep:
+        decode_sweep(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L
@@ -520,7 +608,8 @@ def main():
     wall = time.perf_counter() - t_start
     stage_ms = {name: float(np.mean([ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(args.steps)]))
                 for j, (name, _) in enumerate(stages)}
-    step_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]))
+    step_all = [ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]
+    step_ms = float(np.mean(step_all))
 
     flops, bytes_ = workload_counts(cfg)
     names = [n for n, _ in stages]
@@ -564,6 +653,9 @@ def main():
         "config": {"workload": "32K prefix: 128 chunks x (256+BOS), 28/4 heads, d=128, K=16, B=256, "
                                "L_d=256, window 64; prefill side + top-B + top-K + split decode, 1 layer",
                    "global_batch": cfg.n_seq, "seq_len": cfg.n_chunks * cfg.chunk + cfg.l_d},
+        "step_us_percentiles": {"median": float(np.median(step_all)) * 1e3,
+                                "p10": float(np.percentile(step_all, 10)) * 1e3,
+                                "p90": float(np.percentile(step_all, 90)) * 1e3},
         "stage_us": {n: stage_ms[n] * 1e3 for n in names},
         "roofline": roof(dominant),
         "rooflines": {n: roof(n) for n in names if flops[n] > 0},
