@@ -97,7 +97,7 @@ def softmax_rows(z: np.ndarray):
 # prefill side: chunk-local attention and per-key scoring
 # --------------------------------------------------------------------------
 def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win,
-                        scale, chunks: Optional[Sequence[int]] = None):
+                        scale, chunks: Optional[Sequence[int]] = None, chunk_rows=None):
     """Chunk-local bidirectional attention plus per-key cumulative weight.
 
     Methodology 1 (each chunk, BOS first, attends only to itself) and
@@ -108,12 +108,18 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
     q_chunk        : [n_chunks][R][h_q][d]   the chunk's own queries
     q_win          : [n_win][W][h_q][d]      chunk c is scored by window
                                              c // chunks_per_win
+    chunk_rows     : optional [n_chunks] rows held by each chunk (default R).
+                     A prefix whose length is not a multiple of C ends in a
+                     partial chunk: its BOS and the C' < C remaining tokens,
+                     R_c = C' + 1 rows at the start of its slot.
     Returns (o_chunk [len(chunks)][R][h_q][d], key_score [len(chunks)][R]),
     both float64, for ``chunks`` (default: all chunks, in order).
 
     o_chunk[c, r, h]  = sum_j softmax_j(scale <Qc[c,r,h], K[slot,j,g]>) V[slot,j,g]
     key_score[c, j]   = sum_h sum_w softmax_j(scale <Qw[w,h], K[slot,j,g]>)
-    with g = kv_head_of(h, G) and j over the chunk's R rows.
+    with g = kv_head_of(h, G) and r, j over the chunk's R_c rows: a partial
+    chunk is a chunk of R_c rows.  Its output rows r >= R_c are not defined
+    (NaN here) and its keys j >= R_c score 0.
     """
     n_chunks = q_chunk.shape[0]
     _, r_rows, h_kv, _ = pool_k.shape
@@ -127,17 +133,19 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
     score = np.zeros((len(chunks), r_rows))
     for n, c in enumerate(chunks):
         slot = int(chunk_slot[c])
-        kk = as_f64(pool_k[slot])          # [R][h_kv][d]
-        vv = as_f64(pool_v[slot])
-        qc = as_f64(q_chunk[c])            # [R][h_q][d]
+        rc = r_rows if chunk_rows is None else int(chunk_rows[c])
+        kk = as_f64(pool_k[slot, :rc])     # [R_c][h_kv][d]
+        vv = as_f64(pool_v[slot, :rc])
+        qc = as_f64(q_chunk[c, :rc])       # [R_c][h_q][d]
         qw = as_f64(q_win[c // chunks_per_win])   # [W][h_q][d]
+        o[n, rc:] = np.nan
         for h in range(h_q):
             g = kv_head_of(h, group)
             k_g, v_g = kk[:, g, :], vv[:, g, :]
-            p, _, _ = softmax_rows(scale * (qc[:, h, :] @ k_g.T))      # [R][R]
-            o[n, :, h, :] = p @ v_g
-            pw, _, _ = softmax_rows(scale * (qw[:, h, :] @ k_g.T))     # [W][R]
-            score[n] += pw.sum(axis=0)
+            p, _, _ = softmax_rows(scale * (qc[:, h, :] @ k_g.T))      # [R_c][R_c]
+            o[n, :rc, h, :] = p @ v_g
+            pw, _, _ = softmax_rows(scale * (qw[:, h, :] @ k_g.T))     # [W][R_c]
+            score[n, :rc] += pw.sum(axis=0)
     return o, score
 
 
@@ -156,17 +164,22 @@ def _top(values: np.ndarray, candidates: Sequence[int], count: int) -> List[int]
     return sorted(order[:count])
 
 
-def select_topb(key_score: np.ndarray, b: int) -> np.ndarray:
+def select_topb(key_score: np.ndarray, b: int, chunk_rows=None) -> np.ndarray:
     """Top-B content rows of every chunk (Methodology 2, intra-chunk sparsity).
 
-    key_score : [n_chunks][R] (float32 as the GPU holds it, or float64)
-    Returns keep_rows [n_chunks][b] int32: the b best rows among 1..R-1 (row 0
-    is the BOS anchor, always kept and not a candidate), ascending.
+    key_score  : [n_chunks][R] (float32 as the GPU holds it, or float64)
+    chunk_rows : optional [n_chunks] rows held by each chunk (default R)
+    Returns keep_rows [n_chunks][b] int32: the b best rows among 1..R_c-1 (row
+    0 is the BOS anchor, always kept and not a candidate), ascending.  A
+    partial chunk with fewer than b content rows keeps all of them, and the
+    rest of its entries are -1 (absent).
     """
     n_chunks, r_rows = key_score.shape
-    out = np.empty((n_chunks, b), dtype=np.int32)
+    out = np.full((n_chunks, b), -1, dtype=np.int32)
     for c in range(n_chunks):
-        out[c] = _top(key_score[c], range(1, r_rows), b)
+        rc = r_rows if chunk_rows is None else int(chunk_rows[c])
+        kept = _top(key_score[c], range(1, rc), min(b, rc - 1))
+        out[c, :len(kept)] = kept
     return out
 
 
@@ -192,12 +205,13 @@ def select_topk(chunk_score: np.ndarray, k_per_seq: Sequence[int], k_max: int) -
 def attended_pool_rows(chunk_slot, sel_chunk, keep_rows, k_s: int, seq: int,
                        n_chunks_per_seq: int) -> Tuple[np.ndarray, np.ndarray]:
     """(slot, row) of every cached row sequence ``seq`` attends to, in chunk
-    order: for each selected chunk, BOS row 0 then its kept rows."""
+    order: for each selected chunk, BOS row 0 then its kept rows (absent
+    entries, -1, of a partial chunk are skipped)."""
     slots, rows = [], []
     for k in range(k_s):
         c = seq * n_chunks_per_seq + int(sel_chunk[seq][k])
         slot = int(chunk_slot[c])
-        for r in [0] + [int(x) for x in keep_rows[c]]:
+        for r in [0] + [int(x) for x in keep_rows[c] if x >= 0]:
             slots.append(slot)
             rows.append(r)
     return np.asarray(slots, dtype=np.int64), np.asarray(rows, dtype=np.int64)
@@ -211,20 +225,23 @@ def compact_kept_rows(pool_k, pool_v, chunk_slot, keep_rows, n_chunks: int):
     pool_k, pool_v : [n_slots][R][h_kv][d];  keep_rows : [n_chunks][b]
     Returns (k, v, written): [n_slots][b + 1][h_kv][d] arrays of the pool's
     dtype where slot s = chunk_slot[c] holds the chunk's BOS row, then its
-    kept rows in keep_rows order; ``written`` [n_slots] flags the slots that
-    hold a chunk (the others are zero).
+    kept rows in keep_rows order; ``written`` [n_slots][b + 1] flags the rows
+    that hold a row of a chunk (the others are zero): an absent entry (-1) of
+    a partial chunk writes nothing.
     """
     n_slots, _, h_kv, d = pool_k.shape
     b = keep_rows.shape[1]
     k = np.zeros((n_slots, b + 1, h_kv, d), dtype=pool_k.dtype)
     v = np.zeros_like(k)
-    written = np.zeros(n_slots, dtype=bool)
+    written = np.zeros((n_slots, b + 1), dtype=bool)
     for c in range(n_chunks):
         slot = int(chunk_slot[c])
-        rows = [0] + [int(x) for x in keep_rows[c]]
-        k[slot] = pool_k[slot, rows]
-        v[slot] = pool_v[slot, rows]
-        written[slot] = True
+        for j, r in enumerate([0] + [int(x) for x in keep_rows[c]]):
+            if r < 0:
+                continue
+            k[slot, j] = pool_k[slot, r]
+            v[slot, j] = pool_v[slot, r]
+            written[slot, j] = True
     return k, v, written
 
 

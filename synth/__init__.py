@@ -58,6 +58,7 @@ class Config:
     key_dist: str = "normal"     # "normal" or "t4" (Student-t, 4 dof)
     layers: int = 1
     steps: int = 1
+    last_chunk: int = 0          # tokens of each sequence's last chunk (0: C, a full chunk)
 
     @property
     def rows(self) -> int:
@@ -66,6 +67,15 @@ class Config:
     @property
     def n_slots(self) -> int:
         return self.n_seq * self.n_chunks
+
+    @property
+    def chunk_rows(self) -> np.ndarray:
+        """[n_seq*N] int32 rows held by each chunk: R, except a partial last
+        chunk of each sequence (BOS + last_chunk tokens)."""
+        rows = np.full((self.n_seq, self.n_chunks), self.rows, dtype=np.int32)
+        if self.last_chunk:
+            rows[:, -1] = self.last_chunk + 1
+        return rows.reshape(-1)
 
     @property
     def k_max(self) -> int:
@@ -189,6 +199,18 @@ def generate(cfg: Config, seed: int = 0, with_q_chunk: bool = False) -> Inputs:
     if with_q_chunk:
         inp.q_chunk = _finish(
             rng.standard_normal((n_slots, r, hq, d), dtype=np.float32), cfg.dtype)
+    # A partial last chunk holds last_chunk + 1 rows; the rest of its slot
+    # (and of its queries) is filled with large values, drawn from nothing,
+    # so that any use of those rows shows in the results.
+    if cfg.last_chunk:
+        keep_rows = cfg.last_chunk + 1
+        big_k, big_v = _finish(np.float32([30.0]), cfg.dtype)[0], _finish(np.float32([1000.0]), cfg.dtype)[0]
+        for c in np.flatnonzero(cfg.chunk_rows < r):
+            slot = int(chunk_slot[c])
+            pool_k[slot, keep_rows:] = big_k
+            pool_v[slot, keep_rows:] = big_v
+            if inp.q_chunk is not None:
+                inp.q_chunk[c, keep_rows:] = big_k
     return inp
 
 
@@ -198,16 +220,20 @@ def random_page_table(cfg: Config, seed: int = 0):
     Returns ``(sel_chunk [n_seq][k_max] int32, keep_rows [n_seq*N][B] int32)``:
     each sequence's first K_s entries of ``sel_chunk`` are distinct chunk ids
     in ascending order, the rest are -1; each row of ``keep_rows`` holds B
-    distinct content rows from 1..C in ascending order.
+    distinct content rows from 1..C in ascending order (a partial last chunk
+    with fewer than B content rows: all of them, then -1).
     """
     rng = np.random.default_rng(1_000_003 + seed)
     k_max = cfg.k_max
     sel = np.full((cfg.n_seq, max(k_max, 0)), -1, dtype=np.int32)
     for s, ks in enumerate(cfg.k_per_seq):
         sel[s, :ks] = np.sort(rng.choice(cfg.n_chunks, size=ks, replace=False))
-    keep = np.empty((cfg.n_slots, cfg.b), dtype=np.int32)
+    keep = np.full((cfg.n_slots, cfg.b), -1, dtype=np.int32)
+    rows = cfg.chunk_rows
     for c in range(cfg.n_slots):
-        keep[c] = np.sort(rng.choice(np.arange(1, cfg.chunk + 1), size=cfg.b, replace=False))
+        n_c = int(rows[c]) - 1               # content rows of the chunk
+        count = min(cfg.b, n_c)
+        keep[c, :count] = np.sort(rng.choice(np.arange(1, n_c + 1), size=count, replace=False))
     return sel, keep
 
 

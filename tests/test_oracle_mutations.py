@@ -119,7 +119,7 @@ def test_compaction_without_bos_is_caught(monkeypatch):
         b = keep_rows.shape[1]
         k = np.zeros((n_slots, b + 1, h_kv, d), dtype=pool_k.dtype)
         v = np.zeros_like(k)
-        written = np.zeros(n_slots, dtype=bool)
+        written = np.zeros((n_slots, b + 1), dtype=bool)
         for c in range(n_chunks):
             slot = int(chunk_slot[c])
             rows = [int(x) for x in keep_rows[c]] + [0]    # BOS moved behind the kept rows
@@ -143,3 +143,29 @@ def test_compaction_into_chunk_index_is_caught(monkeypatch):
         return k2, v2, written
     monkeypatch.setattr(oracle, "compact_kept_rows", by_chunk)
     _fails(cp.test_compacted_rows_carry_their_source_coordinates, 5)
+
+
+def test_partial_chunk_read_as_whole_is_caught(monkeypatch):
+    import test_oracle_partial_pins as pp
+    orig = ref.chunk_prefill_score
+    monkeypatch.setattr(oracle, "chunk_prefill_score",
+                        lambda *a, chunk_rows=None, **k: orig(*a, **k))
+    _fails(pp.test_partial_chunk_prefill_is_sdpa_over_its_rows, 0, {})
+    orig_b = ref.select_topb
+    monkeypatch.setattr(oracle, "select_topb", lambda s, b, chunk_rows=None: orig_b(s, b))
+    _fails(pp.test_topb_of_a_partial_chunk, 3)
+
+
+def test_absent_row_read_as_a_row_is_caught(monkeypatch):
+    import test_oracle_partial_pins as pp
+
+    def with_absent(chunk_slot, sel_chunk, keep_rows, k_s, seq, n_chunks_per_seq):
+        slots, rows = [], []
+        for k in range(k_s):
+            c = seq * n_chunks_per_seq + int(sel_chunk[seq][k])
+            for r in [0] + [int(x) for x in keep_rows[c]]:       # -1 indexes the slot's last row
+                slots.append(int(chunk_slot[c]))
+                rows.append(r)
+        return np.asarray(slots, dtype=np.int64), np.asarray(rows, dtype=np.int64)
+    monkeypatch.setattr(ref, "attended_pool_rows", with_absent)
+    _fails(pp.test_decode_skips_absent_rows, 0)
