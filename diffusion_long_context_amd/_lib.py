@@ -55,10 +55,10 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_prefill_score_workspace.restype = sz
     lib.pdllm_prefill_score_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.pdllm_chunk_prefill_score.restype = ctypes.c_int
-    lib.pdllm_chunk_prefill_score.argtypes = [P(Pool), vp, i32, vp, i32, vp, i32, i32, f32, vp, vp,
+    lib.pdllm_chunk_prefill_score.argtypes = [P(Pool), vp, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp,
                                               vp, sz, vp]
     lib.pdllm_select_topB.restype = ctypes.c_int
-    lib.pdllm_select_topB.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.pdllm_select_topB.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.pdllm_select_topK.restype = ctypes.c_int
     lib.pdllm_select_topK.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     lib.pdllm_decode_plan.restype = ctypes.c_int
@@ -79,7 +79,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-ABI_VERSION = 4
+ABI_VERSION = 5
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -128,11 +128,17 @@ def make_pool(pool_k: torch.Tensor, pool_v: torch.Tensor) -> Pool:
 
 
 def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win, scale,
-                        o_chunk=None, key_score=None, workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                        o_chunk=None, key_score=None, workspace=None,
+                        chunk_rows=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """pdllm_chunk_prefill_score.  q_chunk [n_chunks][R][h_q][d], q_win
-    [n_win][W][h_q][d]; returns (o_chunk, key_score [n_chunks][R] float32)."""
+    [n_win][W][h_q][d], chunk_rows [n_chunks] int32 or None (every chunk
+    whole); returns (o_chunk, key_score [n_chunks][R] float32)."""
     pool = make_pool(pool_k, pool_v)
     _dense(chunk_slot, "chunk_slot", torch.int32)
+    if chunk_rows is not None:
+        _dense(chunk_rows, "chunk_rows", torch.int32)
+        if chunk_rows.numel() < q_chunk.shape[0]:
+            raise ValueError("chunk_rows must hold n_chunks entries")
     _dense(q_chunk, "q_chunk", pool_k.dtype)
     _dense(q_win, "q_win", pool_k.dtype)
     n_chunks, rows, h_q, d = q_chunk.shape
@@ -151,7 +157,7 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
     need = lib.pdllm_prefill_score_workspace(n_chunks, h_q, pool.h_kv, rows, w)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check(lib.pdllm_chunk_prefill_score(ctypes.byref(pool), chunk_slot.data_ptr(), n_chunks,
+    _check(lib.pdllm_chunk_prefill_score(ctypes.byref(pool), chunk_slot.data_ptr(), _ptr(chunk_rows), n_chunks,
                                          q_chunk.data_ptr(), h_q, q_win.data_ptr(), w, chunks_per_win,
                                          float(scale), o_chunk.data_ptr(), key_score.data_ptr(),
                                          workspace.data_ptr(), workspace.numel(), _stream(dev)),
@@ -159,13 +165,19 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
     return o_chunk, key_score
 
 
-def select_topb(key_score: torch.Tensor, b: int, keep_rows=None) -> torch.Tensor:
-    """pdllm_select_topB: key_score [n_chunks][R] float32 -> [n_chunks][b] int32."""
+def select_topb(key_score: torch.Tensor, b: int, keep_rows=None, chunk_rows=None) -> torch.Tensor:
+    """pdllm_select_topB: key_score [n_chunks][R] float32 -> [n_chunks][b] int32
+    (-1 entries for a partial chunk of fewer than b content rows, given by
+    chunk_rows [n_chunks] int32)."""
     _dense(key_score, "key_score", torch.float32)
     n_chunks, rows = key_score.shape
+    if chunk_rows is not None:
+        _dense(chunk_rows, "chunk_rows", torch.int32)
+        if chunk_rows.numel() < n_chunks:
+            raise ValueError("chunk_rows must hold n_chunks entries")
     if keep_rows is None:
         keep_rows = torch.empty((n_chunks, b), dtype=torch.int32, device=key_score.device)
-    _check(lib.pdllm_select_topB(key_score.data_ptr(), n_chunks, rows, b, keep_rows.data_ptr(),
+    _check(lib.pdllm_select_topB(key_score.data_ptr(), _ptr(chunk_rows), n_chunks, rows, b, keep_rows.data_ptr(),
                                  _stream(key_score.device)), "pdllm_select_topB")
     return keep_rows
 
@@ -264,18 +276,20 @@ class Decode:
     """A prepared pdllm_split_attn_decode call: the structs, host K_s array,
     outputs and workspace are built once so repeated calls (timing loops,
     denoising steps) only cross the boundary.  ``keep_rows`` is the
-    [n_seq * N][b] table over a whole-chunk pool, or None for a pool of
-    compacted slots (pdllm_compact_kept_rows) whose kept rows are rows
-    1..``b``."""
+    [n_seq * N][b] table over a whole-chunk pool (-1 entries: absent rows of a
+    partial chunk).  For a pool of compacted slots (pdllm_compact_kept_rows),
+    whose kept rows are rows 1..b, pass ``compacted=True`` with ``keep_rows``
+    (read only for its -1 entries) or with keep_rows=None and ``b``."""
 
     def __init__(self, pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                 v_resp, scale, num_splits=0, want_lse=True, out=None, b=None):
+                 v_resp, scale, num_splits=0, want_lse=True, out=None, b=None, compacted=False):
         self.pool = make_pool(pool_k, pool_v)
-        compacted = keep_rows is None
-        if compacted:
+        compacted = compacted or keep_rows is None
+        no_table = keep_rows is None
+        if no_table:
             if b is None:
-                raise ValueError("a compacted pool needs b")
-            keep_rows = torch.empty((chunk_slot.numel(), 0), dtype=torch.int32, device=q.device)
+                raise ValueError("a compacted pool without keep_rows needs b")
+            keep_rows = torch.empty((chunk_slot.numel(), int(b)), dtype=torch.int32, device=q.device)
         for t, name in ((chunk_slot, "chunk_slot"), (sel_chunk, "sel_chunk"), (keep_rows, "keep_rows")):
             _dense(t, name, torch.int32)
         _dense(q, "q", pool_k.dtype)
@@ -291,10 +305,9 @@ class Decode:
         self._keep = (chunk_slot, sel_chunk, keep_rows, q, k_resp, v_resp, pool_k, pool_v)
         self.ks = (ctypes.c_int32 * n_seq)(*[int(x) for x in k_per_seq])
         self.pt = PageTable(chunk_slot.data_ptr(), sel_chunk.data_ptr(),
-                            None if compacted else keep_rows.data_ptr(),
+                            None if no_table else keep_rows.data_ptr(),
                             ctypes.cast(self.ks, ctypes.c_void_p), chunk_slot.numel() // n_seq,
-                            sel_chunk.shape[1], int(b) if compacted else keep_rows.shape[1],
-                            1 if compacted else 0)
+                            sel_chunk.shape[1], keep_rows.shape[1], 1 if compacted else 0)
         self.n_seq, self.l_d, self.h_q = n_seq, l_d, h_q
         self.scale = float(scale)
         self.num_splits = int(num_splits)
@@ -317,8 +330,8 @@ class Decode:
 
 
 def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                      v_resp, scale, num_splits=0, want_lse=True, b=None):
+                      v_resp, scale, num_splits=0, want_lse=True, b=None, compacted=False):
     """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None).
-    keep_rows=None with ``b`` decodes over a pool of compacted slots."""
+    compacted=True (or keep_rows=None with ``b``) decodes over a pool of compacted slots."""
     return Decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp, v_resp,
-                  scale, num_splits, want_lse, b=b)()
+                  scale, num_splits, want_lse, b=b, compacted=compacted)()

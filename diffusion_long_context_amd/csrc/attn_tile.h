@@ -28,6 +28,11 @@
 namespace pdllm {
 
 constexpr float kRescaleLog2 = 8.0f;
+// Starting reference max: finite, so that a block with every row masked
+// (scores -inf) gives p = 2^(-inf - kNoMax) = 0 rather than NaN, and below
+// any score, so that the first block with a counted row replaces it
+// (its rescale factor 2^(kNoMax - m) is 0 on the still-empty sums).
+constexpr float kNoMax = -1e30f;
 
 // D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on one wavefront: lane l
 // supplies A row l % 32 and B column l % 32 with the eight k values
@@ -78,7 +83,7 @@ struct WaveAttn {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
     l_run = 0.f;
-    m_run = -INFINITY;
+    m_run = kNoMax;
   }
 
   // S^T for kv rows [0, 32 NK) of an LDS block: k_lane = &K[c][8 j] (pitch
@@ -100,21 +105,24 @@ struct WaveAttn {
   // interleave the S^T MFMAs of the next block with this block's exp work.
   //
   // (1) Mask, row max and the lazy rescale (the only branches).  Only rows in
-  // [valid_lo, valid_hi) count; the rest are masked (a wave-uniform branch,
-  // taken only by a partial block).
+  // [valid_lo, valid_hi) whose bit in `absent` is clear count; the rest are
+  // masked (a wave-uniform branch, taken only by a partial block or one with
+  // absent rows).  valid_hi must be >= valid_lo.
   template <int NK>
   __device__ __forceinline__ void prep(f32x16 (&sc)[NK], float sl2, int valid_hi, int j,
-                                       int valid_lo = 0) {
-    if (__builtin_expect(valid_hi < 32 * NK || valid_lo > 0, 0)) {
+                                       int valid_lo = 0, uint64_t absent = 0) {
+    if (__builtin_expect(valid_hi < 32 * NK || valid_lo > 0 || absent != 0, 0)) {
       // rows r valid iff valid_lo <= r < valid_hi, as one unsigned compare
       const unsigned span = (unsigned)(valid_hi - valid_lo);
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb)
+      for (int kb = 0; kb < NK; ++kb) {
+        const uint32_t half = (uint32_t)(absent >> (32 * kb)) >> (4 * j);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 32 * kb + 8 * (i >> 2) + 4 * j + (i & 3);
-          if ((unsigned)(r - valid_lo) >= span) sc[kb][i] = -INFINITY;
+          if ((unsigned)(r - valid_lo) >= span || ((half >> (8 * (i >> 2) + (i & 3))) & 1u)) sc[kb][i] = -INFINITY;
         }
+      }
     }
     float mx = max_f(sc[0][0], sc[0][1]);
 #pragma unroll

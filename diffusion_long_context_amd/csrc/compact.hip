@@ -3,8 +3,10 @@
 // cache).  For chunk c, held in slot s = chunk_slot[c]:
 //   dst[s][0] = src[s][0]                       (the BOS anchor)
 //   dst[s][1 + i] = src[s][keep_rows[c][i]]     (i < b, ascending rows)
-// for every KV head, in K and in V.  The decode over the compacted pool then
-// reads each selected chunk's b + 1 rows from consecutive slot rows.
+// for every KV head, in K and in V.  An absent entry (-1: a partial chunk
+// with fewer than b content rows) writes nothing.  The decode over the
+// compacted pool then reads each selected chunk's b + 1 rows from
+// consecutive slot rows.
 //
 // Design for CDNA4: a pure copy, so the bound is HBM bandwidth.  The work of
 // one (chunk, tensor) is a flat run of 16-byte vectors ordered (row, head,
@@ -53,12 +55,12 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactA
   for (int u = 0; u < kCompactVec; ++u) {
     const int h = rem[u] / a.nvec;
     const int vv = rem[u] - h * a.nvec;
-    const int64_t sr = r[u] ? row[u] : 0;
+    const int64_t sr = r[u] ? max(row[u], 0) : 0;    // an absent row reads the BOS row
     w[u] = *(gvec)(src + slot * a.ss + sr * a.sr + (int64_t)h * a.sh + 16 * (int64_t)vv);
   }
 #pragma unroll
   for (int u = 0; u < kCompactVec; ++u) {
-    if (f0 + u * kCompactThreads >= total) continue;
+    if (f0 + u * kCompactThreads >= total || (r[u] > 0 && row[u] < 0)) continue;
     const int h = rem[u] / a.nvec;
     const int vv = rem[u] - h * a.nvec;
     *reinterpret_cast<u32x4*>(dst + slot * a.ds + (int64_t)r[u] * a.dr + (int64_t)h * a.dh + 16 * (int64_t)vv) =

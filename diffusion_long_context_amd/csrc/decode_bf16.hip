@@ -47,6 +47,8 @@ struct Smem {
   uint16_t v[2][kTile * VP];
   gptr16 kptr[kTableTiles * kTile];        // K / V address of each attended row
   gptr16 vptr[kTableTiles * kTile];
+  uint64_t absent[kTableTiles];            // per table tile: bit r = row r is an absent kept row
+  uint64_t kmask[2];                       // the absent mask of the tile in each K buffer
 };
 
 // Element offset of attended row v of sequence s for kv head g.  Pool rows
@@ -54,16 +56,25 @@ struct Smem {
 // (relative to k_resp/v_resp).  Chunk k of the sequence contributes rows
 // [k (b+1), (k+1)(b+1)): its BOS row 0, then its kept rows -- looked up in
 // keep_rows, or rows 1..b of the slot when the pool holds compacted slots.
+// A kept-row entry of -1 (a partial chunk with fewer than b content rows)
+// is an absent row: `absent` is set and the offset is the chunk's BOS row
+// (finite data; its score is masked).
 template <int D>
 __device__ __forceinline__ int64_t resolve_row(const DecodeArgs& a, int s, int g, int k_s,
-                                               int v) {
+                                               int v, bool& absent) {
   const int per = a.b + 1;
+  absent = false;
   if (v < k_s * per) {
     const int k = v / per;
     const int r = v - k * per;
     const int cg = s * a.n_chunks_per_seq + a.sel_chunk[(int64_t)s * a.k_max + k];
     const int slot = a.chunk_slot[cg];
-    const int row = r == 0 ? 0 : a.compact ? r : a.keep_rows[(int64_t)cg * a.b + r - 1];
+    int row = 0;
+    if (r) {
+      const int kr = a.keep_rows != nullptr ? a.keep_rows[(int64_t)cg * a.b + r - 1] : r;
+      absent = kr < 0;
+      row = absent ? 0 : a.compact ? r : kr;
+    }
     return (int64_t)slot * a.ps_slot + (int64_t)row * a.ps_row + (int64_t)g * a.ps_head;
   }
   const int j = v - k_s * per;
@@ -113,17 +124,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const uint16_t* rv = static_cast<const uint16_t*>(a.v_resp);
 
   // ---- row-pointer table for tiles [tw, tw + kTableTiles); rows past n_kv
-  // point at the sequence's first response row (finite data, masked scores)
+  // point at the sequence's last row (finite data, masked scores).  Thread
+  // tid fills row tid, so wavefront w fills table tile w and its ballot is
+  // that tile's absent mask.
   auto build_table = [&](int tw) {
     const int nrow = (min(tw + kTableTiles, t_end) - tw) * kTile;
-    for (int idx = tid; idx < nrow; idx += kThreads) {
-      const int v = tw * kTile + idx;
-      const int64_t off = resolve_row<D>(a, s, g, k_s, min(v, n_kv - 1));
+    bool absent = false;
+    if (tid < nrow) {
+      const int v = tw * kTile + tid;
+      const int64_t off = resolve_row<D>(a, s, g, k_s, min(v, n_kv - 1), absent);
+      absent = absent && v < n_kv;
       const bool pool = off >= 0;
       const int64_t e = pool ? off : -1 - off;
-      sm.kptr[idx] = (gptr16)((pool ? pk : rk) + e);
-      sm.vptr[idx] = (gptr16)((pool ? pv : rv) + e);
+      sm.kptr[tid] = (gptr16)((pool ? pk : rk) + e);
+      sm.vptr[tid] = (gptr16)((pool ? pv : rv) + e);
     }
+    const uint64_t m = __ballot(absent);
+    if (lane == 0) sm.absent[wave] = m;
   };
   int tw = t_begin;
 
@@ -147,9 +164,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : a.chunk_slot);
     const int cg = s * a.n_chunks_per_seq + min(max(c0, 0), a.n_chunks_per_seq - 1);
     const int slot = *(gptr32)(a.chunk_slot + cg);
-    const int krow_ld = *(gptr32)(a.b > 0 && !a.compact ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0)
-                                                       : a.chunk_slot);
-    const int krow = a.compact ? r : krow_ld;   // compacted slots: kept row i sits at row 1 + i
+    const int krow_ld = *(gptr32)(a.b > 0 && a.keep_rows != nullptr ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0)
+                                                                   : a.chunk_slot);
+    // compacted slots: kept row i sits at row 1 + i; keep_rows, when given,
+    // only marks absent rows (-1), which point at the BOS row
+    const bool absent = r > 0 && a.keep_rows != nullptr && krow_ld < 0;
+    const int krow = absent ? 0 : a.compact ? r : krow_ld;
     __builtin_amdgcn_sched_barrier(0);     // the index loads go out before the queries
     // queries: B-operand fragments of S^T (lane: query column lc, d = 16 dc
     // + 8 lj ..); rows past the end read the last row (never stored)
@@ -165,6 +185,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
                            : (((int64_t)s * a.l_d + (v - k_s * per)) * a.h_kv + g) * D;
     sm.kptr[tid] = (gptr16)((pool ? pk : rk) + e);
     sm.vptr[tid] = (gptr16)((pool ? pv : rv) + e);
+    const uint64_t m = __ballot(pool && absent && tid < nrow);
+    if (lane == 0) sm.absent[wave] = m;
   }
 
   // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values of
@@ -179,14 +201,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const int n_loc = t_end - t_begin;
   u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
   gptr16 kp_next[RPT], vp_next[RPT];       // row pointers of the next unit to load
+  // A K tile's absent mask travels with its rows: read from the table with
+  // the pointers, held with the staged registers, written beside the tile
+  // into LDS, read back with the tile's S^T (wave-uniform values)
+  uint64_t km_next = 0, km_set[STAGES];
   auto fetch_ptrs = [&](int uk, int uv) {  // local tiles of the K and V rows
-    const int ik = (t_begin + min(uk, n_loc - 1) - tw) * kTile + ld_r0;
+    const int tk = t_begin + min(uk, n_loc - 1) - tw;
+    const int ik = tk * kTile + ld_r0;
     const int iv = (t_begin + min(max(uv, 0), n_loc - 1) - tw) * kTile + ld_r0;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       kp_next[i] = sm.kptr[ik + i];
       vp_next[i] = sm.vptr[iv + i];
     }
+    km_next = uniform_u64(sm.absent[tk]);
   };
   auto load_unit = [&](int set) {
 #pragma unroll
@@ -194,11 +222,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       kreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(kp_next[i] + ld_d0);
       vreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(vp_next[i] + ld_d0);
     }
+    km_set[set] = km_next;
   };
   auto store_k = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[set][i];
+    if (tid == 0) sm.kmask[buf] = km_set[set];
   };
   auto store_v = [&](int buf, int set) {
 #pragma unroll
@@ -242,6 +272,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   __syncthreads();
   f32x16 sc_a[NK], sc_b[NK];
   at.template qk<NK>(sc_a, k_base, qf);
+  uint64_t am_a = uniform_u64(sm.kmask[0]), am_b = 0;   // absent masks of the tiles in sc_a / sc_b
   __syncthreads();                         // K buffer 0 is rewritten in iteration 0
 
   // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
@@ -252,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   // Every iteration issues exactly one unit's loads, so the wait before a
   // store covers only loads issued STAGES iterations earlier.  One barrier
   // per tile.
-  auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK]) {
+  auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], uint64_t am_cur, uint64_t& am_nxt) {
     const int set = u % STAGES;
     if (u + 2 < n_loc) store_k(u & 1, set);
     if (u + 1 < n_loc) store_v((u + 1) & 1, set);
@@ -269,11 +300,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     }
     const int t = t_begin + u;
     bf16x8 pf[2 * NK];
-    at.template prep<NK>(cur, sl2, n_kv - t * kTile, lj);
-    if (u + 1 < n_loc)
+    at.template prep<NK>(cur, sl2, n_kv - t * kTile, lj, 0, am_cur);
+    if (u + 1 < n_loc) {
+      am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
       at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
-    else
+    } else {
       at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
+    }
     at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
     __syncthreads();
   };
@@ -282,17 +315,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     // only after the second half's loads (exact wait counts before stores)
     int u = 0;
     for (; u + 1 < n_loc; u += 2) {
-      iter(u, sc_a, sc_b);
-      iter(u + 1, sc_b, sc_a);
+      iter(u, sc_a, sc_b, am_a, am_b);
+      iter(u + 1, sc_b, sc_a, am_b, am_a);
     }
-    if (u < n_loc) iter(u, sc_a, sc_b);
+    if (u < n_loc) iter(u, sc_a, sc_b, am_a, am_b);
   }
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
   const float l = at.row_sum();
   if (qrow < rows_total) {
     const int i = qrow / G, h = g * G + (qrow - i * G);
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;   // a split of absent rows only: o = 0, lse = -inf
     const float lse_v = at.lse(l);
     if (n_splits == 1) {
       store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj,

@@ -16,6 +16,8 @@ namespace {
 constexpr int kTile = kDecodeTile;
 constexpr int64_t kMaskedRow = INT64_MIN;
 
+// Element offset of attended row v (pool rows >= 0, response rows -1 - offset);
+// an absent kept row (entry -1 of a partial chunk) is kMaskedRow.
 template <int D>
 __device__ __forceinline__ int64_t resolve_row_f32(const DecodeArgs& a, int s, int g, int k_s,
                                                    int v) {
@@ -25,7 +27,12 @@ __device__ __forceinline__ int64_t resolve_row_f32(const DecodeArgs& a, int s, i
     const int r = v - k * per;
     const int cg = s * a.n_chunks_per_seq + a.sel_chunk[(int64_t)s * a.k_max + k];
     const int slot = a.chunk_slot[cg];
-    const int row = r == 0 ? 0 : a.compact ? r : a.keep_rows[(int64_t)cg * a.b + r - 1];
+    int row = 0;
+    if (r) {
+      const int kr = a.keep_rows != nullptr ? a.keep_rows[(int64_t)cg * a.b + r - 1] : r;
+      if (kr < 0) return kMaskedRow;
+      row = a.compact ? r : kr;
+    }
     return (int64_t)slot * a.ps_slot + (int64_t)row * a.ps_row + (int64_t)g * a.ps_head;
   }
   const int j = v - k_s * per;
@@ -103,10 +110,11 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeArgs a) {
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < D; ++e) dot = fmaf(q[e], ks[r0 + rr][e], dot);
-        z[rr] = r0 + rr < nvalid ? dot * sl2 : -INFINITY;
+        z[rr] = r0 + rr < nvalid && rowoff[r0 + rr] != kMaskedRow ? dot * sl2 : -INFINITY;
         mx = fmaxf(mx, z[rr]);
       }
       const float m_new = fmaxf(m_run, mx);
+      if (m_new == -INFINITY) continue;    // only masked rows so far
       const float alpha = exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeArgs a) {
   }
 
   if (!valid) return;
-  const float inv = 1.f / l_run;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;   // a split of absent rows only: o = 0, lse = -inf
   const float lse_v = m_run * kLn2 + logf(l_run);
   if (n_splits == 1) {
     float* op = static_cast<float*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D;

@@ -73,6 +73,13 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_row<0x140>(v);
 }
 
+// A wave-uniform 64-bit value (e.g. read from LDS) moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id % 8).  Remap
 // them so that each XCD receives one contiguous range of logical work items;
 // neighbouring items share K/V tiles, which then stay in that XCD's L2.

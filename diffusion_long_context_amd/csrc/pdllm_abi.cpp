@@ -182,7 +182,8 @@ size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_q, int32_t h_kv
 }
 
 pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* chunk_slot,
-                                       int32_t n_chunks, const void* q_chunk, int32_t h_q,
+                                       const int32_t* chunk_rows, int32_t n_chunks,
+                                       const void* q_chunk, int32_t h_q,
                                        const void* q_win, int32_t w, int32_t chunks_per_win,
                                        float scale, void* o_chunk, float* key_score,
                                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -215,6 +216,7 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
   a.ps_row = pool->stride_row;
   a.ps_head = pool->stride_head;
   a.chunk_slot = chunk_slot;
+  a.chunk_rows = chunk_rows;
   a.q_chunk = q_chunk;
   a.q_win = q_win;
   a.o_chunk = o_chunk;
@@ -243,8 +245,8 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
   return ok();
 }
 
-pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t slot_rows,
-                               int32_t b, int32_t* keep_rows, void* stream) {
+pdllm_status pdllm_select_topB(const float* key_score, const int32_t* chunk_rows, int32_t n_chunks,
+                               int32_t slot_rows, int32_t b, int32_t* keep_rows, void* stream) {
   if (n_chunks < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 0");
   if (slot_rows < 1) return fail(PDLLM_ERR_INVALID_ARG, "slot_rows must be >= 1");
   if (slot_rows > 4097) return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > 4097 is not supported", slot_rows);
@@ -253,8 +255,8 @@ pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t
   if (n_chunks == 0 || b == 0) return ok();
   if (key_score == nullptr || keep_rows == nullptr)
     return fail(PDLLM_ERR_INVALID_ARG, "key_score / keep_rows is NULL");
-  pdllm_status st = hip_status(pdllm::launch_select_topb(key_score, n_chunks, slot_rows, b, keep_rows, stream),
-                               "top-B launch");
+  pdllm_status st = hip_status(
+      pdllm::launch_select_topb(key_score, chunk_rows, n_chunks, slot_rows, b, keep_rows, stream), "top-B launch");
   return st != PDLLM_OK ? st : ok();
 }
 

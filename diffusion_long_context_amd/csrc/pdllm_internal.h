@@ -85,6 +85,7 @@ struct PrefillArgs {
   const void* pool_v;
   int64_t ps_slot, ps_row, ps_head;
   const int32_t* chunk_slot;
+  const int32_t* chunk_rows; // nullable [n_chunks]: rows held by each chunk (default slot_rows)
   const void* q_chunk;
   const void* q_win;
   void* o_chunk;
@@ -107,8 +108,8 @@ constexpr int kPrefillMaxRows = 288;     // bf16 rows the resident kernel holds 
 int launch_score_finalize(const PrefillArgs& a, void* stream);
 
 // ---------------------------------------------------------------- select
-int launch_select_topb(const float* key_score, int n_chunks, int slot_rows, int b,
-                       int32_t* keep_rows, void* stream);
+int launch_select_topb(const float* key_score, const int32_t* chunk_rows, int n_chunks, int slot_rows,
+                       int b, int32_t* keep_rows, void* stream);
 constexpr int kMaxTopkSeqPerLaunch = 64;
 struct TopkArgs {
   const float* chunk_score;

@@ -57,7 +57,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 
   const int c = blockIdx.x / a.h_kv;
   const int g = blockIdx.x - c * a.h_kv;
-  const int R = a.slot_rows;
+  const int R = a.slot_rows;               // the layout's rows per chunk
+  // rows this chunk holds (a partial last chunk holds fewer): keys and
+  // query rows past Rc take no part
+  const int Rc = a.chunk_rows != nullptr ? min(max(a.chunk_rows[c], 1), R) : R;
   constexpr int rpad = 16 * NKB;
   const int slot = a.chunk_slot[c];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   bf16x8 qw_cur[2][DC];
   if (n_wb > 0) fetch_w(min(wave, n_wb - 1), qw_cur);
 
-  // ---- stage the chunk's K and V (rows >= R are zero); every load is issued
+  // ---- stage the chunk's K and V (rows >= Rc are zero); every load is issued
   // before the first LDS store so the staging costs one memory round trip
   {
     const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k);
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r_first + ps * kRowsPerPass + i;
-        if (r < R) {
+        if (r < Rc) {
           const int64_t off = base + (int64_t)r * a.ps_row + d0;
           kr[ps][i] = *reinterpret_cast<const u32x4*>(pk + off);
           vr[ps][i] = *reinterpret_cast<const u32x4*>(pv + off);
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   }
   __syncthreads();
 
-  const int n_rows_c = R * G;
+  const int n_rows_c = Rc * G;
   const int n_cb = (n_rows_c + 31) / 32;
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_chunk) + (int64_t)c * R * a.h_q * D;
   uint16_t* oc = static_cast<uint16_t*>(a.o_chunk) + (int64_t)c * R * a.h_q * D;
@@ -147,16 +150,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     __builtin_amdgcn_sched_barrier(0);     // keep items apart: no cross-item hoisting
     Attn at;
     at.init();
-    // 64-row steps over rows [0, 64 (NKB / 4)), the last one masked at R;
-    // when NKB % 4 == 2 the remaining 32 rows (R = C + 1 puts a single row
-    // there for C a multiple of 64) run as one 32-row step
+    // 64-row steps over rows [0, 64 (NKB / 4)), masked at Rc; when
+    // NKB % 4 == 2 the remaining 32 rows (R = C + 1 puts a single row there
+    // for C a multiple of 64) run as one 32-row step.  A step wholly past Rc
+    // (a partial chunk) is masked throughout.
     constexpr int n_full = NKB / 4;
 #pragma unroll 1
     for (int st = 0; st < n_full; ++st)
-      at.template step<2>(k_lane + st * 64 * KP, v_lane + st * 64 * VP, qf, sl2, R - st * 64, lh);
+      at.template step<2>(k_lane + st * 64 * KP, v_lane + st * 64 * VP, qf, sl2, max(Rc - st * 64, 0), lh);
     if constexpr (NKB % 4 == 2) {
       constexpr int kv0 = 64 * n_full;
-      at.template step<1>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, R - kv0, lh);
+      at.template step<1>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, max(Rc - kv0, 0), lh);
     }
     const float l = at.row_sum();
     const int x = row_of(item);
@@ -204,10 +208,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // keys past R: only the last two blocks can hold any
+      // keys past Rc (only in the last two blocks unless the chunk is partial;
+      // the first test is workgroup-uniform)
 #pragma unroll
-      for (int kb = NKB - 2; kb < NKB; ++kb)
-        if (16 * kb + lr >= R) sw[kb] = ninf;
+      for (int kb = 0; kb < NKB; ++kb)
+        if (16 * kb + 15 >= Rc && 16 * kb + lr >= Rc) sw[kb] = ninf;
       float mx[4], sum[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

@@ -30,7 +30,9 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
   __shared__ float colsum[4097];
   const int c = blockIdx.x / a.h_kv;
   const int g = blockIdx.x - c * a.h_kv;
-  const int R = a.slot_rows, G = a.group;
+  const int R = a.slot_rows, G = a.group;  // R: the layout's rows per chunk
+  // rows this chunk holds (a partial last chunk holds fewer)
+  const int Rc = a.chunk_rows != nullptr ? min(max(a.chunk_rows[c], 1), R) : R;
   const int slot = a.chunk_slot[c];
   const float* kb = static_cast<const float*>(a.pool_k) + (int64_t)slot * a.ps_slot + (int64_t)g * a.ps_head;
   const float* vb = static_cast<const float*>(a.pool_v) + (int64_t)slot * a.ps_slot + (int64_t)g * a.ps_head;
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
   // chunk rows
   const float* qc = static_cast<const float*>(a.q_chunk) + (int64_t)c * R * a.h_q * D;
   float* oc = static_cast<float*>(a.o_chunk) + (int64_t)c * R * a.h_q * D;
-  for (int x = tid; x < R * G; x += kThreads) {
+  for (int x = tid; x < Rc * G; x += kThreads) {
     const int r = x / G, h = g * G + (x - r * G);
     float q[D], acc[D];
 #pragma unroll
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
       acc[e] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    for (int j = 0; j < R; ++j) {
+    for (int j = 0; j < Rc; ++j) {
       const float z = dot_row<D>(q, kb + (int64_t)j * a.ps_row) * sl2;
       const float m_new = fmaxf(m, z);
       const float alpha = exp2f(m - m_new);
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
       const int w = x / G, h = g * G + (x - w * G);
       const float* q = qw + ((int64_t)w * a.h_q + h) * D;
       float m = -INFINITY, l = 0.f;
-      for (int j = 0; j < R; ++j) {
+      for (int j = 0; j < Rc; ++j) {
         const float z = dot_row<D>(q, kb + (int64_t)j * a.ps_row) * sl2;
         const float m_new = fmaxf(m, z);
         l = l * exp2f(m - m_new) + exp2f(z - m_new);
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
     }
     __syncthreads();
     const int n_here = min(kThreads, n_win - x0);
-    for (int j = tid; j < R; j += kThreads) {
+    for (int j = tid; j < Rc; j += kThreads) {     // keys past Rc keep their 0
       const float* k = kb + (int64_t)j * a.ps_row;
       float s = colsum[j];
       for (int t = 0; t < n_here; ++t) {

@@ -61,8 +61,11 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
   const int qt = wg % n_qt;
   const int cg = wg / n_qt;
   const int g = cg % a.h_kv, c = cg / a.h_kv;
-  const int R = a.slot_rows, G = a.group;
-  const int n_rows = (WIN ? a.w : R) * G;
+  const int R = a.slot_rows, G = a.group;  // R: the layout's rows per chunk
+  // rows this chunk holds (a partial last chunk holds fewer); past Rc no key
+  // or query row takes part
+  const int Rc = a.chunk_rows != nullptr ? min(max(a.chunk_rows[c], 1), R) : R;
+  const int n_rows = (WIN ? a.w : Rc) * G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 31, lj = lane >> 5;
   const int64_t base = (int64_t)a.chunk_slot[c] * a.ps_slot + (int64_t)g * a.ps_head;
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
   // a tile.  Load unit u carries K of tile u and V of tile u-1 (tile numbers
   // clamped to the slot, rows clamped to its last row, so every load reads
   // valid data); the window pass has no V.
-  const int n_tiles = (R + kTile - 1) / kTile;
+  const int n_tiles = (Rc + kTile - 1) / kTile;
   const int ld_d0 = 8 * (tid % TPR);
   const int ld_r0 = RPT * (tid / TPR);
   u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
@@ -93,11 +96,11 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
     const int tk = min(u, n_tiles - 1), tv = min(max(u - 1, 0), n_tiles - 1);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int rk = min(tk * kTile + ld_r0 + i, R - 1);
+      const int rk = min(tk * kTile + ld_r0 + i, Rc - 1);
       kreg[set][i] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
           (gptr16)(pk + (int64_t)rk * a.ps_row + ld_d0));
       if constexpr (!WIN) {
-        const int rv = min(tv * kTile + ld_r0 + i, R - 1);
+        const int rv = min(tv * kTile + ld_r0 + i, Rc - 1);
         vreg[set][i] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
             (gptr16)(pv + (int64_t)rv * a.ps_row + ld_d0));
       }
@@ -150,13 +153,13 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
     if (u + 1 < n_tiles) store_v((u + 1) & 1, set);
     load_unit(set, u + 4);
     bf16x8 pf[2 * NK];
-    at.template prep<NK>(cur, sl2, R - u * kTile, lj);
+    at.template prep<NK>(cur, sl2, Rc - u * kTile, lj);
     if (u + 1 < n_tiles)
       at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
     else
       at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
     if constexpr (!WIN)
-      at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (R - u * kTile + 15) >> 4));
+      at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (Rc - u * kTile + 15) >> 4));
     __syncthreads();
   };
   {
@@ -202,14 +205,15 @@ __global__ __launch_bounds__(64 * kColWaves) void window_colsum_kernel(const Pre
   const int cg = blockIdx.x / n_kt;
   const int g = cg % a.h_kv, c = cg / a.h_kv;
   const int R = a.slot_rows, G = a.group;
+  const int Rc = a.chunk_rows != nullptr ? min(max(a.chunk_rows[c], 1), R) : R;
   const int n_rows = a.w * G;
   const int n_qb = (n_rows + 31) / 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 31, lj = lane >> 5;
   const int j0 = kt * kColKeys;
 
-  // ---- stage the key tile; rows past the slot clamp to its last row (their
-  // sums are never written).  All loads go out before the first store.
+  // ---- stage the key tile; rows past the chunk clamp to its last row
+  // (their sums are written as 0).  All loads go out before the first store.
   {
     const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k) + (int64_t)a.chunk_slot[c] * a.ps_slot +
                          (int64_t)g * a.ps_head;
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(64 * kColWaves) void window_colsum_kernel(const Pre
     for (int i = 0; i < kLoads; ++i) {
       const int e = tid + i * 64 * kColWaves;
       const int rr = e / TPR, d0 = 8 * (e - rr * TPR);
-      kr[i] = *reinterpret_cast<const u32x4*>(pk + (int64_t)min(j0 + rr, R - 1) * a.ps_row + d0);
+      kr[i] = *reinterpret_cast<const u32x4*>(pk + (int64_t)min(j0 + rr, Rc - 1) * a.ps_row + d0);
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -269,11 +273,11 @@ __global__ __launch_bounds__(64 * kColWaves) void window_colsum_kernel(const Pre
     if (lj == 0) red[wave][32 * kb + lc] = v;
   }
   __syncthreads();
-  if (tid < kColKeys && j0 + tid < R) {
+  if (tid < kColKeys && j0 + tid < R) {    // keys past Rc (a partial chunk) score 0
     float s = red[0][tid];
 #pragma unroll
     for (int wv = 1; wv < kColWaves; ++wv) s += red[wv][tid];
-    a.part_score[((int64_t)c * a.h_kv + g) * R + j0 + tid] = s;
+    a.part_score[((int64_t)c * a.h_kv + g) * R + j0 + tid] = j0 + tid < Rc ? s : 0.f;
   }
 }
 

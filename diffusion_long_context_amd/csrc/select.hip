@@ -59,17 +59,23 @@ __device__ void select_sorted(const uint64_t* keys, int n, int count, int index_
   }
 }
 
-// One workgroup per chunk.  Candidates are the content rows 1..slot_rows-1.
-__global__ __launch_bounds__(kThreads) void topb_kernel(const float* key_score, int slot_rows,
-                                                        int b, int32_t* keep_rows) {
+// One workgroup per chunk.  Candidates are the content rows 1..R_c-1, R_c =
+// chunk_rows[c] (slot_rows when absent).  A chunk with fewer than b of them
+// keeps them all and fills the rest of its row with -1.
+__global__ __launch_bounds__(kThreads) void topb_kernel(const float* key_score, const int32_t* chunk_rows,
+                                                        int slot_rows, int b, int32_t* keep_rows) {
   __shared__ uint64_t keys[4096];
   __shared__ int wave_counts[kThreads / 64];
   const int c = blockIdx.x;
-  const int n = slot_rows - 1;
+  const int rc = chunk_rows != nullptr ? min(max(chunk_rows[c], 1), slot_rows) : slot_rows;
+  const int n = rc - 1;
+  const int count = min(b, n);
   const float* row = key_score + (int64_t)c * slot_rows + 1;
+  int32_t* out = keep_rows + (int64_t)c * b;
+  for (int i = count + threadIdx.x; i < b; i += kThreads) out[i] = -1;
   for (int i = threadIdx.x; i < n; i += kThreads) keys[i] = rank_key(row[i], (uint32_t)i);
   __syncthreads();
-  select_sorted(keys, n, b, 1, keep_rows + (int64_t)c * b, wave_counts);
+  select_sorted(keys, n, count, 1, out, wave_counts);
 }
 
 // One workgroup per sequence; the K_s of this launch's sequences travel in
@@ -90,11 +96,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkArgs a) {
 
 }  // namespace
 
-int launch_select_topb(const float* key_score, int n_chunks, int slot_rows, int b,
-                       int32_t* keep_rows, void* stream) {
+int launch_select_topb(const float* key_score, const int32_t* chunk_rows, int n_chunks, int slot_rows,
+                       int b, int32_t* keep_rows, void* stream) {
   if (n_chunks == 0 || b == 0) return (int)hipSuccess;
   hipLaunchKernelGGL(topb_kernel, dim3(n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
-                     key_score, slot_rows, b, keep_rows);
+                     key_score, chunk_rows, slot_rows, b, keep_rows);
   return (int)hipGetLastError();
 }
 

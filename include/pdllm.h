@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 4
+#define PDLLM_ABI_VERSION 5
 
 typedef enum {
   PDLLM_OK = 0,
@@ -85,15 +85,18 @@ typedef struct {
  *                      (its first k_per_seq[s] entries are used), as written
  *                      by pdllm_select_topK
  *   keep_rows   device [n_seq * n_chunks_per_seq][b]   kept content rows
- *                      (1..C) of every chunk, as written by pdllm_select_topB
+ *                      (1..C) of every chunk, as written by pdllm_select_topB;
+ *                      an entry of -1 is an absent row (a partial last chunk
+ *                      with fewer than b content rows) and is not attended
  *   k_per_seq   host   [n_seq]   K_s, 0 <= K_s <= k_max
  *   rows_compacted  0: the pool holds whole chunks and keep_rows names the
  *                      kept rows;  1: the pool holds compacted slots (the
  *                      layout pdllm_compact_kept_rows writes), whose kept
- *                      rows are rows 1..b in order -- keep_rows is not read
- *                      and may be NULL
- * A selected chunk contributes its BOS row and its b kept rows, in that
- * order; chunks are visited in sel_chunk order.
+ *                      rows are rows 1..b in order -- keep_rows is then read
+ *                      only for its absent (-1) entries, and may be NULL when
+ *                      there are none
+ * A selected chunk contributes its BOS row and its b kept rows (less the
+ * absent ones), in that order; chunks are visited in sel_chunk order.
  */
 typedef struct {
   const int32_t* chunk_slot;
@@ -133,6 +136,12 @@ size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_q, int32_t h_kv
  *              key_score[c,j] = sum_h sum_w softmax_j(scale <q_win[.,w,h], K[s,j,g]>)
  *              (the window rows' softmax runs over the chunk's own rows only)
  *   chunk_slot device [n_chunks]
+ *   chunk_rows device [n_chunks], nullable: rows R_c (1..slot_rows, BOS
+ *              included) that chunk c holds at the start of its slot; NULL =
+ *              slot_rows for every chunk.  A prefix whose length is not a
+ *              multiple of C ends in a partial chunk of fewer rows: its keys
+ *              j >= R_c take no part (key_score[c,j] = 0) and its output rows
+ *              r >= R_c are not written.
  *   workspace  device, >= pdllm_prefill_score_workspace(n_chunks, h_q, h_kv, slot_rows, w),
  *              16-byte aligned
  * Supported: slot_rows <= 4097 (chunk sizes up to 4096 plus BOS); f32 with d
@@ -144,7 +153,8 @@ size_t pdllm_prefill_score_workspace(int32_t n_chunks, int32_t h_q, int32_t h_kv
  * reproducible run to run.
  */
 pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* chunk_slot,
-                                       int32_t n_chunks, const void* q_chunk, int32_t h_q,
+                                       const int32_t* chunk_rows, int32_t n_chunks,
+                                       const void* q_chunk, int32_t h_q,
                                        const void* q_win, int32_t w, int32_t chunks_per_win,
                                        float scale, void* o_chunk, float* key_score,
                                        void* workspace, size_t workspace_bytes, void* stream);
@@ -152,15 +162,19 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
 /*
  * Top-B rows per chunk (Methodology 2, intra-chunk sparsity).
  *   key_score  device [n_chunks][slot_rows] float
+ *   chunk_rows device [n_chunks], nullable: rows R_c each chunk holds (see
+ *              pdllm_chunk_prefill_score); NULL = slot_rows
  *   keep_rows  device [n_chunks][b] int32 out: the b best rows among the
- *              content rows 1..slot_rows-1 (row 0, the BOS anchor, is always
- *              kept and is not a candidate), in ascending order.
+ *              content rows 1..R_c-1 (row 0, the BOS anchor, is always kept
+ *              and is not a candidate), in ascending order.  A chunk with
+ *              fewer than b content rows keeps them all and fills the rest of
+ *              its row with -1 (absent).
  * Order: larger score first; equal scores (-0 == +0) go to the lower row;
  * NaN ranks after every number.  0 <= b <= slot_rows - 1, slot_rows <= 4097.
  * Bit-exact: integer comparisons only.
  */
-pdllm_status pdllm_select_topB(const float* key_score, int32_t n_chunks, int32_t slot_rows,
-                               int32_t b, int32_t* keep_rows, void* stream);
+pdllm_status pdllm_select_topB(const float* key_score, const int32_t* chunk_rows, int32_t n_chunks,
+                               int32_t slot_rows, int32_t b, int32_t* keep_rows, void* stream);
 
 /*
  * Top-K chunks per sequence over given chunk scores (Methodology 1,
@@ -184,13 +198,14 @@ pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t 
  * destination: its BOS row first, then its b kept rows in keep_rows order,
  *   dst[s][0] = src[s][0],   dst[s][1 + i] = src[s][keep_rows[c][i]],
  * for every KV head, in K and in V.  The copy is bit-exact; destination rows
- * past b and slots of no listed chunk are not written.  A decode over the
- * destination with rows_compacted = 1 and the same b attends exactly the rows
- * a decode over the source with keep_rows attends, in the same order.
+ * past b, rows of absent (-1) entries and slots of no listed chunk are not
+ * written.  A decode over the destination with rows_compacted = 1 and the
+ * same b (and keep_rows, when it has absent entries) attends exactly the
+ * rows a decode over the source with keep_rows attends, in the same order.
  *   src        the whole-chunk pool
  *   chunk_slot device [n_chunks]
- *   keep_rows  device [n_chunks][b] rows in 1..src->slot_rows-1 (as written by
- *              pdllm_select_topB); may be NULL when b = 0
+ *   keep_rows  device [n_chunks][b] rows in 1..src->slot_rows-1 or -1 (as
+ *              written by pdllm_select_topB); may be NULL when b = 0
  *   dst_k, dst_v  device, the source's dtype, h_kv, d and n_slots, with
  *              dst_slot_rows >= b + 1 rows per slot and element strides
  *              dst_stride_slot, dst_stride_row, dst_stride_head (d contiguous;

@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 4
+    assert L.lib.pdllm_abi_version() == 5
 
 
 def _pool(**kw):
@@ -124,7 +124,7 @@ def test_decode_workspace_query_matches_plan():
 def test_prefill_validation():
     pool = _pool()
     f = L.lib.pdllm_chunk_prefill_score
-    args = lambda **kw: [ctypes.byref(kw.get("pool", pool)), 0x30000, kw.get("n", 128), 0x60000,
+    args = lambda **kw: [ctypes.byref(kw.get("pool", pool)), 0x30000, None, kw.get("n", 128), 0x60000,
                          kw.get("h_q", 28), 0x70000, kw.get("w", 64), kw.get("cpw", 128), 0.088, 0x90000,
                          0xA0000, kw.get("ws", None), kw.get("ws_bytes", 0), None]
     assert f(*args(h_q=30)) == INVALID
@@ -146,10 +146,10 @@ def test_prefill_validation():
 
 def test_select_validation():
     tb = L.lib.pdllm_select_topB
-    assert tb(0x1000, 4, 33, 33, 0x2000, None) == INVALID          # b > slot_rows - 1
-    assert tb(0x1000, 4, 5000, 3, 0x2000, None) == UNSUPPORTED
-    assert tb(0x1000, -1, 33, 3, 0x2000, None) == INVALID
-    assert tb(0x1000, 4, 33, 0, 0x2000, None) == OK                # b = 0: nothing to do
+    assert tb(0x1000, None, 4, 33, 33, 0x2000, None) == INVALID          # b > slot_rows - 1
+    assert tb(0x1000, None, 4, 5000, 3, 0x2000, None) == UNSUPPORTED
+    assert tb(0x1000, None, -1, 33, 3, 0x2000, None) == INVALID
+    assert tb(0x1000, None, 4, 33, 0, 0x2000, None) == OK                # b = 0: nothing to do
     tk = L.lib.pdllm_select_topK
     ks = (ctypes.c_int32 * 2)(3, 9)
     assert tk(0x1000, 2, 8, ks, 8, 0x2000, None) == INVALID        # K_s > k_max
