@@ -65,12 +65,12 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "f5b7fb1869271615",
+    "sources_sha": "b0b25bb9a30a89f6",
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149196.34, "write_kib": 234575.95},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149208.28, "write_kib": 234627.37},
         "score_finalize_kernel": {"fetch_kib": 2551.44, "write_kib": 128.5},
     },
-    "copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.26,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 

@@ -49,6 +49,7 @@ struct Smem {
   gptr16 vptr[kTableTiles * kTile];
   uint64_t absent[kTableTiles];            // per table tile: bit r = row r is an absent kept row
   uint64_t kmask[2];                       // the absent mask of the tile in each K buffer
+  int flag[WAVES];                         // per wavefront: the split holds an absent row
 };
 
 // Element offset of attended row v of sequence s for kv head g.  Pool rows
@@ -161,11 +162,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     const int v = max(0, min(tw * kTile + min(tid, nrow - 1), n_kv - 1));
     const int kk = min(v / per, max(k_s - 1, 0));
     const int r = min(v - kk * per, per - 1);   // BOS row 0, then kept rows 1..b
+    // the chunks this split's rows fall in (one per thread, clamped): any
+    // with an absent row has -1 as its last kept-row entry
+    const bool tbl = a.b > 0 && a.keep_rows != nullptr;
+    const int k_lo = min(t_begin * kTile / per, max(k_s - 1, 0));
+    const int k_hi = min((t_end * kTile - 1) / per, max(k_s - 1, 0));
+    const int kx = min(k_lo + tid, k_hi);
     const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : a.chunk_slot);
+    const int cx = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kx : a.chunk_slot);
     const int cg = s * a.n_chunks_per_seq + min(max(c0, 0), a.n_chunks_per_seq - 1);
+    const int cgx = s * a.n_chunks_per_seq + min(max(cx, 0), a.n_chunks_per_seq - 1);
     const int slot = *(gptr32)(a.chunk_slot + cg);
-    const int krow_ld = *(gptr32)(a.b > 0 && a.keep_rows != nullptr ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0)
-                                                                   : a.chunk_slot);
+    const int krow_ld = *(gptr32)(tbl ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0) : a.chunk_slot);
+    const int klast = *(gptr32)(tbl ? a.keep_rows + (int64_t)cgx * a.b + (a.b - 1) : a.chunk_slot);
     // compacted slots: kept row i sits at row 1 + i; keep_rows, when given,
     // only marks absent rows (-1), which point at the BOS row
     const bool absent = r > 0 && a.keep_rows != nullptr && krow_ld < 0;
@@ -187,54 +196,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     sm.vptr[tid] = (gptr16)((pool ? pv : rv) + e);
     const uint64_t m = __ballot(pool && absent && tid < nrow);
     if (lane == 0) sm.absent[wave] = m;
+    // a split spanning more chunks than threads (a long split of short
+    // chunks) takes the masked path unchecked: its masks are exact either way
+    const bool flag = tbl && k_s > 0 && t_begin * kTile < k_s * per && (klast < 0 || k_hi - k_lo >= kThreads);
+    const uint64_t fw = __ballot(flag);
+    if (lane == 0) sm.flag[wave] = fw != 0;
   }
-
-  // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values of
-  // a tile.  K runs one tile ahead of V: load unit a carries K of tile a and
-  // V of tile a-1 (local tile numbers u = t - t_begin, clamped to the split,
-  // so a unit past its end re-reads valid rows that are never stored).
-  // STAGES staging register sets let a unit's loads be issued STAGES
-  // iterations before its LDS store.
-  constexpr int STAGES = RPT <= 2 ? 2 : 1;
-  const int ld_d0 = 8 * (tid % TPR);
-  const int ld_r0 = RPT * (tid / TPR);
-  const int n_loc = t_end - t_begin;
-  u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
-  gptr16 kp_next[RPT], vp_next[RPT];       // row pointers of the next unit to load
-  // A K tile's absent mask travels with its rows: read from the table with
-  // the pointers, held with the staged registers, written beside the tile
-  // into LDS, read back with the tile's S^T (wave-uniform values)
-  uint64_t km_next = 0, km_set[STAGES];
-  auto fetch_ptrs = [&](int uk, int uv) {  // local tiles of the K and V rows
-    const int tk = t_begin + min(uk, n_loc - 1) - tw;
-    const int ik = tk * kTile + ld_r0;
-    const int iv = (t_begin + min(max(uv, 0), n_loc - 1) - tw) * kTile + ld_r0;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      kp_next[i] = sm.kptr[ik + i];
-      vp_next[i] = sm.vptr[iv + i];
-    }
-    km_next = uniform_u64(sm.absent[tk]);
-  };
-  auto load_unit = [&](int set) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      kreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(kp_next[i] + ld_d0);
-      vreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(vp_next[i] + ld_d0);
-    }
-    km_set[set] = km_next;
-  };
-  auto store_k = [&](int buf, int set) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[set][i];
-    if (tid == 0) sm.kmask[buf] = km_set[set];
-  };
-  auto store_v = [&](int buf, int set) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[set][i];
-  };
 
   Attn at;
   at.init();
@@ -245,81 +212,146 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const uint16_t* k_base = &sm.k[0][0] + k_lane;
   const uint16_t* v_base = &sm.v[0][0] + v_lane;
 
-  // ---- prologue: K and V of tile 0 and K of tile 1 into LDS, units 2 ..
-  // 1 + STAGES in flight, S^T of tile 0 computed
   __syncthreads();                         // row table ready
-  fetch_ptrs(0, 0);
-  load_unit(0);
-  if constexpr (STAGES == 2) {             // tiles 0 and 1 in one memory round trip
-    fetch_ptrs(1, 1);
-    load_unit(1);
-    store_k(0, 0);
-    store_v(0, 0);
-    store_k(1, 1);
-  } else {
-    store_k(0, 0);
-    store_v(0, 0);
-    fetch_ptrs(1, 1);
-    load_unit(0);
-    store_k(1, 0);
-  }
+  bool has_absent = false;
 #pragma unroll
-  for (int i = 0; i < STAGES; ++i) {
-    fetch_ptrs(2 + i, 1 + i);
-    load_unit((2 + i) % STAGES);
-  }
-  fetch_ptrs(2 + STAGES, 1 + STAGES);
-  __syncthreads();
-  f32x16 sc_a[NK], sc_b[NK];
-  at.template qk<NK>(sc_a, k_base, qf);
-  uint64_t am_a = uniform_u64(sm.kmask[0]), am_b = 0;   // absent masks of the tiles in sc_a / sc_b
-  __syncthreads();                         // K buffer 0 is rewritten in iteration 0
+  for (int w = 0; w < WAVES; ++w) has_absent = has_absent || sm.flag[w];
+  has_absent = __builtin_amdgcn_readfirstlane((int)has_absent) != 0;
 
-  // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
-  // u & 1, whose tile u was last read in iteration u-1; V of tile u+1 into V
-  // buffer (u+1) & 1, last read by tile u-1), issues the loads of unit
-  // u+2+STAGES into the staging set just freed, then runs the softmax of
-  // tile u with the S^T MFMAs of tile u+1 interleaved, and the PV of tile u.
-  // Every iteration issues exactly one unit's loads, so the wait before a
-  // store covers only loads issued STAGES iterations earlier.  One barrier
-  // per tile.
-  auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], uint64_t am_cur, uint64_t& am_nxt) {
-    const int set = u % STAGES;
-    if (u + 2 < n_loc) store_k(u & 1, set);
-    if (u + 1 < n_loc) store_v((u + 1) & 1, set);
-    load_unit(set);
-    const int un = u + 3 + STAGES;         // the unit the next iteration loads
-    if (un <= n_loc) {                     // beyond, the clamped pointers stay valid
-      if (t_begin + min(un, n_loc - 1) - tw >= kTableTiles) {   // refill the row table (rare)
-        __syncthreads();                   // every wave has read the old table
-        tw = t_begin + min(un, n_loc - 1) - 1;
-        build_table(tw);
-        __syncthreads();
+  // The tile loader, prologue and main loop, in two instances: ABS for a
+  // split that holds an absent kept row, and the plain one.
+  auto run = [&](auto abs_flag) {
+    constexpr bool ABS = decltype(abs_flag)::value;
+    // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values
+    // of a tile.  K runs one tile ahead of V: load unit a carries K of tile a
+    // and V of tile a-1 (local tile numbers u = t - t_begin, clamped to the
+    // split, so a unit past its end re-reads valid rows that are never
+    // stored).  STAGES staging register sets let a unit's loads be issued
+    // STAGES iterations before its LDS store.
+    constexpr int STAGES = RPT <= 2 ? 2 : 1;
+    const int ld_d0 = 8 * (tid % TPR);
+    const int ld_r0 = RPT * (tid / TPR);
+    const int n_loc = t_end - t_begin;
+    u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
+    gptr16 kp_next[RPT], vp_next[RPT];       // row pointers of the next unit to load
+    // A K tile's absent mask (bit r: row r is an absent kept row) travels with
+    // its rows: read from the table with the pointers, held with the staged
+    // registers, written beside the tile into LDS, read back with the tile's
+    // S^T (wave-uniform values; ABS instance only).
+    uint64_t km_next = 0, km_set[STAGES];
+    auto fetch_ptrs = [&](int uk, int uv) {  // local tiles of the K and V rows
+      const int tk = t_begin + min(uk, n_loc - 1) - tw;
+      const int ik = tk * kTile + ld_r0;
+      const int iv = (t_begin + min(max(uv, 0), n_loc - 1) - tw) * kTile + ld_r0;
+  #pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        kp_next[i] = sm.kptr[ik + i];
+        vp_next[i] = sm.vptr[iv + i];
       }
-      fetch_ptrs(un, un - 1);
-    }
-    const int t = t_begin + u;
-    bf16x8 pf[2 * NK];
-    at.template prep<NK>(cur, sl2, n_kv - t * kTile, lj, 0, am_cur);
-    if (u + 1 < n_loc) {
-      am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
-      at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
+      if constexpr (ABS) km_next = uniform_u64(sm.absent[tk]);
+    };
+    auto load_unit = [&](int set) {
+  #pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        kreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(kp_next[i] + ld_d0);
+        vreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(vp_next[i] + ld_d0);
+      }
+      if constexpr (ABS) km_set[set] = km_next;
+    };
+    auto store_k = [&](int buf, int set) {
+  #pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[set][i];
+      if constexpr (ABS)
+        if (tid == 0) sm.kmask[buf] = km_set[set];
+    };
+    auto store_v = [&](int buf, int set) {
+  #pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[set][i];
+    };
+
+
+    // ---- prologue: K and V of tile 0 and K of tile 1 into LDS, units 2 ..
+    // 1 + STAGES in flight, S^T of tile 0 computed
+    fetch_ptrs(0, 0);
+    load_unit(0);
+    if constexpr (STAGES == 2) {             // tiles 0 and 1 in one memory round trip
+      fetch_ptrs(1, 1);
+      load_unit(1);
+      store_k(0, 0);
+      store_v(0, 0);
+      store_k(1, 1);
     } else {
-      at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
+      store_k(0, 0);
+      store_v(0, 0);
+      fetch_ptrs(1, 1);
+      load_unit(0);
+      store_k(1, 0);
     }
-    at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
+  #pragma unroll
+    for (int i = 0; i < STAGES; ++i) {
+      fetch_ptrs(2 + i, 1 + i);
+      load_unit((2 + i) % STAGES);
+    }
+    fetch_ptrs(2 + STAGES, 1 + STAGES);
     __syncthreads();
-  };
-  {
-    // both halves unconditional inside the loop, so the loop head is reached
-    // only after the second half's loads (exact wait counts before stores)
-    int u = 0;
-    for (; u + 1 < n_loc; u += 2) {
-      iter(u, sc_a, sc_b, am_a, am_b);
-      iter(u + 1, sc_b, sc_a, am_b, am_a);
+    f32x16 sc_a[NK], sc_b[NK];
+    at.template qk<NK>(sc_a, k_base, qf);
+    uint64_t am_a = 0, am_b = 0;             // absent masks of the tiles in sc_a / sc_b
+    if constexpr (ABS) am_a = uniform_u64(sm.kmask[0]);
+    __syncthreads();                         // K buffer 0 is rewritten in iteration 0
+
+    // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
+    // u & 1, whose tile u was last read in iteration u-1; V of tile u+1 into V
+    // buffer (u+1) & 1, last read by tile u-1), issues the loads of unit
+    // u+2+STAGES into the staging set just freed, then runs the softmax of
+    // tile u with the S^T MFMAs of tile u+1 interleaved, and the PV of tile u.
+    // Every iteration issues exactly one unit's loads, so the wait before a
+    // store covers only loads issued STAGES iterations earlier.  One barrier
+    // per tile.
+    auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], uint64_t am_cur, uint64_t& am_nxt) {
+      const int set = u % STAGES;
+      if (u + 2 < n_loc) store_k(u & 1, set);
+      if (u + 1 < n_loc) store_v((u + 1) & 1, set);
+      load_unit(set);
+      const int un = u + 3 + STAGES;         // the unit the next iteration loads
+      if (un <= n_loc) {                     // beyond, the clamped pointers stay valid
+        if (t_begin + min(un, n_loc - 1) - tw >= kTableTiles) {   // refill the row table (rare)
+          __syncthreads();                   // every wave has read the old table
+          tw = t_begin + min(un, n_loc - 1) - 1;
+          build_table(tw);
+          __syncthreads();
+        }
+        fetch_ptrs(un, un - 1);
+      }
+      const int t = t_begin + u;
+      bf16x8 pf[2 * NK];
+      at.template prep<NK>(cur, sl2, n_kv - t * kTile, lj, 0, am_cur);
+      if (u + 1 < n_loc) {
+        if constexpr (ABS) am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
+        at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
+      } else {
+        at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
+      }
+      at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
+      __syncthreads();
+    };
+    {
+      // both halves unconditional inside the loop, so the loop head is reached
+      // only after the second half's loads (exact wait counts before stores)
+      int u = 0;
+      for (; u + 1 < n_loc; u += 2) {
+        iter(u, sc_a, sc_b, am_a, am_b);
+        iter(u + 1, sc_b, sc_a, am_b, am_a);
+      }
+      if (u < n_loc) iter(u, sc_a, sc_b, am_a, am_b);
     }
-    if (u < n_loc) iter(u, sc_a, sc_b, am_a, am_b);
-  }
+  };
+  if (has_absent)
+    run(BoolConst<true>{});
+  else
+    run(BoolConst<false>{});
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
   const float l = at.row_sum();

@@ -73,6 +73,12 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_row<0x140>(v);
 }
 
+// A compile-time flag passed to a generic lambda (instantiates it twice).
+template <bool B>
+struct BoolConst {
+  static constexpr bool value = B;
+};
+
 // A wave-uniform 64-bit value (e.g. read from LDS) moved to scalar registers.
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
