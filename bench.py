@@ -5,12 +5,16 @@ One step is one pass of the whole path over the 32K-prefix workload
 randomly permuted pool; K = 16 chunks, B = 256 rows kept, L_d = 256 decode
 rows; scoring window = the first 64 decode rows):
 
-  1. chunk-local attention over all 128 chunks with fused per-key scoring
-     (pdllm_chunk_prefill_score: prefill kernel + key-score finalize),
-  2. top-B rows per chunk (pdllm_select_topB),
-  3. top-K chunks over the given chunk scores (pdllm_select_topK),
-  4. split-KV decode attention over the selected page table, with the
+  1. chunk-local attention over all 128 chunks with fused per-key scoring,
+     top-B rows per chunk and top-K chunks over the given chunk scores
+     (pdllm_prefill_select: the prefill kernel, then one launch for the
+     key-score finalize and both selections),
+  2. split-KV decode attention over the selected page table, with the
      log-sum-exp merge (pdllm_split_attn_decode).
+
+With --unfused the prefill side runs as three calls instead
+(pdllm_chunk_prefill_score, pdllm_select_topB, pdllm_select_topK), with the
+same outputs bit for bit.
 
 Inputs are seeded synthetic data already resident in HBM.  The JSON line
 reports algorithmic TFLOP/s of the step (QK^T + PV of the chunk attention,
@@ -49,12 +53,14 @@ COPY_BYTES = 1 << 30             # --copy-calibration: bytes read (and written) 
 
 # Sources whose code the prefill stage's kernels are built from.
 PREFILL_SOURCES = ("diffusion_long_context_amd/csrc/prefill_bf16.hip",
+                   "diffusion_long_context_amd/csrc/select.hip",
                    "diffusion_long_context_amd/csrc/attn_tile.h",
                    "diffusion_long_context_amd/csrc/device_common.h",
                    "diffusion_long_context_amd/csrc/pdllm_internal.h")
 
 # Kernels each stage launches (one launch of each per step on this workload).
 STAGE_KERNELS = {
+    "prefill_select": "prefill_bf16_kernel<128, 18> + finalize_select_kernel",
     "prefill": "prefill_bf16_kernel<128, 18> + score_finalize_kernel",
     "select_topb": "topb_kernel",
     "select_topk": "topk_kernel",
@@ -84,6 +90,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of COPY_BYTES (byte-counter scale)")
+    p.add_argument("--unfused", action="store_true",
+                   help="run the prefill side as three calls (prefill + scoring, top-B, top-K)")
     p.add_argument("--decode-only", action="store_true",
                    help="time only the decode call (diagnostic; not the headline step)")
     p.add_argument("--full-step", action="store_true",
@@ -115,6 +123,7 @@ def workload_counts(cfg):
         "select_topk": 0.0,
         "decode": sum(4.0 * cfg.l_d * hq * d * x for x in n_kv),
     }
+    flops["prefill_select"] = flops["prefill"]
     bytes_ = {
         # q_chunk + o_chunk + the chunks' pool K/V + query window + key scores
         "prefill": 2.0 * n * r * hq * d * e + 2.0 * n * r * hk * d * e + cfg.n_seq * w * hq * d * e
@@ -124,6 +133,7 @@ def workload_counts(cfg):
         # q + kept pool K/V rows (BOS included) + response K/V + o
         "decode": sum(2.0 * cfg.l_d * hq * d * e + 2.0 * x * hk * d * e for x in n_kv),
     }
+    bytes_["prefill_select"] = bytes_["prefill"] + bytes_["select_topb"] + bytes_["select_topk"]
     return flops, bytes_
 
 
@@ -135,16 +145,21 @@ def sources_sha(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def prefill_traffic():
-    """HBM bytes of one prefill-stage launch from the recorded counters,
-    scaled by the copy kernel's readings; None if not taken on these sources."""
+def prefill_traffic(fused: bool):
+    """HBM bytes of one prefill-stage launch (the prefill kernel and the
+    finalize of its key scores, fused with the selections or not) from the
+    recorded counters, scaled by the copy kernel's readings; None if not
+    taken on these sources."""
     rec = PREFILL_COUNTERS
     if rec is None or rec["sources_sha"] != sources_sha(PREFILL_SOURCES):
         return None
     f_read = COPY_BYTES / (rec["copy_fetch_kib"] * 1024.0)
     f_write = COPY_BYTES / (rec["copy_write_kib"] * 1024.0)
-    return sum(k["fetch_kib"] * 1024.0 * f_read + k["write_kib"] * 1024.0 * f_write
-               for k in rec["kernels"].values())
+    names = ["prefill_bf16_kernel<128, 18>", "finalize_select_kernel" if fused else "score_finalize_kernel"]
+    if any(n not in rec["kernels"] for n in names):
+        return None
+    return sum(rec["kernels"][n]["fetch_kib"] * 1024.0 * f_read + rec["kernels"][n]["write_kib"] * 1024.0 * f_write
+               for n in names)
 
 
 def copy_calibration():
@@ -583,14 +598,22 @@ def main():
         L.chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, cfg.n_chunks, cfg.scale,
                               o_chunk=o_chunk, key_score=key_score, workspace=ws_prefill)
 
-    stages = [("prefill", stage_prefill),
-              ("select_topb", lambda: L.select_topb(key_score, cfg.b, keep_rows=keep)),
-              ("select_topk", lambda: L.select_topk(chunk_score, cfg.k_per_seq, cfg.k_max, sel_chunk=sel)),
-              ("decode", lambda: decode())]
+    def stage_prefill_select():
+        L.prefill_select(pool_k, pool_v, chunk_slot, q_chunk, q_win, cfg.n_chunks, cfg.scale, cfg.b, chunk_score,
+                         cfg.k_per_seq, cfg.k_max, o_chunk=o_chunk, key_score=key_score, keep_rows=keep,
+                         sel_chunk=sel, workspace=ws_prefill)
+
+    if args.unfused:
+        stages = [("prefill", stage_prefill),
+                  ("select_topb", lambda: L.select_topb(key_score, cfg.b, keep_rows=keep)),
+                  ("select_topk", lambda: L.select_topk(chunk_score, cfg.k_per_seq, cfg.k_max, sel_chunk=sel)),
+                  ("decode", lambda: decode())]
+    else:
+        stages = [("prefill_select", stage_prefill_select), ("decode", lambda: decode())]
     if args.decode_only:
-        for _, fn in stages[:3]:
+        for _, fn in stages[:-1]:
             fn()
-        stages = stages[3:]
+        stages = stages[-1:]
 
     for _ in range(args.warmup):
         for _, fn in stages:
@@ -616,7 +639,7 @@ def main():
     step_flops = sum(flops[n] for n in names)
     value = step_flops / (step_ms * 1e-3) / 1e12
 
-    traffic = {"prefill": prefill_traffic()}
+    traffic = {"prefill": prefill_traffic(False), "prefill_select": prefill_traffic(True)}
 
     peaks = measured_peaks()
 
@@ -651,7 +674,8 @@ def main():
         "ms_per_step": step_ms, "us_per_step": step_ms * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, numpy PCG64)",
         "config": {"workload": "32K prefix: 128 chunks x (256+BOS), 28/4 heads, d=128, K=16, B=256, "
-                               "L_d=256, window 64; prefill side + top-B + top-K + split decode, 1 layer",
+                               "L_d=256, window 64; prefill side + top-B + top-K + split decode, 1 layer"
+                               + (" (prefill side as three calls)" if args.unfused else ""),
                    "global_batch": cfg.n_seq, "seq_len": cfg.n_chunks * cfg.chunk + cfg.l_d},
         "step_us_percentiles": {"median": float(np.median(step_all)) * 1e3,
                                 "p10": float(np.percentile(step_all, 10)) * 1e3,

@@ -39,7 +39,8 @@ class PageTable(ctypes.Structure):
 EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_select_topB",
            "pdllm_select_topK", "pdllm_decode_plan", "pdllm_split_attn_decode_workspace",
            "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
-           "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows")
+           "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows",
+           "pdllm_prefill_select")
 
 
 def _load() -> ctypes.CDLL:
@@ -73,13 +74,16 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_chunk_score_workspace.argtypes = [i32, i32, i32]
     lib.pdllm_chunk_score.restype = ctypes.c_int
     lib.pdllm_chunk_score.argtypes = [vp, i32, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.pdllm_prefill_select.restype = ctypes.c_int
+    lib.pdllm_prefill_select.argtypes = [P(Pool), vp, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp, i32, vp, vp,
+                                         i32, vp, i32, vp, vp, sz, vp]
     lib.pdllm_compact_kept_rows.restype = ctypes.c_int
     lib.pdllm_compact_kept_rows.argtypes = [P(Pool), vp, i32, vp, i32, vp, vp, i64, i64, i64, i32, vp]
     return lib
 
 
 lib = _load()
-ABI_VERSION = 5
+ABI_VERSION = 6
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -163,6 +167,49 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
                                          workspace.data_ptr(), workspace.numel(), _stream(dev)),
            "pdllm_chunk_prefill_score")
     return o_chunk, key_score
+
+
+def prefill_select(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win, scale, b, chunk_score,
+                   k_per_seq: Sequence[int], k_max: int, chunk_rows=None, o_chunk=None, key_score=None,
+                   keep_rows=None, sel_chunk=None, workspace=None):
+    """pdllm_prefill_select: chunk_prefill_score, select_topb and select_topk in
+    one call (chunk_score [n_seq][n_chunks / n_seq] float32).  Returns
+    (o_chunk, key_score, keep_rows, sel_chunk)."""
+    pool = make_pool(pool_k, pool_v)
+    _dense(chunk_slot, "chunk_slot", torch.int32)
+    _dense(q_chunk, "q_chunk", pool_k.dtype)
+    _dense(q_win, "q_win", pool_k.dtype)
+    _dense(chunk_score, "chunk_score", torch.float32)
+    n_chunks, rows, h_q, d = q_chunk.shape
+    if rows != pool.slot_rows or d != pool.d or q_win.shape[2:] != (h_q, d):
+        raise ValueError("q_chunk / q_win shapes do not match the pool")
+    if chunks_per_win < 1 or q_win.shape[0] * chunks_per_win < n_chunks or chunk_slot.numel() < n_chunks:
+        raise ValueError("q_win / chunk_slot do not cover n_chunks")
+    if chunk_rows is not None:
+        _dense(chunk_rows, "chunk_rows", torch.int32)
+        if chunk_rows.numel() < n_chunks:
+            raise ValueError("chunk_rows must hold n_chunks entries")
+    n_seq = chunk_score.shape[0]
+    if chunk_score.dim() != 2 or n_seq * chunk_score.shape[1] != n_chunks or len(k_per_seq) != n_seq:
+        raise ValueError("chunk_score must be [n_seq][n_chunks / n_seq] with one K_s per sequence")
+    dev = q_chunk.device
+    o_chunk = torch.empty_like(q_chunk) if o_chunk is None else o_chunk
+    if key_score is None:
+        key_score = torch.empty((n_chunks, rows), dtype=torch.float32, device=dev)
+    if keep_rows is None:
+        keep_rows = torch.empty((n_chunks, b), dtype=torch.int32, device=dev)
+    if sel_chunk is None:
+        sel_chunk = torch.empty((n_seq, k_max), dtype=torch.int32, device=dev)
+    need = lib.pdllm_prefill_score_workspace(n_chunks, h_q, pool.h_kv, rows, q_win.shape[1])
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ks = (ctypes.c_int32 * max(n_seq, 1))(*[int(x) for x in k_per_seq])
+    _check(lib.pdllm_prefill_select(ctypes.byref(pool), chunk_slot.data_ptr(), _ptr(chunk_rows), n_chunks,
+                                    q_chunk.data_ptr(), h_q, q_win.data_ptr(), q_win.shape[1], chunks_per_win,
+                                    float(scale), o_chunk.data_ptr(), key_score.data_ptr(), b, keep_rows.data_ptr(),
+                                    chunk_score.data_ptr(), n_seq, ks, k_max, sel_chunk.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), _stream(dev)), "pdllm_prefill_select")
+    return o_chunk, key_score, keep_rows, sel_chunk
 
 
 def select_topb(key_score: torch.Tensor, b: int, keep_rows=None, chunk_rows=None) -> torch.Tensor:

@@ -161,6 +161,21 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
   return PDLLM_OK;
 }
 
+// Validation and argument block of the chunk prefill (shared by the two
+// entry points that run it).
+pdllm_status prepare_prefill(const pdllm_pool* pool, const int32_t* chunk_slot, const int32_t* chunk_rows,
+                             int32_t n_chunks, const void* q_chunk, int32_t h_q, const void* q_win, int32_t w,
+                             int32_t chunks_per_win, float scale, void* o_chunk, float* key_score,
+                             void* workspace, size_t workspace_bytes, pdllm::PrefillArgs* out);
+
+pdllm_status launch_prefill_kernels(const pdllm::PrefillArgs& a, const pdllm_pool* pool, void* stream) {
+  const bool streamed = pool->dtype == PDLLM_BF16 && pool->slot_rows > pdllm::kPrefillMaxRows;
+  const int err = pool->dtype == PDLLM_F32 ? pdllm::launch_prefill_f32(a, pool->d, stream)
+                  : streamed               ? pdllm::launch_prefill_stream(a, pool->d, stream)
+                                           : pdllm::launch_prefill_bf16(a, pool->d, stream);
+  return hip_status(err, "chunk prefill launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,61 +202,74 @@ pdllm_status pdllm_chunk_prefill_score(const pdllm_pool* pool, const int32_t* ch
                                        const void* q_win, int32_t w, int32_t chunks_per_win,
                                        float scale, void* o_chunk, float* key_score,
                                        void* workspace, size_t workspace_bytes, void* stream) {
-  pdllm_status st = check_pool(pool);
-  if (st != PDLLM_OK) return st;
-  if (n_chunks < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 0");
-  if (h_q < 1 || h_q % pool->h_kv != 0)
-    return fail(PDLLM_ERR_INVALID_ARG, "h_q %d must be a positive multiple of h_kv %d", h_q, pool->h_kv);
-  if (w < 1 || chunks_per_win < 1)
-    return fail(PDLLM_ERR_INVALID_ARG, "w and chunks_per_win must be >= 1 (got %d, %d)", w, chunks_per_win);
-  if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
-  if (pool->slot_rows > 4097)
-    return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > 4097 is not supported", pool->slot_rows);
-  if (n_chunks == 0) return ok();
-  if (chunk_slot == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot is NULL");
-  if ((st = check_tensor(q_chunk, "q_chunk")) != PDLLM_OK) return st;
-  if ((st = check_tensor(q_win, "q_win")) != PDLLM_OK) return st;
-  if ((st = check_tensor(o_chunk, "o_chunk")) != PDLLM_OK) return st;
-  if ((st = check_tensor(key_score, "key_score")) != PDLLM_OK) return st;
-  const size_t need = pdllm_prefill_score_workspace(n_chunks, h_q, pool->h_kv, pool->slot_rows, w);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (!aligned16(workspace)) return fail(PDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-
   pdllm::PrefillArgs a{};
-  a.pool_k = pool->k;
-  a.pool_v = pool->v;
-  a.ps_slot = pool->stride_slot;
-  a.ps_row = pool->stride_row;
-  a.ps_head = pool->stride_head;
-  a.chunk_slot = chunk_slot;
-  a.chunk_rows = chunk_rows;
-  a.q_chunk = q_chunk;
-  a.q_win = q_win;
-  a.o_chunk = o_chunk;
-  a.key_score = key_score;
-  a.part_score = static_cast<float*>(workspace);
-  a.n_chunks = n_chunks;
-  a.slot_rows = pool->slot_rows;
-  a.h_q = h_q;
-  a.h_kv = pool->h_kv;
-  a.group = h_q / pool->h_kv;
-  a.w = w;
-  a.chunks_per_win = chunks_per_win;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  const bool streamed = pool->dtype == PDLLM_BF16 && pool->slot_rows > pdllm::kPrefillMaxRows;
-  a.parts = pool->dtype == PDLLM_BF16 && !streamed ? pdllm::kPrefillParts : 1;
-  if (streamed) {
-    const int64_t part_bytes = ((int64_t)n_chunks * pool->h_kv * pool->slot_rows * 4 + 255) / 256 * 256;
-    a.win_norm = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
-  }
-  const int err = pool->dtype == PDLLM_F32 ? pdllm::launch_prefill_f32(a, pool->d, stream)
-                  : streamed               ? pdllm::launch_prefill_stream(a, pool->d, stream)
-                                           : pdllm::launch_prefill_bf16(a, pool->d, stream);
-  if ((st = hip_status(err, "chunk prefill launch")) != PDLLM_OK) return st;
+  pdllm_status st = prepare_prefill(pool, chunk_slot, chunk_rows, n_chunks, q_chunk, h_q, q_win, w, chunks_per_win,
+                                    scale, o_chunk, key_score, workspace, workspace_bytes, &a);
+  if (st != PDLLM_OK || n_chunks == 0) return st;
+  if ((st = launch_prefill_kernels(a, pool, stream)) != PDLLM_OK) return st;
   if ((st = hip_status(pdllm::launch_score_finalize(a, stream), "score finalize launch")) != PDLLM_OK)
     return st;
+  return ok();
+}
+
+pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_slot, const int32_t* chunk_rows,
+                                  int32_t n_chunks, const void* q_chunk, int32_t h_q, const void* q_win, int32_t w,
+                                  int32_t chunks_per_win, float scale, void* o_chunk, float* key_score, int32_t b,
+                                  int32_t* keep_rows, const float* chunk_score, int32_t n_seq,
+                                  const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pdllm::PrefillArgs a{};
+  pdllm_status st = prepare_prefill(pool, chunk_slot, chunk_rows, n_chunks, q_chunk, h_q, q_win, w, chunks_per_win,
+                                    scale, o_chunk, key_score, workspace, workspace_bytes, &a);
+  if (st != PDLLM_OK) return st;
+  if (b < 0 || b > pool->slot_rows - 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "b %d outside [0, slot_rows - 1 = %d]", b, pool->slot_rows - 1);
+  if (b > 0 && n_chunks > 0 && keep_rows == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
+  if (n_seq < 1 || n_chunks % n_seq != 0)
+    return fail(PDLLM_ERR_INVALID_ARG, "n_seq %d must be >= 1 and divide n_chunks %d", n_seq, n_chunks);
+  const int n_per_seq = n_chunks / n_seq;
+  if (n_per_seq > 8192) return fail(PDLLM_ERR_UNSUPPORTED, "%d chunks per sequence > 8192", n_per_seq);
+  if (k_max < 0 || k_max > n_per_seq)
+    return fail(PDLLM_ERR_INVALID_ARG, "k_max %d outside [0, chunks per sequence %d]", k_max, n_per_seq);
+  if (k_max > 0) {
+    if (k_per_seq == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq (host) is NULL");
+    for (int s = 0; s < n_seq; ++s)
+      if (k_per_seq[s] < 0 || k_per_seq[s] > k_max)
+        return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq[%d] = %d outside [0, k_max %d]", s, k_per_seq[s], k_max);
+    if (chunk_score == nullptr || sel_chunk == nullptr)
+      return fail(PDLLM_ERR_INVALID_ARG, "chunk_score / sel_chunk is NULL");
+  }
+  if (n_chunks == 0) return ok();
+  if ((st = launch_prefill_kernels(a, pool, stream)) != PDLLM_OK) return st;
+  pdllm::FinalizeSelectArgs f{};
+  f.part = a.part_score;
+  f.key_score = key_score;
+  f.chunk_rows = chunk_rows;
+  f.keep_rows = keep_rows;
+  f.n_chunks = n_chunks;
+  f.h_kv = a.h_kv;
+  f.parts = a.parts;
+  f.slot_rows = a.slot_rows;
+  f.b = b;
+  // top-K rides in the same launch for the first sequences, and in launches
+  // of its own past kMaxTopkSeqPerLaunch of them
+  for (int s0 = 0; s0 < std::max(n_seq, 1); s0 += pdllm::kMaxTopkSeqPerLaunch) {
+    pdllm::TopkArgs& t = f.topk;
+    t = pdllm::TopkArgs{};
+    t.chunk_score = chunk_score;
+    t.sel_chunk = sel_chunk;
+    t.n_chunks = n_per_seq;
+    t.k_max = k_max;
+    t.seq0 = s0;
+    t.n_seq_launch = k_max > 0 ? std::min(pdllm::kMaxTopkSeqPerLaunch, n_seq - s0) : 0;
+    for (int i = 0; i < t.n_seq_launch; ++i) t.k[i] = k_per_seq[s0 + i];
+    if (s0 == 0) {
+      st = hip_status(pdllm::launch_finalize_select(f, stream), "finalize / select launch");
+    } else {
+      st = hip_status(pdllm::launch_select_topk(t, stream), "top-K launch");
+    }
+    if (st != PDLLM_OK) return st;
+  }
   return ok();
 }
 
@@ -485,3 +513,64 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
 }
 
 }  // extern "C"
+
+namespace {
+
+pdllm_status prepare_prefill(const pdllm_pool* pool, const int32_t* chunk_slot, const int32_t* chunk_rows,
+                             int32_t n_chunks, const void* q_chunk, int32_t h_q, const void* q_win, int32_t w,
+                             int32_t chunks_per_win, float scale, void* o_chunk, float* key_score,
+                             void* workspace, size_t workspace_bytes, pdllm::PrefillArgs* out) {
+  pdllm_status st = check_pool(pool);
+  if (st != PDLLM_OK) return st;
+  if (n_chunks < 0) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks must be >= 0");
+  if (h_q < 1 || h_q % pool->h_kv != 0)
+    return fail(PDLLM_ERR_INVALID_ARG, "h_q %d must be a positive multiple of h_kv %d", h_q, pool->h_kv);
+  if (w < 1 || chunks_per_win < 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "w and chunks_per_win must be >= 1 (got %d, %d)", w, chunks_per_win);
+  if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
+  if (pool->slot_rows > 4097)
+    return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > 4097 is not supported", pool->slot_rows);
+  if (n_chunks == 0) return ok();
+  if (chunk_slot == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot is NULL");
+  if ((st = check_tensor(q_chunk, "q_chunk")) != PDLLM_OK) return st;
+  if ((st = check_tensor(q_win, "q_win")) != PDLLM_OK) return st;
+  if ((st = check_tensor(o_chunk, "o_chunk")) != PDLLM_OK) return st;
+  if ((st = check_tensor(key_score, "key_score")) != PDLLM_OK) return st;
+  const size_t need = pdllm_prefill_score_workspace(n_chunks, h_q, pool->h_kv, pool->slot_rows, w);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(PDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  pdllm::PrefillArgs& a = *out;
+  a = pdllm::PrefillArgs{};
+  a.pool_k = pool->k;
+  a.pool_v = pool->v;
+  a.ps_slot = pool->stride_slot;
+  a.ps_row = pool->stride_row;
+  a.ps_head = pool->stride_head;
+  a.chunk_slot = chunk_slot;
+  a.chunk_rows = chunk_rows;
+  a.q_chunk = q_chunk;
+  a.q_win = q_win;
+  a.o_chunk = o_chunk;
+  a.key_score = key_score;
+  a.part_score = static_cast<float*>(workspace);
+  a.n_chunks = n_chunks;
+  a.slot_rows = pool->slot_rows;
+  a.h_q = h_q;
+  a.h_kv = pool->h_kv;
+  a.group = h_q / pool->h_kv;
+  a.w = w;
+  a.chunks_per_win = chunks_per_win;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool streamed = pool->dtype == PDLLM_BF16 && pool->slot_rows > pdllm::kPrefillMaxRows;
+  a.parts = pool->dtype == PDLLM_BF16 && !streamed ? pdllm::kPrefillParts : 1;
+  if (streamed) {
+    const int64_t part_bytes = ((int64_t)n_chunks * pool->h_kv * pool->slot_rows * 4 + 255) / 256 * 256;
+    a.win_norm = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
+  }
+  return PDLLM_OK;
+}
+
+}  // namespace

@@ -119,6 +119,20 @@ struct TopkArgs {
 };
 int launch_select_topk(const TopkArgs& a, void* stream);
 
+// Score finalize fused with both selections (one launch): workgroup c <
+// n_chunks adds chunk c's key-score partials (the order of the finalize
+// kernel) and selects its top-B rows; the next topk.n_seq_launch workgroups
+// select the top-K chunks of one sequence each.
+struct FinalizeSelectArgs {
+  const float* part;        // [n_chunks][h_kv][parts][slot_rows]
+  float* key_score;         // [n_chunks][slot_rows] out
+  const int32_t* chunk_rows;   // nullable
+  int32_t* keep_rows;       // [n_chunks][b] out
+  int32_t n_chunks, h_kv, parts, slot_rows, b;
+  TopkArgs topk;            // n_seq_launch = 0: no top-K work
+};
+int launch_finalize_select(const FinalizeSelectArgs& a, void* stream);
+
 // ---------------------------------------------------------------- chunk scores
 struct ChunkScoreArgs {
   const void* logits;       // [n_chunks][n_query + n_pseudo] rows of `vocab` logits

@@ -35,14 +35,27 @@ __device__ __forceinline__ uint64_t rank_key(float x, uint32_t index) {
 __device__ void select_sorted(const uint64_t* keys, int n, int count, int index_base,
                               int32_t* out, int* wave_counts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (count >= n) {                         // every candidate is kept
+    for (int i = tid; i < n; i += kThreads) out[i] = i + index_base;
+    return;
+  }
   int written = 0;
   for (int base = 0; base < n; base += kThreads) {
     const int i = base + tid;
     bool keep = false;
     if (i < n) {
       const uint64_t mine = keys[i];
+      // the rank: how many keys are larger (8 LDS reads in flight at a time)
       int rank = 0;
-      for (int j = 0; j < n; ++j) rank += keys[j] > mine ? 1 : 0;
+      int j = 0;
+      for (; j + 8 <= n; j += 8) {
+        uint64_t kj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kj[u] = keys[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += kj[u] > mine ? 1 : 0;
+      }
+      for (; j < n; ++j) rank += keys[j] > mine ? 1 : 0;
       keep = rank < count;
     }
     const uint64_t mask = __ballot(keep);
@@ -94,7 +107,77 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkArgs a) {
   select_sorted(keys, a.n_chunks, ks, 0, out, wave_counts);
 }
 
+// Score finalize, top-B and top-K in one launch (see FinalizeSelectArgs).
+// key_score[c][j] is the float sum of the partial rows in index order, the
+// same operations as score_finalize_kernel, so the scores, and the rows
+// selected from them, match the separate calls bit for bit.
+__global__ __launch_bounds__(kThreads) void finalize_select_kernel(const FinalizeSelectArgs a) {
+  __shared__ uint64_t keys[8192];
+  __shared__ int wave_counts[kThreads / 64];
+  const int blk = blockIdx.x;
+  if (blk >= a.n_chunks) {                // top-K of one sequence
+    const int si = blk - a.n_chunks;
+    const int s = a.topk.seq0 + si;
+    const int ks = a.topk.k[si];
+    const float* row = a.topk.chunk_score + (int64_t)s * a.topk.n_chunks;
+    int32_t* out = a.topk.sel_chunk + (int64_t)s * a.topk.k_max;
+    for (int i = threadIdx.x; i < a.topk.n_chunks; i += kThreads) keys[i] = rank_key(row[i], (uint32_t)i);
+    for (int i = ks + threadIdx.x; i < a.topk.k_max; i += kThreads) out[i] = -1;
+    __syncthreads();
+    select_sorted(keys, a.topk.n_chunks, ks, 0, out, wave_counts);
+    return;
+  }
+  const int c = blk;
+  const int R = a.slot_rows;
+  const int n_part = a.h_kv * a.parts;
+  const float* pc = a.part + (int64_t)c * n_part * R;
+  // keys j and j + kThreads together: the partial loads of both (32 each,
+  // clamped to valid addresses) are all in flight at once; each sum is
+  // added in index order
+  for (int j = threadIdx.x; j < R; j += 2 * kThreads) {
+    constexpr int kGroup = 32;
+    const int j2 = min(j + kThreads, R - 1);
+    float x = 0.f, x2 = 0.f;
+    for (int q0 = 0; q0 < n_part; q0 += kGroup) {
+      float v[kGroup], v2[kGroup];
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const int64_t q = min(q0 + u, n_part - 1);
+        v[u] = pc[q * R + j];
+        v2[u] = pc[q * R + j2];
+      }
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u)
+        if (q0 + u < n_part) {
+          x += v[u];
+          x2 += v2[u];
+        }
+    }
+    a.key_score[(int64_t)c * R + j] = x;
+    if (j > 0) keys[j - 1] = rank_key(x, (uint32_t)(j - 1));
+    if (j + kThreads < R) {
+      a.key_score[(int64_t)c * R + j2] = x2;
+      keys[j2 - 1] = rank_key(x2, (uint32_t)(j2 - 1));
+    }
+  }
+  if (a.b == 0) return;
+  const int rc = a.chunk_rows != nullptr ? min(max(a.chunk_rows[c], 1), R) : R;
+  const int n = rc - 1;
+  const int count = min(a.b, n);
+  int32_t* out = a.keep_rows + (int64_t)c * a.b;
+  for (int i = count + threadIdx.x; i < a.b; i += kThreads) out[i] = -1;
+  __syncthreads();
+  select_sorted(keys, n, count, 1, out, wave_counts);
+}
+
 }  // namespace
+
+int launch_finalize_select(const FinalizeSelectArgs& a, void* stream) {
+  const int grid = a.n_chunks + a.topk.n_seq_launch;
+  if (grid == 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(finalize_select_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
 
 int launch_select_topb(const float* key_score, const int32_t* chunk_rows, int n_chunks, int slot_rows,
                        int b, int32_t* keep_rows, void* stream) {

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 5
+#define PDLLM_ABI_VERSION 6
 
 typedef enum {
   PDLLM_OK = 0,
@@ -216,6 +216,27 @@ pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk
                                      const int32_t* keep_rows, int32_t b, void* dst_k, void* dst_v,
                                      int64_t dst_stride_slot, int64_t dst_stride_row,
                                      int64_t dst_stride_head, int32_t dst_slot_rows, void* stream);
+
+/*
+ * The prefill side in one call: pdllm_chunk_prefill_score, then
+ * pdllm_select_topB over its key scores, and pdllm_select_topK over the given
+ * chunk scores, with the same outputs bit for bit.  The key-score finalize and
+ * both selections share one launch after the attention kernels, so the call
+ * pays one kernel boundary where the three calls pay three.
+ *   pool .. workspace   as pdllm_chunk_prefill_score (the same workspace size)
+ *   b, keep_rows        as pdllm_select_topB (slot_rows = pool->slot_rows,
+ *                       chunk_rows as given); keep_rows may be NULL when b = 0
+ *   chunk_score, n_seq, k_per_seq, k_max, sel_chunk
+ *                       as pdllm_select_topK, with n_chunks / n_seq chunks
+ *                       per sequence (n_seq must divide n_chunks); chunk_score,
+ *                       k_per_seq and sel_chunk may be NULL when k_max = 0
+ */
+pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_slot, const int32_t* chunk_rows,
+                                  int32_t n_chunks, const void* q_chunk, int32_t h_q, const void* q_win, int32_t w,
+                                  int32_t chunks_per_win, float scale, void* o_chunk, float* key_score, int32_t b,
+                                  int32_t* keep_rows, const float* chunk_score, int32_t n_seq,
+                                  const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace pdllm_chunk_score needs (0 when the arguments are
  * invalid).  Pure host function. */

@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 5
+    assert L.lib.pdllm_abi_version() == 6
 
 
 def _pool(**kw):
@@ -231,3 +231,24 @@ def test_compaction_validation():
     assert f(*args(n=-1)) == INVALID
     assert f(*args(pool=_pool(d=96))) == UNSUPPORTED
     assert f(*args(n=0)) == OK                              # nothing to do, nothing enqueued
+
+
+def test_prefill_select_validation():
+    f = L.lib.pdllm_prefill_select
+    pool = _pool()
+    ks = (ctypes.c_int32 * 2)(16, 16)
+    ws = L.lib.pdllm_prefill_score_workspace(128, 28, 4, 257, 64)
+    args = lambda **kw: [ctypes.byref(kw.get("pool", pool)), 0x30000, None, kw.get("n", 128), 0x60000, 28,
+                         0x70000, 64, 128, 0.088, 0x90000, 0xA0000, kw.get("b", 256), kw.get("keep", 0xB0000),
+                         kw.get("cs", 0xC0000), kw.get("n_seq", 1), kw.get("ks", ks), kw.get("k_max", 16),
+                         kw.get("sel", 0xD0000), kw.get("ws", 0x100000), kw.get("ws_bytes", ws), None]
+    assert f(*args(b=257)) == INVALID and "b 257" in _err()
+    assert f(*args(keep=None)) == INVALID and "keep_rows" in _err()
+    assert f(*args(n_seq=3)) == INVALID and "divide" in _err()
+    assert f(*args(k_max=129)) == INVALID and "k_max" in _err()
+    assert f(*args(ks=(ctypes.c_int32 * 1)(17))) == INVALID and "k_per_seq[0]" in _err()
+    assert f(*args(cs=None)) == INVALID
+    assert f(*args(sel=None)) == INVALID
+    assert f(*args(ws_bytes=ws - 1)) == WS_SMALL
+    assert f(*args(pool=_pool(d=96))) == UNSUPPORTED
+    assert f(*args(n=0, n_seq=1, k_max=0)) == OK        # nothing to do, nothing enqueued

@@ -1,0 +1,82 @@
+"""GPU parity of pdllm_prefill_select (chunk prefill, key-score finalize,
+top-B and top-K in one call) through the C ABI: its outputs equal those of
+pdllm_chunk_prefill_score + pdllm_select_topB + pdllm_select_topK bit for
+bit, and its selections equal the oracle's on the same score arrays.  Covers
+the 32K workload, several sequences (more than one top-K launch's worth too),
+a partial last chunk, streamed chunks, float32, B = 0 and K = 0."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _parity import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(cfg, seed, b=None, k_max=None, chunk_rows=None):
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    b = cfg.b if b is None else b
+    k_per_seq = list(cfg.k_per_seq) if k_max is None else [min(k, k_max) for k in cfg.k_per_seq]
+    k_max = cfg.k_max if k_max is None else k_max
+    inp = synth.generate(cfg, seed, with_q_chunk=True)
+    pk, pv, slot = dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot)
+    qc, qw, cs = dev(inp.q_chunk), dev(inp.q_win), dev(inp.chunk_score)
+    rows = dev(chunk_rows) if chunk_rows is not None else None
+    o1, ks1 = L.chunk_prefill_score(pk, pv, slot, qc, qw, cfg.n_chunks, cfg.scale, chunk_rows=rows)
+    keep1 = L.select_topb(ks1, b, chunk_rows=rows)
+    sel1 = L.select_topk(cs, k_per_seq, k_max)
+    o2, ks2, keep2, sel2 = L.prefill_select(pk, pv, slot, qc, qw, cfg.n_chunks, cfg.scale, b, cs, k_per_seq, k_max,
+                                            chunk_rows=rows)
+    torch.cuda.synchronize()
+    return inp, (o1, ks1, keep1, sel1), (o2, ks2, keep2, sel2), b, k_per_seq, k_max
+
+
+def _check(cfg, sep, fused, inp, b, k_per_seq, k_max, chunk_rows=None, what=""):
+    import torch
+    o1, ks1, keep1, sel1 = sep
+    o2, ks2, keep2, sel2 = fused
+    rows = cfg.chunk_rows if chunk_rows is None else chunk_rows
+    valid = torch.from_numpy(np.arange(cfg.rows)[None, :] < rows[:, None]).to(o1.device)
+    assert torch.equal(o1[valid], o2[valid]), f"{what}: o_chunk differs"
+    assert torch.equal(ks1, ks2), f"{what}: key_score differs"
+    assert torch.equal(keep1, keep2), f"{what}: keep_rows differs"
+    assert torch.equal(sel1, sel2), f"{what}: sel_chunk differs"
+    ks = ks2.cpu().numpy()
+    assert np.array_equal(keep2.cpu().numpy(), oracle.select_topb(ks, b, chunk_rows=chunk_rows))
+    if k_max:
+        assert np.array_equal(sel2.cpu().numpy(), oracle.select_topk(inp.chunk_score, k_per_seq, k_max))
+
+
+CASES = [
+    ("s32", synth.config("s32"), {}),
+    ("two_seq", synth.Config("p", 28, 4, 128, "bf16", 6, 256, (3, 5), 100, 64, 64, n_seq=2), {}),
+    ("b0", synth.Config("p", 14, 2, 128, "bf16", 4, 64, (2,), 0, 32, 32), {}),
+    ("k0", synth.Config("p", 14, 2, 64, "bf16", 4, 64, (2,), 20, 32, 32), dict(k_max=0)),
+    ("c512", synth.Config("p", 14, 2, 128, "bf16", 3, 512, (2,), 200, 64, 64), {}),
+    ("tiny_f32", synth.config("tiny"), {}),
+]
+
+
+@pytest.mark.parametrize("name,cfg,kw", CASES, ids=[c[0] for c in CASES])
+def test_fused_equals_separate_calls(device, name, cfg, kw):
+    say(f"prefill_select {name}")
+    inp, sep, fused, b, ks, k_max = _both(cfg, 0, **kw)
+    _check(cfg, sep, fused, inp, b, ks, k_max, what=name)
+
+
+def test_fused_with_partial_last_chunk(device):
+    cfg = synth.Config("p", 28, 4, 128, "bf16", 4, 256, (4, 2), 128, 64, 64, n_seq=2, last_chunk=60)
+    say("prefill_select, partial last chunk")
+    inp, sep, fused, b, ks, k_max = _both(cfg, 1, chunk_rows=cfg.chunk_rows)
+    _check(cfg, sep, fused, inp, b, ks, k_max, chunk_rows=cfg.chunk_rows, what="partial")
+    assert (fused[2].cpu().numpy()[cfg.chunk_rows < cfg.rows, 60:] == -1).all()
+
+
+def test_fused_with_many_sequences(device):
+    """70 sequences: top-K needs a second launch past the fused one."""
+    cfg = synth.Config("p", 4, 2, 64, "bf16", 3, 32, tuple([1, 2, 3, 0] * 17 + [2, 1]), 8, 16, 16, n_seq=70)
+    say("prefill_select, 70 sequences")
+    inp, sep, fused, b, ks, k_max = _both(cfg, 2)
+    _check(cfg, sep, fused, inp, b, ks, k_max, what="70 sequences")
