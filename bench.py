@@ -71,12 +71,13 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "b0b25bb9a30a89f6",
+    "sources_sha": "177bb851a0e9f843",
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149208.28, "write_kib": 234627.37},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149208.66, "write_kib": 234605.73},
+        "finalize_select_kernel": {"fetch_kib": 2101.31, "write_kib": 260.06},
         "score_finalize_kernel": {"fetch_kib": 2551.44, "write_kib": 128.5},
     },
-    "copy_fetch_kib": 524301.26,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.28,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 
