@@ -377,7 +377,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
 // in float32 and rounded once to the output type.  With BF16 the partial
 // outputs are bf16 (the bf16 decode kernel writes them so) and each thread
 // takes 8 values of a row, otherwise float32 and 4 values.
-template <int D, bool BF16>
+template <int D, bool BF16, int kBatch>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
   constexpr int EPT = BF16 ? 8 : 4;        // values per thread (16 bytes of partial)
   constexpr int TPR = D / EPT;
@@ -407,11 +407,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
       for (int q = 0; q < 4; ++q) x[q] = w[q];
     }
   };
-  // Splits are visited in groups of kBatch whose lse and partial loads are
-  // all in flight together (one memory round trip per group; the S32 plans
-  // have one group).  The weights of a group are taken against the running
-  // maximum, and the sums of earlier groups are rescaled when it grows.
-  constexpr int kBatch = 16;
+  // Splits are visited in groups of kBatch (4 to 16, fitted at launch to
+  // the largest split count) whose lse and partial loads are all in flight
+  // together: one memory round trip per group.  The weights of a group are
+  // taken against the running maximum (in log2 units), and the sums of
+  // earlier groups are rescaled when it grows.
   float mx = -INFINITY, tot = 0.f;
   float o[EPT];
 #pragma unroll
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int j = min(j0 + u, n_splits - 1);   // past the end: a valid split, weight 0
-      t[u] = j0 + u < n_splits ? pl[j * sl] : -INFINITY;
+      t[u] = j0 + u < n_splits ? pl[j * sl] * kLog2e : -INFINITY;
       load(j, x[u]);
     }
     float m_new = mx;
@@ -430,13 +430,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
     for (int u = 0; u < kBatch; ++u) m_new = fmaxf(m_new, t[u]);
     // every split so far empty (lse = -inf): weigh against 0, all weights are 0
     const float ref = m_new == -INFINITY ? 0.f : m_new;
-    const float c = expf(mx - ref);            // 0 on the first group
+    const float c = __builtin_amdgcn_exp2f(mx - ref);   // 0 on the first group
     tot *= c;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) o[e] *= c;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float w = expf(t[u] - ref);        // 0 for an empty split and past the end
+      const float w = __builtin_amdgcn_exp2f(t[u] - ref);   // 0 for an empty split and past the end
       tot += w;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) o[e] += w * x[u][e];
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + out) =
         f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   }
-  if (a.lse != nullptr && e0 == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = mx + logf(tot);
+  if (a.lse != nullptr && e0 == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = (mx + __log2f(tot)) * kLn2;
 }
 
 template <int D, bool BF16>
@@ -463,7 +463,17 @@ int merge_launch(const DecodeArgs& a, void* stream) {
   constexpr int RPB = 256 / (D / (BF16 ? 8 : 4));
   const int rows = a.l_d * a.h_q;
   dim3 grid((rows + RPB - 1) / RPB, a.n_seq_launch);
-  hipLaunchKernelGGL((lse_merge_kernel<D, BF16>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  int ns = 1;
+  for (int i = 0; i < a.n_seq_launch; ++i) ns = max(ns, a.seq[i].n_splits);
+  const hipStream_t st = (hipStream_t)stream;
+  if (ns <= 4)
+    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 4>), grid, dim3(256), 0, st, a);
+  else if (ns <= 8)
+    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 8>), grid, dim3(256), 0, st, a);
+  else if (ns <= 12)
+    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 12>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 16>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
