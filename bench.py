@@ -5,16 +5,18 @@ One step is one pass of the whole path over the 32K-prefix workload
 randomly permuted pool; K = 16 chunks, B = 256 rows kept, L_d = 256 decode
 rows; scoring window = the first 64 decode rows):
 
-  1. chunk-local attention over all 128 chunks with fused per-key scoring,
-     top-B rows per chunk and top-K chunks over the given chunk scores
-     (pdllm_prefill_select: the prefill kernel, then one launch for the
-     key-score finalize and both selections),
+  1. chunk-local attention over all 128 chunks, top-K chunks over the given
+     chunk scores, and per-key scoring and top-B rows inside the K kept
+     chunks (pdllm_prefill_select with selected_only: the prefill kernel,
+     whose workgroups score their chunk only if top-K keeps it, then one
+     launch for the key-score finalize and both selections),
   2. split-KV decode attention over the selected page table, with the
      log-sum-exp merge (pdllm_split_attn_decode).
 
-With --unfused the prefill side runs as three calls instead
-(pdllm_chunk_prefill_score, pdllm_select_topB, pdllm_select_topK), with the
-same outputs bit for bit.
+With --score-all every chunk is scored and gets its top-B rows (the kept
+chunks' results are the same bit for bit); with --unfused the prefill side
+runs as three calls instead (pdllm_chunk_prefill_score, pdllm_select_topB,
+pdllm_select_topK), scoring every chunk.
 
 Inputs are seeded synthetic data already resident in HBM.  The JSON line
 reports algorithmic TFLOP/s of the step (QK^T + PV of the chunk attention,
@@ -91,6 +93,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of COPY_BYTES (byte-counter scale)")
+    p.add_argument("--score-all", action="store_true",
+                   help="score every chunk (top-B for all chunks), not only the K kept ones")
     p.add_argument("--unfused", action="store_true",
                    help="run the prefill side as three calls (prefill + scoring, top-B, top-K)")
     p.add_argument("--decode-only", action="store_true",
@@ -113,9 +117,11 @@ def parse():
     return p.parse_args()
 
 
-def workload_counts(cfg):
-    """Algorithmic FLOPs and HBM bytes of each stage of one step."""
+def workload_counts(cfg, scored=None):
+    """Algorithmic FLOPs and HBM bytes of each stage of one step; `scored`
+    chunks (default: all) run the window scoring and get top-B rows."""
     n, r, hq, hk, d, w = cfg.n_slots, cfg.rows, cfg.h_q, cfg.h_kv, cfg.d, cfg.w
+    ns = n if scored is None else scored
     e = 2  # bf16 bytes
     n_kv = [k * (cfg.b + 1) + cfg.l_d for k in cfg.k_per_seq]
     flops = {
@@ -124,7 +130,7 @@ def workload_counts(cfg):
         "select_topk": 0.0,
         "decode": sum(4.0 * cfg.l_d * hq * d * x for x in n_kv),
     }
-    flops["prefill_select"] = flops["prefill"]
+    flops["prefill_select"] = 4.0 * n * r * r * hq * d + 2.0 * ns * w * r * hq * d
     bytes_ = {
         # q_chunk + o_chunk + the chunks' pool K/V + query window + key scores
         "prefill": 2.0 * n * r * hq * d * e + 2.0 * n * r * hk * d * e + cfg.n_seq * w * hq * d * e
@@ -134,7 +140,8 @@ def workload_counts(cfg):
         # q + kept pool K/V rows (BOS included) + response K/V + o
         "decode": sum(2.0 * cfg.l_d * hq * d * e + 2.0 * x * hk * d * e for x in n_kv),
     }
-    bytes_["prefill_select"] = bytes_["prefill"] + bytes_["select_topb"] + bytes_["select_topk"]
+    bytes_["prefill_select"] = (2.0 * n * r * hq * d * e + 2.0 * n * r * hk * d * e + cfg.n_seq * w * hq * d * e
+                                + 4.0 * ns * r + 4.0 * ns * r + 4.0 * ns * cfg.b + bytes_["select_topk"])
     return flops, bytes_
 
 
@@ -602,7 +609,7 @@ def main():
     def stage_prefill_select():
         L.prefill_select(pool_k, pool_v, chunk_slot, q_chunk, q_win, cfg.n_chunks, cfg.scale, cfg.b, chunk_score,
                          cfg.k_per_seq, cfg.k_max, o_chunk=o_chunk, key_score=key_score, keep_rows=keep,
-                         sel_chunk=sel, workspace=ws_prefill)
+                         sel_chunk=sel, workspace=ws_prefill, selected_only=not args.score_all)
 
     if args.unfused:
         stages = [("prefill", stage_prefill),
@@ -635,7 +642,8 @@ def main():
     step_all = [ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]
     step_ms = float(np.mean(step_all))
 
-    flops, bytes_ = workload_counts(cfg)
+    scored = None if (args.score_all or args.unfused) else sum(cfg.k_per_seq)
+    flops, bytes_ = workload_counts(cfg, scored)
     names = [n for n, _ in stages]
     step_flops = sum(flops[n] for n in names)
     value = step_flops / (step_ms * 1e-3) / 1e12
@@ -675,8 +683,10 @@ def main():
         "ms_per_step": step_ms, "us_per_step": step_ms * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, numpy PCG64)",
         "config": {"workload": "32K prefix: 128 chunks x (256+BOS), 28/4 heads, d=128, K=16, B=256, "
-                               "L_d=256, window 64; prefill side + top-B + top-K + split decode, 1 layer"
-                               + (" (prefill side as three calls)" if args.unfused else ""),
+                               "L_d=256, window 64; prefill side + top-K + top-B + split decode, 1 layer; "
+                               + ("prefill side as three calls, every chunk scored" if args.unfused else
+                                  "every chunk scored" if args.score_all else
+                                  "the K kept chunks scored (top-B inside them)"),
                    "global_batch": cfg.n_seq, "seq_len": cfg.n_chunks * cfg.chunk + cfg.l_d},
         "step_us_percentiles": {"median": float(np.median(step_all)) * 1e3,
                                 "p10": float(np.percentile(step_all, 10)) * 1e3,

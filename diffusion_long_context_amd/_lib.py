@@ -76,14 +76,14 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_chunk_score.argtypes = [vp, i32, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.pdllm_prefill_select.restype = ctypes.c_int
     lib.pdllm_prefill_select.argtypes = [P(Pool), vp, vp, i32, vp, i32, vp, i32, i32, f32, vp, vp, i32, vp, vp,
-                                         i32, vp, i32, vp, vp, sz, vp]
+                                         i32, vp, i32, vp, i32, vp, sz, vp]
     lib.pdllm_compact_kept_rows.restype = ctypes.c_int
     lib.pdllm_compact_kept_rows.argtypes = [P(Pool), vp, i32, vp, i32, vp, vp, i64, i64, i64, i32, vp]
     return lib
 
 
 lib = _load()
-ABI_VERSION = 6
+ABI_VERSION = 7
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -171,10 +171,11 @@ def chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_w
 
 def prefill_select(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win, scale, b, chunk_score,
                    k_per_seq: Sequence[int], k_max: int, chunk_rows=None, o_chunk=None, key_score=None,
-                   keep_rows=None, sel_chunk=None, workspace=None):
+                   keep_rows=None, sel_chunk=None, workspace=None, selected_only=False):
     """pdllm_prefill_select: chunk_prefill_score, select_topb and select_topk in
-    one call (chunk_score [n_seq][n_chunks / n_seq] float32).  Returns
-    (o_chunk, key_score, keep_rows, sel_chunk)."""
+    one call (chunk_score [n_seq][n_chunks / n_seq] float32).  With
+    selected_only, key_score and keep_rows are written for the chunks top-K
+    selects only.  Returns (o_chunk, key_score, keep_rows, sel_chunk)."""
     pool = make_pool(pool_k, pool_v)
     _dense(chunk_slot, "chunk_slot", torch.int32)
     _dense(q_chunk, "q_chunk", pool_k.dtype)
@@ -208,7 +209,8 @@ def prefill_select(pool_k, pool_v, chunk_slot, q_chunk, q_win, chunks_per_win, s
                                     q_chunk.data_ptr(), h_q, q_win.data_ptr(), q_win.shape[1], chunks_per_win,
                                     float(scale), o_chunk.data_ptr(), key_score.data_ptr(), b, keep_rows.data_ptr(),
                                     chunk_score.data_ptr(), n_seq, ks, k_max, sel_chunk.data_ptr(),
-                                    workspace.data_ptr(), workspace.numel(), _stream(dev)), "pdllm_prefill_select")
+                                    1 if selected_only else 0, workspace.data_ptr(), workspace.numel(), _stream(dev)),
+           "pdllm_prefill_select")
     return o_chunk, key_score, keep_rows, sel_chunk
 
 

@@ -73,6 +73,45 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_row<0x140>(v);
 }
 
+// Selection order as an integer key: a float score becomes an order-
+// preserving 32-bit key (-0 and +0 share one, NaN gets the lowest), and
+// candidate i gets (key << 32) | ~i, so that equal scores rank the lower
+// index first and all keys differ.  i outranks j iff key_i > key_j.
+__device__ __forceinline__ uint64_t rank_key(float x, uint32_t index) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t key;
+  if (x != x) {
+    key = 0u;                               // NaN: after every number
+  } else {
+    if (x == 0.f) u = 0u;                   // -0 == +0
+    key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - index);
+}
+
+// Whether candidate c of row[0..n) is among the k best (fewer than k
+// candidates outrank it), the rule top-K selects by.  Called by a whole
+// wavefront; the result is wave-uniform.
+__device__ __forceinline__ bool in_top_k(const float* row, int n, int c, int k) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t mine = rank_key(row[c], (uint32_t)c);
+  int larger = 0;
+  for (int j = lane; j < n; j += 64) larger += rank_key(row[j], (uint32_t)j) > mine ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) larger += __shfl_xor(larger, off, 64);
+  return __builtin_amdgcn_readfirstlane(larger) < k;
+}
+
+// Whether chunk c of a prefill launch takes part in the window scoring: every
+// chunk, or (a.sel_score set) the chunks top-K selects -- chunk c is chunk
+// c % sel_per_seq of sequence c / sel_per_seq.  Wave-uniform.
+template <class Args>
+__device__ __forceinline__ bool chunk_scored(const Args& a, int c) {
+  if (a.sel_score == nullptr) return true;
+  const int s = c / a.sel_per_seq;
+  return in_top_k(a.sel_score + (int64_t)s * a.sel_per_seq, a.sel_per_seq, c - s * a.sel_per_seq, a.sel_k[s]);
+}
+
 // A compile-time flag passed to a generic lambda (instantiates it twice).
 template <bool B>
 struct BoolConst {

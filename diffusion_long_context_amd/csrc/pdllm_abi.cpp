@@ -216,8 +216,8 @@ pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_s
                                   int32_t n_chunks, const void* q_chunk, int32_t h_q, const void* q_win, int32_t w,
                                   int32_t chunks_per_win, float scale, void* o_chunk, float* key_score, int32_t b,
                                   int32_t* keep_rows, const float* chunk_score, int32_t n_seq,
-                                  const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
+                                  int32_t selected_only, void* workspace, size_t workspace_bytes, void* stream) {
   pdllm::PrefillArgs a{};
   pdllm_status st = prepare_prefill(pool, chunk_slot, chunk_rows, n_chunks, q_chunk, h_q, q_win, w, chunks_per_win,
                                     scale, o_chunk, key_score, workspace, workspace_bytes, &a);
@@ -239,7 +239,21 @@ pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_s
     if (chunk_score == nullptr || sel_chunk == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "chunk_score / sel_chunk is NULL");
   }
+  if (selected_only != 0 && selected_only != 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "selected_only must be 0 or 1 (got %d)", selected_only);
+  if (selected_only && chunk_score == nullptr)
+    return fail(PDLLM_ERR_INVALID_ARG, "selected_only needs chunk_score");
+  if (selected_only && k_max == 0 && k_per_seq == nullptr)
+    return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq (host) is NULL");
   if (n_chunks == 0) return ok();
+  // only the selected chunks are scored: the sequences' K_s travel in the
+  // launch arguments (up to kMaxSelSeq sequences; past that, every chunk is)
+  const bool sel = selected_only && n_seq <= pdllm::kMaxSelSeq;
+  if (sel) {
+    a.sel_score = chunk_score;
+    a.sel_per_seq = n_per_seq;
+    for (int s = 0; s < n_seq; ++s) a.sel_k[s] = k_max > 0 ? k_per_seq[s] : 0;
+  }
   if ((st = launch_prefill_kernels(a, pool, stream)) != PDLLM_OK) return st;
   pdllm::FinalizeSelectArgs f{};
   f.part = a.part_score;
@@ -251,6 +265,7 @@ pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_s
   f.parts = a.parts;
   f.slot_rows = a.slot_rows;
   f.b = b;
+  f.selected_only = sel ? 1 : 0;
   // top-K rides in the same launch for the first sequences, and in launches
   // of its own past kMaxTopkSeqPerLaunch of them
   for (int s0 = 0; s0 < std::max(n_seq, 1); s0 += pdllm::kMaxTopkSeqPerLaunch) {
@@ -262,7 +277,8 @@ pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_s
     t.k_max = k_max;
     t.seq0 = s0;
     t.n_seq_launch = k_max > 0 ? std::min(pdllm::kMaxTopkSeqPerLaunch, n_seq - s0) : 0;
-    for (int i = 0; i < t.n_seq_launch; ++i) t.k[i] = k_per_seq[s0 + i];
+    for (int i = 0; i < std::min(pdllm::kMaxTopkSeqPerLaunch, n_seq - s0); ++i)
+      t.k[i] = k_max > 0 ? k_per_seq[s0 + i] : 0;
     if (s0 == 0) {
       st = hip_status(pdllm::launch_finalize_select(f, stream), "finalize / select launch");
     } else {

@@ -80,6 +80,7 @@ int launch_decode_f32(const DecodeArgs& a, int d, void* stream);
 int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_out, void* stream);
 
 // ---------------------------------------------------------------- prefill
+constexpr int kMaxSelSeq = 64;           // sequences whose K_s a prefill launch carries
 struct PrefillArgs {
   const void* pool_k;
   const void* pool_v;
@@ -95,7 +96,14 @@ struct PrefillArgs {
   int32_t n_chunks, slot_rows, h_q, h_kv, group, w, chunks_per_win;
   int32_t parts;            // partial key-score rows per (chunk, kv head)
   float scale_log2;
+  // Scoring only the chunks top-K selects (sel_score != nullptr): chunk c,
+  // chunk c % sel_per_seq of sequence c / sel_per_seq, is scored iff it is
+  // among the sel_k[sequence] best of its sequence's row of sel_score.
+  const float* sel_score;   // [n_seq][sel_per_seq] or nullptr (score every chunk)
+  int32_t sel_per_seq;
+  int32_t sel_k[kMaxSelSeq];
 };
+
 
 // partial key-score rows per (chunk, kv head): one per wavefront of the bf16
 // kernel, one for the f32 kernel; the workspace is sized for the larger
@@ -129,6 +137,7 @@ struct FinalizeSelectArgs {
   const int32_t* chunk_rows;   // nullable
   int32_t* keep_rows;       // [n_chunks][b] out
   int32_t n_chunks, h_kv, parts, slot_rows, b;
+  int32_t selected_only;    // 1: only chunks top-K selects (topk holds every sequence) are finalized
   TopkArgs topk;            // n_seq_launch = 0: no top-K work
 };
 int launch_finalize_select(const FinalizeSelectArgs& a, void* stream);

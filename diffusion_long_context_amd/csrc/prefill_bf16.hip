@@ -86,6 +86,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   bf16x8 qw_cur[2][DC];
   if (n_wb > 0) fetch_w(min(wave, n_wb - 1), qw_cur);
 
+  bool scored = true;
   // ---- stage the chunk's K and V (rows >= Rc are zero); every load is issued
   // before the first LDS store so the staging costs one memory round trip
   {
@@ -110,6 +111,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           kr[ps][i] = vr[ps][i] = u32x4{0, 0, 0, 0};
         }
       }
+    // whether this chunk is scored (its score loads queue behind the
+    // staging loads, which the stores below wait for anyway)
+    scored = chunk_scored(a, c);
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps)
 #pragma unroll
@@ -175,7 +179,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) colsum[kb] = 0.f;
   const uint16_t* k16 = &sm.k[lr * KP + 8 * lj];
-  for (int witem = wave; witem < n_wb; witem += kWaves) {
+  // (a chunk that top-K does not select is not scored when only the
+  // selected ones are asked for: its waves go straight to the chunk items)
+  for (int witem = wave; scored && witem < n_wb; witem += kWaves) {
     const int first = witem * 32;
     bf16x8 qf[2][DC];
 #pragma unroll
@@ -246,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // per-key sums of this wave: across its 4 lane groups, then one row of
   // the partial key scores (the finalize kernel adds the waves and kv heads
   // in a fixed order)
-  {
+  if (scored) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       colsum[kb] = wave_xor_sum(colsum[kb], 16);

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(const PrefillArgs
     for (int e = 0; e < D; ++e) oc[((int64_t)r * a.h_q + h) * D + e] = acc[e] * inv;
   }
 
-  // window rows -> per-key weight
+  // window rows -> per-key weight (only for a scored chunk; uniform)
+  if (!chunk_scored(a, c)) return;
   const float* qw = static_cast<const float*>(a.q_win) + (int64_t)(c / a.chunks_per_win) * a.w * a.h_q * D;
   for (int j = tid; j < R; j += kThreads) colsum[j] = 0.f;
   const int n_win = a.w * G;

@@ -71,6 +71,9 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
   const int64_t base = (int64_t)a.chunk_slot[c] * a.ps_slot + (int64_t)g * a.ps_head;
   const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k) + base;
   const uint16_t* pv = static_cast<const uint16_t*>(a.pool_v) + base;
+  if constexpr (WIN) {
+    if (!chunk_scored(a, c)) return;        // a chunk top-K does not select (uniform)
+  }
 
   // ---- queries (B operand of S^T); pairs past the end clamp to the last one
   const int xq = qt * kRows + wave * 32 + lc;
@@ -211,6 +214,7 @@ __global__ __launch_bounds__(64 * kColWaves) void window_colsum_kernel(const Pre
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 31, lj = lane >> 5;
   const int j0 = kt * kColKeys;
+  if (!chunk_scored(a, c)) return;          // a chunk top-K does not select (uniform)
 
   // ---- stage the key tile; rows past the chunk clamp to its last row
   // (their sums are written as 0).  All loads go out before the first store.

@@ -18,18 +18,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint64_t rank_key(float x, uint32_t index) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t key;
-  if (x != x) {
-    key = 0u;                               // NaN: after every number
-  } else {
-    if (x == 0.f) u = 0u;                   // -0 == +0
-    key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - index);
-}
-
 // Select the `count` best of the n keys in `keys` (LDS) and write their
 // indices + `index_base`, ascending, to out[0..count).
 __device__ void select_sorted(const uint64_t* keys, int n, int count, int index_base,
@@ -128,6 +116,12 @@ __global__ __launch_bounds__(kThreads) void finalize_select_kernel(const Finaliz
     return;
   }
   const int c = blk;
+  if (a.selected_only) {                    // only the chunks top-K selects (uniform)
+    const int s = c / a.topk.n_chunks;
+    if (!in_top_k(a.topk.chunk_score + (int64_t)s * a.topk.n_chunks, a.topk.n_chunks, c - s * a.topk.n_chunks,
+                  a.topk.k[s]))
+      return;
+  }
   const int R = a.slot_rows;
   const int n_part = a.h_kv * a.parts;
   const float* pc = a.part + (int64_t)c * n_part * R;

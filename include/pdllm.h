@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 6
+#define PDLLM_ABI_VERSION 7
 
 typedef enum {
   PDLLM_OK = 0,
@@ -230,13 +230,21 @@ pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk
  *                       as pdllm_select_topK, with n_chunks / n_seq chunks
  *                       per sequence (n_seq must divide n_chunks); chunk_score,
  *                       k_per_seq and sel_chunk may be NULL when k_max = 0
+ *   selected_only       0: every chunk is scored and gets its top-B rows.
+ *                       1: only the chunks top-K selects (Methodology 2 keeps
+ *                       top-B rows inside the K kept chunks): the scoring
+ *                       window runs on those chunks only, and key_score and
+ *                       keep_rows are written for them only, with the same
+ *                       values as with 0; o_chunk is written for every chunk
+ *                       either way.  Needs chunk_score.  With more than 64
+ *                       sequences every chunk is scored.
  */
 pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_slot, const int32_t* chunk_rows,
                                   int32_t n_chunks, const void* q_chunk, int32_t h_q, const void* q_win, int32_t w,
                                   int32_t chunks_per_win, float scale, void* o_chunk, float* key_score, int32_t b,
                                   int32_t* keep_rows, const float* chunk_score, int32_t n_seq,
-                                  const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
+                                  int32_t selected_only, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace pdllm_chunk_score needs (0 when the arguments are
  * invalid).  Pure host function. */

@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 6
+    assert L.lib.pdllm_abi_version() == 7
 
 
 def _pool(**kw):
@@ -241,7 +241,8 @@ def test_prefill_select_validation():
     args = lambda **kw: [ctypes.byref(kw.get("pool", pool)), 0x30000, None, kw.get("n", 128), 0x60000, 28,
                          0x70000, 64, 128, 0.088, 0x90000, 0xA0000, kw.get("b", 256), kw.get("keep", 0xB0000),
                          kw.get("cs", 0xC0000), kw.get("n_seq", 1), kw.get("ks", ks), kw.get("k_max", 16),
-                         kw.get("sel", 0xD0000), kw.get("ws", 0x100000), kw.get("ws_bytes", ws), None]
+                         kw.get("sel", 0xD0000), kw.get("so", 0), kw.get("ws", 0x100000), kw.get("ws_bytes", ws),
+                         None]
     assert f(*args(b=257)) == INVALID and "b 257" in _err()
     assert f(*args(keep=None)) == INVALID and "keep_rows" in _err()
     assert f(*args(n_seq=3)) == INVALID and "divide" in _err()
@@ -251,4 +252,6 @@ def test_prefill_select_validation():
     assert f(*args(sel=None)) == INVALID
     assert f(*args(ws_bytes=ws - 1)) == WS_SMALL
     assert f(*args(pool=_pool(d=96))) == UNSUPPORTED
+    assert f(*args(so=2)) == INVALID and "selected_only" in _err()
+    assert f(*args(so=1, cs=None, k_max=0)) == INVALID and "chunk_score" in _err()
     assert f(*args(n=0, n_seq=1, k_max=0)) == OK        # nothing to do, nothing enqueued

@@ -80,3 +80,52 @@ def test_fused_with_many_sequences(device):
     say("prefill_select, 70 sequences")
     inp, sep, fused, b, ks, k_max = _both(cfg, 2)
     _check(cfg, sep, fused, inp, b, ks, k_max, what="70 sequences")
+
+
+SELECTED = [
+    ("s32", synth.config("s32"), None),
+    ("two_seq_partial", synth.Config("p", 28, 4, 128, "bf16", 6, 256, (3, 5), 100, 64, 64, n_seq=2, last_chunk=50),
+     "rows"),
+    ("k0", synth.Config("p", 14, 2, 64, "bf16", 4, 64, (0,), 20, 32, 32), None),
+    ("c512", synth.Config("p", 14, 2, 128, "bf16", 4, 512, (2,), 200, 64, 64), None),
+    ("tiny_f32", synth.config("tiny"), None),
+    ("70_seq", synth.Config("p", 4, 2, 64, "bf16", 3, 32, tuple([1, 2, 3, 0] * 17 + [2, 1]), 8, 16, 16, n_seq=70),
+     None),
+]
+
+
+@pytest.mark.parametrize("name,cfg,rows_kind", SELECTED, ids=[c[0] for c in SELECTED])
+def test_selected_only(device, name, cfg, rows_kind):
+    """selected_only: the chunks top-K selects get the key scores and kept rows
+    of the full call bit for bit; the others' rows are not written (past 64
+    sequences every chunk is); o_chunk and sel_chunk equal the full call's."""
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    inp = synth.generate(cfg, 3, with_q_chunk=True)
+    rows = dev(cfg.chunk_rows) if rows_kind else None
+    pk, pv, slot = dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot)
+    qc, qw, cs = dev(inp.q_chunk), dev(inp.q_win), dev(inp.chunk_score)
+    say(f"selected_only {name}")
+    full = L.prefill_select(pk, pv, slot, qc, qw, cfg.n_chunks, cfg.scale, cfg.b, cs, cfg.k_per_seq, cfg.k_max,
+                            chunk_rows=rows)
+    ks_m = torch.full((cfg.n_slots, cfg.rows), -7.0, dtype=torch.float32, device=qc.device)
+    keep_m = torch.full((cfg.n_slots, cfg.b), -9, dtype=torch.int32, device=qc.device)
+    part = L.prefill_select(pk, pv, slot, qc, qw, cfg.n_chunks, cfg.scale, cfg.b, cs, cfg.k_per_seq, cfg.k_max,
+                            chunk_rows=rows, key_score=ks_m, keep_rows=keep_m, selected_only=True)
+    torch.cuda.synchronize()
+    sel = oracle.select_topk(inp.chunk_score, cfg.k_per_seq, cfg.k_max)
+    picked = np.zeros(cfg.n_slots, dtype=bool)
+    for s in range(cfg.n_seq):
+        for c in sel[s, :cfg.k_per_seq[s]]:
+            picked[s * cfg.n_chunks + c] = True
+    if cfg.n_seq > 64:
+        picked[:] = True                    # past 64 sequences every chunk is scored
+    pk_t = torch.from_numpy(picked).to(qc.device)
+    valid = np.arange(cfg.rows)[None, :] < cfg.chunk_rows[:, None]
+    valid_t = torch.from_numpy(valid).to(qc.device)
+    assert torch.equal(full[0][valid_t], part[0][valid_t]), "o_chunk"
+    assert torch.equal(full[1][pk_t], part[1][pk_t]), "key_score of selected chunks"
+    assert torch.equal(full[2][pk_t], part[2][pk_t]), "keep_rows of selected chunks"
+    assert torch.equal(full[3], part[3]), "sel_chunk"
+    assert (part[1][~pk_t] == -7.0).all() and (part[2][~pk_t] == -9).all(), "unselected chunks were written"
+    assert picked.any() or cfg.k_max == 0
