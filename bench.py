@@ -66,20 +66,20 @@ STAGE_KERNELS = {
     "prefill": "prefill_bf16_kernel<128, 18> + score_finalize_kernel",
     "select_topb": "topb_kernel",
     "select_topk": "topk_kernel",
-    "decode": "decode_bf16_kernel<128, *> + lse_merge_kernel<128, bf16>",
+    "decode": "decode_bf16_kernel<128, *> + lse_merge_kernel<128, bf16, *>",
 }
 
 # rocprofv3 counter readings (KiB per dispatch, mean over the dispatches of
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "177bb851a0e9f843",
+    "sources_sha": "b552437856578168",
+    # the default step (only the kept chunks scored); other forms get no traffic figure
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149208.66, "write_kib": 234605.73},
-        "finalize_select_kernel": {"fetch_kib": 2101.31, "write_kib": 260.06},
-        "score_finalize_kernel": {"fetch_kib": 2551.44, "write_kib": 128.5},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149401.95, "write_kib": 231163.51},
+        "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56},
     },
-    "copy_fetch_kib": 524301.28,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.22,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 
@@ -648,7 +648,8 @@ def main():
     step_flops = sum(flops[n] for n in names)
     value = step_flops / (step_ms * 1e-3) / 1e12
 
-    traffic = {"prefill": prefill_traffic(False), "prefill_select": prefill_traffic(True)}
+    traffic = {"prefill_select": prefill_traffic(True) if not args.score_all else None,
+               "prefill": prefill_traffic(False)}
 
     peaks = measured_peaks()
 
