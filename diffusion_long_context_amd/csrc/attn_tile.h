@@ -104,13 +104,15 @@ struct WaveAttn {
   // The softmax and PV of one block come in three parts, so that a caller can
   // interleave the S^T MFMAs of the next block with this block's exp work.
   //
-  // (1) Mask, row max and the lazy rescale (the only branches).  Only rows in
-  // [valid_lo, valid_hi) whose bit in `absent` is clear count; the rest are
-  // masked (a wave-uniform branch, taken only by a partial block or one with
-  // absent rows).  valid_hi must be >= valid_lo.
+  // (1) Mask, row max and the lazy rescale (the only branches), in two
+  // parts so that a caller can compute a block's max ahead of its rescale.
+  // Only rows in [valid_lo, valid_hi) whose bit in `absent` is clear count;
+  // the rest are masked (a wave-uniform branch, taken only by a partial block
+  // or one with absent rows).  valid_hi must be >= valid_lo.
+  // (1a) Mask in place; returns the block's row max, scaled (log2 units).
   template <int NK>
-  __device__ __forceinline__ void prep(f32x16 (&sc)[NK], float sl2, int valid_hi, int j,
-                                       int valid_lo = 0, uint64_t absent = 0) {
+  __device__ __forceinline__ float block_max(f32x16 (&sc)[NK], float sl2, int valid_hi, int j,
+                                             int valid_lo = 0, uint64_t absent = 0) const {
     if (__builtin_expect(valid_hi < 32 * NK || valid_lo > 0 || absent != 0, 0)) {
       // rows r valid iff valid_lo <= r < valid_hi, as one unsigned compare
       const unsigned span = (unsigned)(valid_hi - valid_lo);
@@ -129,8 +131,11 @@ struct WaveAttn {
     for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
       for (int i = kb ? 0 : 2; i < 16; i += 2) mx = max_f(max_f(mx, sc[kb][i]), sc[kb][i + 1]);
-    mx = max_halves(mx);
-    const float ms = mx * sl2;
+    return max_halves(mx) * sl2;
+  }
+
+  // (1b) The lazy rescale for a block whose scaled row max is ms.
+  __device__ __forceinline__ void rescale(float ms) {
     const bool need = ms > m_run + kRescaleLog2;
     if (__ballot(need)) {
       const float m_new = need ? ms : m_run;
@@ -140,6 +145,12 @@ struct WaveAttn {
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       l_run *= alpha;
     }
+  }
+
+  template <int NK>
+  __device__ __forceinline__ void prep(f32x16 (&sc)[NK], float sl2, int valid_hi, int j,
+                                       int valid_lo = 0, uint64_t absent = 0) {
+    rescale(block_max<NK>(sc, sl2, valid_hi, j, valid_lo, absent));
   }
 
   // (2) p = 2^(s * sl2 - m) in place, the row sums (float32, unrounded p)

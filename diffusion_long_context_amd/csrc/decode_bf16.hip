@@ -298,8 +298,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     __syncthreads();
     f32x16 sc_a[NK], sc_b[NK];
     at.template qk<NK>(sc_a, k_base, qf);
-    uint64_t am_a = 0, am_b = 0;             // absent masks of the tiles in sc_a / sc_b
-    if constexpr (ABS) am_a = uniform_u64(sm.kmask[0]);
+    uint64_t am0 = 0;                        // the absent mask of tile 0
+    if constexpr (ABS) am0 = uniform_u64(sm.kmask[0]);
+    // each tile's mask and scaled row max are taken one iteration ahead,
+    // after the previous tile's PV MFMAs (ms_a / ms_b go with sc_a / sc_b)
+    float ms_a = at.template block_max<NK>(sc_a, sl2, n_kv - t_begin * kTile, lj, 0, am0), ms_b = 0.f;
     __syncthreads();                         // K buffer 0 is rewritten in iteration 0
 
     // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     // Every iteration issues exactly one unit's loads, so the wait before a
     // store covers only loads issued STAGES iterations earlier.  One barrier
     // per tile.
-    auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], uint64_t am_cur, uint64_t& am_nxt) {
+    auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], float ms_cur, float& ms_nxt) {
       const int set = u % STAGES;
       if (u + 2 < n_loc) store_k(u & 1, set);
       if (u + 1 < n_loc) store_v((u + 1) & 1, set);
@@ -327,7 +330,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       }
       const int t = t_begin + u;
       bf16x8 pf[2 * NK];
-      at.template prep<NK>(cur, sl2, n_kv - t * kTile, lj, 0, am_cur);
+      at.rescale(ms_cur);
+      uint64_t am_nxt = 0;
       if (u + 1 < n_loc) {
         if constexpr (ABS) am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
         at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
@@ -335,6 +339,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
         at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
       }
       at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
+      if (u + 1 < n_loc) ms_nxt = at.template block_max<NK>(nxt, sl2, n_kv - (t + 1) * kTile, lj, 0, am_nxt);
       __syncthreads();
     };
     {
@@ -342,10 +347,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       // only after the second half's loads (exact wait counts before stores)
       int u = 0;
       for (; u + 1 < n_loc; u += 2) {
-        iter(u, sc_a, sc_b, am_a, am_b);
-        iter(u + 1, sc_b, sc_a, am_b, am_a);
+        iter(u, sc_a, sc_b, ms_a, ms_b);
+        iter(u + 1, sc_b, sc_a, ms_b, ms_a);
       }
-      if (u < n_loc) iter(u, sc_a, sc_b, am_a, am_b);
+      if (u < n_loc) iter(u, sc_a, sc_b, ms_a, ms_b);
     }
   };
   if (has_absent)
