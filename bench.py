@@ -73,10 +73,10 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "b552437856578168",
+    "sources_sha": "3e93cfedd53d0ccd",
     # the default step (only the kept chunks scored); other forms get no traffic figure
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149401.95, "write_kib": 231163.51},
+        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149387.80, "write_kib": 231279.85},
         "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56},
     },
     "copy_fetch_kib": 524301.22,      # __amd_rocclr_copyBuffer of COPY_BYTES
