@@ -697,6 +697,7 @@ def main():
         "rooflines": {n: roof(n) for n in names if flops[n] > 0},
         "measured_peaks": peaks,
         "wall_s": wall,
+        "inputs_sha256": inp.sha256(),     # the seeded inputs, as generated on the host
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
