@@ -231,6 +231,40 @@ struct WaveAttn {
     pv<NK>(pf, v_lane, min(2 * NK, (valid_hi + 15) >> 4));
   }
 
+  // One kv row j that is the only counted row of its 32-row block (the row
+  // past the last full block of a chunk of C + 1 rows).  Its scores come from
+  // VALU dot products instead of a 32-row S^T block whose other 31 rows would
+  // be masked: k_row = &K[j][8 lh] holds the d values of the lane's query
+  // fragments.  Then the lazy rescale, and the PV of one 16-row piece
+  // (v_lane as in pv, at row j) whose P fragment holds only row j (element 0
+  // of the lanes with lh = 0); the other 15 V rows get weight 0.  The row sum
+  // takes p once, in the lh = 0 half.
+  __device__ __forceinline__ void one_row(const uint16_t* __restrict__ k_row,
+                                          const uint16_t* __restrict__ v_lane, const bf16x8 (&qf)[DC],
+                                          float sl2, int lh) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float part[2] = {0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_row + 16 * dc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{qf[dc][2 * e], qf[dc][2 * e + 1]},
+                                                      bf16x2{kf[2 * e], kf[2 * e + 1]}, part[e & 1], false);
+      if (dc & 1) __builtin_amdgcn_sched_barrier(0);   // at most two K fragments live
+    }
+    const float s = sum_halves(part[0] + part[1]);
+    rescale(s * sl2);
+    const float p = __builtin_amdgcn_exp2f(fmaf(s, sl2, -m_run));
+    const float p0 = lh == 0 ? p : 0.f;
+    l_run += p0;
+    bf16x8 pf[2];
+    pf[0] = bf16x8{(__bf16)p0, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f,
+                   (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    pf[1] = pf[0];
+    pv<1>(pf, v_lane, 1);
+  }
+
   // Full row sum (both kv halves) and natural-log normaliser.
   __device__ __forceinline__ float row_sum() const { return sum_halves(l_run); }
   __device__ __forceinline__ float lse(float l) const { return m_run * kLn2 + logf(l); }

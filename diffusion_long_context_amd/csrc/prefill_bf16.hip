@@ -45,10 +45,12 @@ struct PSmem {
 };
 
 // NKB = 16-row kv blocks of the chunk padded to 32 rows (compile-time, so
-// every loop over keys is static).
-template <int D, int NKB>
+// every loop over keys is static).  ONE_ROW: the layout has a single row
+// past its last 64-row block (R = 64 (NKB / 4) + 1, as for R = C + 1).
+template <int D, int NKB, bool ONE_ROW>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillArgs a) {
   static_assert(NKB % 2 == 0 && NKB <= kMaxKb, "kv blocks");
+  static_assert(!ONE_ROW || NKB % 4 == 2, "a single row past the 64-row blocks");
   __shared__ PSmem<D> sm;
   constexpr int KP = PSmem<D>::KP, VP = PSmem<D>::VP;
   constexpr int DC = D / 32;               // 32-wide d chunks (16x16x32 MFMA)
@@ -155,16 +157,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     Attn at;
     at.init();
     // 64-row steps over rows [0, 64 (NKB / 4)), masked at Rc; when
-    // NKB % 4 == 2 the remaining 32 rows (R = C + 1 puts a single row there
-    // for C a multiple of 64) run as one 32-row step.  A step wholly past Rc
-    // (a partial chunk) is masked throughout.
+    // NKB % 4 == 2 the remaining rows run as one 32-row step, or, when the
+    // layout has a single row there (R = C + 1 for C a multiple of 64), as a
+    // one-row update.  A step wholly past Rc (a partial chunk) is masked
+    // throughout; a one-row update past Rc is skipped.
     constexpr int n_full = NKB / 4;
 #pragma unroll 1
     for (int st = 0; st < n_full; ++st)
       at.template step<2>(k_lane + st * 64 * KP, v_lane + st * 64 * VP, qf, sl2, max(Rc - st * 64, 0), lh);
     if constexpr (NKB % 4 == 2) {
       constexpr int kv0 = 64 * n_full;
-      at.template step<1>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, max(Rc - kv0, 0), lh);
+      if constexpr (ONE_ROW) {
+        if (Rc > kv0) at.one_row(&sm.k[kv0 * KP + 8 * lh], v_lane + kv0 * VP, qf, sl2, lh);
+      } else {
+        at.template step<1>(k_lane + kv0 * KP, v_lane + kv0 * VP, qf, sl2, max(Rc - kv0, 0), lh);
+      }
     }
     const float l = at.row_sum();
     const int x = row_of(item);
@@ -330,16 +337,28 @@ template <int D>
 int prefill_launch(const PrefillArgs& a, void* stream) {
   const dim3 grid(a.n_chunks * a.h_kv), block(kThreads);
   const hipStream_t st = (hipStream_t)stream;
+  // one row past the last 64-row block: the one-row tail instance
+  const bool one = a.slot_rows % 64 == 1;
   switch ((a.slot_rows + 31) / 32) {
-    case 1: hipLaunchKernelGGL((prefill_bf16_kernel<D, 2>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_bf16_kernel<D, 4>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((prefill_bf16_kernel<D, 6>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_bf16_kernel<D, 8>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((prefill_bf16_kernel<D, 10>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((prefill_bf16_kernel<D, 12>), grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((prefill_bf16_kernel<D, 14>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((prefill_bf16_kernel<D, 16>), grid, block, 0, st, a); break;
-    case 9: hipLaunchKernelGGL((prefill_bf16_kernel<D, 18>), grid, block, 0, st, a); break;
+    case 1: if (one) hipLaunchKernelGGL((prefill_bf16_kernel<D, 2, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, 2, false>), grid, block, 0, st, a);
+            break;
+    case 2: hipLaunchKernelGGL((prefill_bf16_kernel<D, 4, false>), grid, block, 0, st, a); break;
+    case 3: if (one) hipLaunchKernelGGL((prefill_bf16_kernel<D, 6, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, 6, false>), grid, block, 0, st, a);
+            break;
+    case 4: hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, false>), grid, block, 0, st, a); break;
+    case 5: if (one) hipLaunchKernelGGL((prefill_bf16_kernel<D, 10, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, 10, false>), grid, block, 0, st, a);
+            break;
+    case 6: hipLaunchKernelGGL((prefill_bf16_kernel<D, 12, false>), grid, block, 0, st, a); break;
+    case 7: if (one) hipLaunchKernelGGL((prefill_bf16_kernel<D, 14, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, 14, false>), grid, block, 0, st, a);
+            break;
+    case 8: hipLaunchKernelGGL((prefill_bf16_kernel<D, 16, false>), grid, block, 0, st, a); break;
+    case 9: if (one) hipLaunchKernelGGL((prefill_bf16_kernel<D, 18, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<D, 18, false>), grid, block, 0, st, a);
+            break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -51,6 +51,10 @@ SMALL = [
     ("g1_c8", dict(h_q=2, h_kv=2, d=128, n_chunks=6, chunk=8, w=3)),
     ("c100_w70", dict(h_q=7, h_kv=1, d=128, n_chunks=2, chunk=100, w=70)),
     ("f32_d32", dict(h_q=6, h_kv=3, d=32, dtype="f32", n_chunks=3, chunk=50, w=7)),
+    # one row past the last 64-row block (the one-row update), at d = 64
+    ("d64_c128_one_row", dict(h_q=4, h_kv=1, d=64, n_chunks=3, chunk=128, w=20)),
+    # 27 rows past the last 64-row block (a masked 32-row step)
+    ("c90_tail27", dict(h_q=7, h_kv=1, d=128, n_chunks=2, chunk=90, w=33)),
 ]
 
 
