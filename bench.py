@@ -62,8 +62,8 @@ PREFILL_SOURCES = ("diffusion_long_context_amd/csrc/prefill_bf16.hip",
 
 # Kernels each stage launches (one launch of each per step on this workload).
 STAGE_KERNELS = {
-    "prefill_select": "prefill_bf16_kernel<128, 18> + finalize_select_kernel",
-    "prefill": "prefill_bf16_kernel<128, 18> + score_finalize_kernel",
+    "prefill_select": "prefill_bf16_kernel<128, 18, true> + finalize_select_kernel",
+    "prefill": "prefill_bf16_kernel<128, 18, true> + score_finalize_kernel",
     "select_topb": "topb_kernel",
     "select_topk": "topk_kernel",
     "decode": "decode_bf16_kernel<128, *> + lse_merge_kernel<128, bf16, *>",
@@ -73,13 +73,13 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "3e93cfedd53d0ccd",
+    "sources_sha": "21d4ab4b300a23a1",
     # the default step (only the kept chunks scored); other forms get no traffic figure
     "kernels": {
-        "prefill_bf16_kernel<128, 18>": {"fetch_kib": 149387.80, "write_kib": 231279.85},
+        "prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149353.67, "write_kib": 231541.11},
         "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56},
     },
-    "copy_fetch_kib": 524301.22,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.12,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 
@@ -163,7 +163,7 @@ def prefill_traffic(fused: bool):
         return None
     f_read = COPY_BYTES / (rec["copy_fetch_kib"] * 1024.0)
     f_write = COPY_BYTES / (rec["copy_write_kib"] * 1024.0)
-    names = ["prefill_bf16_kernel<128, 18>", "finalize_select_kernel" if fused else "score_finalize_kernel"]
+    names = ["prefill_bf16_kernel<128, 18, true>", "finalize_select_kernel" if fused else "score_finalize_kernel"]
     if any(n not in rec["kernels"] for n in names):
         return None
     return sum(rec["kernels"][n]["fetch_kib"] * 1024.0 * f_read + rec["kernels"][n]["write_kib"] * 1024.0 * f_write
