@@ -231,14 +231,16 @@ struct WaveAttn {
     pv<NK>(pf, v_lane, min(2 * NK, (valid_hi + 15) >> 4));
   }
 
-  // One kv row j that is the only counted row of its 32-row block (the row
-  // past the last full block of a chunk of C + 1 rows).  Its scores come from
+  // One kv row j that is the only counted row of its block (the row past
+  // the last full block of a chunk of C + 1 rows).  Its scores come from
   // VALU dot products instead of a 32-row S^T block whose other 31 rows would
   // be masked: k_row = &K[j][8 lh] holds the d values of the lane's query
   // fragments.  Then the lazy rescale, and the PV of one 16-row piece
   // (v_lane as in pv, at row j) whose P fragment holds only row j (element 0
   // of the lanes with lh = 0); the other 15 V rows get weight 0.  The row sum
-  // takes p once, in the lh = 0 half.
+  // takes p once, in the lh = 0 half.  Without PV only the softmax statistics
+  // are updated (v_lane unused).
+  template <bool PV = true>
   __device__ __forceinline__ void one_row(const uint16_t* __restrict__ k_row,
                                           const uint16_t* __restrict__ v_lane, const bf16x8 (&qf)[DC],
                                           float sl2, int lh) {
@@ -258,11 +260,13 @@ struct WaveAttn {
     const float p = __builtin_amdgcn_exp2f(fmaf(s, sl2, -m_run));
     const float p0 = lh == 0 ? p : 0.f;
     l_run += p0;
-    bf16x8 pf[2];
-    pf[0] = bf16x8{(__bf16)p0, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f,
-                   (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-    pf[1] = pf[0];
-    pv<1>(pf, v_lane, 1);
+    if constexpr (PV) {
+      bf16x8 pf[2];
+      pf[0] = bf16x8{(__bf16)p0, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f,
+                     (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+      pf[1] = pf[0];
+      pv<1>(pf, v_lane, 1);
+    }
   }
 
   // Full row sum (both kv halves) and natural-log normaliser.

@@ -92,6 +92,10 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
   // clamped to the slot, rows clamped to its last row, so every load reads
   // valid data); the window pass has no V.
   const int n_tiles = (Rc + kTile - 1) / kTile;
+  // a last tile holding a single row (Rc = 64 k + 1, as for C + 1 rows) is a
+  // one-row update after the MFMA tiles, not a 64-row tile with 63 masked rows
+  const bool one_row = Rc % kTile == 1;
+  const int n_mt = one_row ? n_tiles - 1 : n_tiles;   // tiles through the MFMA loop
   const int ld_d0 = 8 * (tid % TPR);
   const int ld_r0 = RPT * (tid / TPR);
   u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
     load_unit(set, u + 4);
     bf16x8 pf[2 * NK];
     at.template prep<NK>(cur, sl2, Rc - u * kTile, lj);
-    if (u + 1 < n_tiles)
+    if (u + 1 < n_mt)
       at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
     else
       at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
@@ -167,12 +171,17 @@ __global__ __launch_bounds__(kThreads) void stream_attn_kernel(const PrefillArgs
   };
   {
     int u = 0;
-    for (; u + 1 < n_tiles; u += 2) {
+    for (; u + 1 < n_mt; u += 2) {
       iter(u, sc_a, sc_b);
       iter(u + 1, sc_b, sc_a);
     }
-    if (u < n_tiles) iter(u, sc_a, sc_b);
+    if (u < n_mt) iter(u, sc_a, sc_b);
   }
+  // the single-row tile n_mt: its K (and V) went to buffer n_mt & 1 in the
+  // prologue or in iterations n_mt - 2 (K) and n_mt - 1 (V), before the last
+  // barrier
+  if (one_row)
+    at.template one_row<!WIN>(&sm.k[n_mt & 1][8 * lj], v_base + (n_mt & 1) * (kTile * VP), qf, sl2, lj);
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
   const float l = at.row_sum();

@@ -52,6 +52,8 @@ PREFILL = [
     ("bf16_c64_last30", synth.Config("p", 8, 2, 128, "bf16", 4, 64, (2,), 32, 20, 17, last_chunk=30)),
     ("bf16_c512_last300", synth.Config("p", 14, 2, 128, "bf16", 2, 512, (2,), 128, 64, 64, last_chunk=300)),
     ("bf16_c1024_last17", synth.Config("p", 8, 2, 64, "bf16", 2, 1024, (2,), 128, 48, 48, last_chunk=17)),
+    # R_c = 129: a single row past the last 64-row tile of the partial chunk
+    ("bf16_c512_last128", synth.Config("p", 14, 2, 128, "bf16", 2, 512, (2,), 128, 40, 40, last_chunk=128)),
     ("f32_c64_last20", synth.Config("p", 2, 1, 64, "f32", 4, 64, (2,), 16, 32, 32, last_chunk=20)),
 ]
 
