@@ -73,13 +73,13 @@ STAGE_KERNELS = {
 # the run) of the prefill stage's kernels on this workload, and of the plain
 # copy; None until taken.  Filled from the summaries kept with the profiles.
 PREFILL_COUNTERS = {
-    "sources_sha": "21d4ab4b300a23a1",
+    "sources_sha": "56faf14e1edd9bc8",
     # the default step (only the kept chunks scored); other forms get no traffic figure
     "kernels": {
-        "prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149353.67, "write_kib": 231541.11},
+        "prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149365.95, "write_kib": 231490.18},
         "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56},
     },
-    "copy_fetch_kib": 524301.12,      # __amd_rocclr_copyBuffer of COPY_BYTES
+    "copy_fetch_kib": 524301.29,      # __amd_rocclr_copyBuffer of COPY_BYTES
     "copy_write_kib": 1048576.0,
 }
 
