@@ -36,11 +36,16 @@ class PageTable(ctypes.Structure):
                 ("b", ctypes.c_int32), ("rows_compacted", ctypes.c_int32)]
 
 
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("q_rows_per_wg", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
 EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_select_topB",
            "pdllm_select_topK", "pdllm_decode_plan", "pdllm_split_attn_decode_workspace",
            "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
            "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows",
-           "pdllm_prefill_select")
+           "pdllm_prefill_select", "pdllm_split_attn_decode_ex_workspace", "pdllm_split_attn_decode_ex")
 
 
 def _load() -> ctypes.CDLL:
@@ -70,6 +75,11 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_split_attn_decode.restype = ctypes.c_int
     lib.pdllm_split_attn_decode.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32,
                                             i32, vp, vp, vp, sz, vp]
+    lib.pdllm_split_attn_decode_ex_workspace.restype = sz
+    lib.pdllm_split_attn_decode_ex_workspace.argtypes = [P(Pool), P(PageTable), i32, i32, i32, P(DecodeOpts)]
+    lib.pdllm_split_attn_decode_ex.restype = ctypes.c_int
+    lib.pdllm_split_attn_decode_ex.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32,
+                                               P(DecodeOpts), vp, vp, vp, sz, vp]
     lib.pdllm_chunk_score_workspace.restype = sz
     lib.pdllm_chunk_score_workspace.argtypes = [i32, i32, i32]
     lib.pdllm_chunk_score.restype = ctypes.c_int
@@ -83,7 +93,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-ABI_VERSION = 7
+ABI_VERSION = 8
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -328,10 +338,13 @@ class Decode:
     [n_seq * N][b] table over a whole-chunk pool (-1 entries: absent rows of a
     partial chunk).  For a pool of compacted slots (pdllm_compact_kept_rows),
     whose kept rows are rows 1..b, pass ``compacted=True`` with ``keep_rows``
-    (read only for its -1 entries) or with keep_rows=None and ``b``."""
+    (read only for its -1 entries) or with keep_rows=None and ``b``.
+    ``q_rows_per_wg`` forces the workgroup shape (pdllm_decode_opts; 0 =
+    the planner's choice)."""
 
     def __init__(self, pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                 v_resp, scale, num_splits=0, want_lse=True, out=None, b=None, compacted=False):
+                 v_resp, scale, num_splits=0, want_lse=True, out=None, b=None, compacted=False,
+                 q_rows_per_wg=0):
         self.pool = make_pool(pool_k, pool_v)
         compacted = compacted or keep_rows is None
         no_table = keep_rows is None
@@ -360,27 +373,28 @@ class Decode:
         self.n_seq, self.l_d, self.h_q = n_seq, l_d, h_q
         self.scale = float(scale)
         self.num_splits = int(num_splits)
+        self.opts = DecodeOpts(int(num_splits), int(q_rows_per_wg))
         dev = q.device
         self.device = dev
         self.o = out if out is not None else torch.empty_like(q)
         self.lse = torch.empty((n_seq, h_q, l_d), dtype=torch.float32, device=dev) if want_lse else None
-        need = lib.pdllm_split_attn_decode_workspace(ctypes.byref(self.pool), ctypes.byref(self.pt),
-                                                     n_seq, l_d, h_q, self.num_splits)
+        need = lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(self.pool), ctypes.byref(self.pt),
+                                                        n_seq, l_d, h_q, ctypes.byref(self.opts))
         self.workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
 
     def __call__(self, stream: Optional[int] = None):
-        st = lib.pdllm_split_attn_decode(
+        st = lib.pdllm_split_attn_decode_ex(
             ctypes.byref(self.pool), ctypes.byref(self.pt), self._keep[3].data_ptr(),
             self._keep[4].data_ptr(), self._keep[5].data_ptr(), self.n_seq, self.l_d, self.h_q,
-            self.scale, self.num_splits, self.o.data_ptr(), _ptr(self.lse), self.workspace.data_ptr(),
+            self.scale, ctypes.byref(self.opts), self.o.data_ptr(), _ptr(self.lse), self.workspace.data_ptr(),
             self.workspace.numel(), _stream(self.device) if stream is None else stream)
-        _check(st, "pdllm_split_attn_decode")
+        _check(st, "pdllm_split_attn_decode_ex")
         return self.o, self.lse
 
 
 def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                      v_resp, scale, num_splits=0, want_lse=True, b=None, compacted=False):
+                      v_resp, scale, num_splits=0, want_lse=True, b=None, compacted=False, q_rows_per_wg=0):
     """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None).
     compacted=True (or keep_rows=None with ``b``) decodes over a pool of compacted slots."""
     return Decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp, v_resp,
-                  scale, num_splits, want_lse, b=b, compacted=compacted)()
+                  scale, num_splits, want_lse, b=b, compacted=compacted, q_rows_per_wg=q_rows_per_wg)()

@@ -164,17 +164,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     const int r = min(v - kk * per, per - 1);   // BOS row 0, then kept rows 1..b
     // the chunks this split's rows fall in (one per thread, clamped): any
     // with an absent row has -1 as its last kept-row entry
-    const bool tbl = a.b > 0 && a.keep_rows != nullptr;
+    const bool tbl = k_s > 0 && a.b > 0 && a.keep_rows != nullptr;
     const int k_lo = min(t_begin * kTile / per, max(k_s - 1, 0));
     const int k_hi = min((t_end * kTile - 1) / per, max(k_s - 1, 0));
     const int kx = min(k_lo + tid, k_hi);
-    const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : a.chunk_slot);
-    const int cx = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kx : a.chunk_slot);
+    // a sequence with no selected chunk reads only idx_dummy (valid device
+    // memory): its chunk_slot / sel_chunk may be NULL
+    const int32_t* dummy = a.idx_dummy;
+    const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : dummy);
+    const int cx = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kx : dummy);
     const int cg = s * a.n_chunks_per_seq + min(max(c0, 0), a.n_chunks_per_seq - 1);
     const int cgx = s * a.n_chunks_per_seq + min(max(cx, 0), a.n_chunks_per_seq - 1);
-    const int slot = *(gptr32)(a.chunk_slot + cg);
-    const int krow_ld = *(gptr32)(tbl ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0) : a.chunk_slot);
-    const int klast = *(gptr32)(tbl ? a.keep_rows + (int64_t)cgx * a.b + (a.b - 1) : a.chunk_slot);
+    const int slot = *(gptr32)(k_s > 0 ? a.chunk_slot + cg : dummy);
+    const int krow_ld = *(gptr32)(tbl ? a.keep_rows + (int64_t)cg * a.b + max(r - 1, 0) : dummy);
+    const int klast = *(gptr32)(tbl ? a.keep_rows + (int64_t)cgx * a.b + (a.b - 1) : dummy);
     // compacted slots: kept row i sits at row 1 + i; keep_rows, when given,
     // only marks absent rows (-1), which point at the BOS row
     const bool absent = r > 0 && a.keep_rows != nullptr && krow_ld < 0;
@@ -228,7 +231,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     // split, so a unit past its end re-reads valid rows that are never
     // stored).  STAGES staging register sets let a unit's loads be issued
     // STAGES iterations before its LDS store.
-    constexpr int STAGES = RPT <= 2 ? 2 : 1;
+    // The prologue fetches the row pointers of units up to 2 + STAGES
+    // without a refill check, so they must lie in the first table fill: the
+    // 4-wave table (4 tiles) allows one staging set only.
+    constexpr int STAGES = (RPT <= 2 && 2 + 2 < kTableTiles) ? 2 : 1;
+    static_assert(2 + STAGES < kTableTiles, "prologue units must lie in the first row table");
     const int ld_d0 = 8 * (tid % TPR);
     const int ld_r0 = RPT * (tid / TPR);
     const int n_loc = t_end - t_begin;

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "pdllm.h"
 #include "pdllm_internal.h"
@@ -109,6 +110,7 @@ pdllm::DecodeArgs base_decode_args(const pdllm_pool* pool, const pdllm_page_tabl
   a.chunk_slot = pt->chunk_slot;
   a.sel_chunk = pt->sel_chunk;
   a.keep_rows = pt->keep_rows;
+  a.idx_dummy = static_cast<const int32_t*>(q);   // any valid device memory of >= 16 bytes
   a.q = q;
   a.k_resp = k_resp;
   a.v_resp = v_resp;
@@ -158,6 +160,30 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
     if (pt->b > 0 && !pt->rows_compacted && pt->keep_rows == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
   }
+  return PDLLM_OK;
+}
+
+// Validation of a decode call's shapes and options, then its split plan.
+pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq, int32_t l_d,
+                       int32_t h_q, const pdllm_decode_opts* opts, pdllm::DecodePlan* plan) {
+  if (opts == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "decode options are NULL");
+  for (int r : opts->reserved)
+    if (r != 0) return fail(PDLLM_ERR_INVALID_ARG, "reserved decode option fields must be 0");
+  pdllm_status st = check_decode(pool, pt, n_seq, l_d, h_q, opts->num_splits);
+  if (st != PDLLM_OK) return st;
+  const int rows = opts->q_rows_per_wg;
+  if (rows != 0) {
+    const bool ok_rows = pool->dtype == PDLLM_BF16
+                             ? rows == pdllm::kDecodeRowsBf16Small || rows == pdllm::kDecodeRowsBf16Large
+                             : rows == pdllm::kDecodeRowsF32;
+    if (!ok_rows)
+      return fail(PDLLM_ERR_UNSUPPORTED, "q_rows_per_wg %d is not a workgroup shape of the %s kernel", rows,
+                  pool->dtype == PDLLM_BF16 ? "bf16 (128, 256)" : "f32 (64)");
+  }
+  const char* err = "";
+  if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
+                          opts->num_splits, rows, device_cu_count(), plan, &err))
+    return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
   return PDLLM_OK;
 }
 
@@ -438,7 +464,7 @@ pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t 
   if (dtype != PDLLM_F32 && dtype != PDLLM_BF16) return fail(PDLLM_ERR_INVALID_ARG, "bad dtype %d", dtype);
   pdllm::DecodePlan plan;
   const char* err = "";
-  if (!pdllm::plan_decode(k_per_seq, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, n_cu, &plan, &err))
+  if (!pdllm::plan_decode(k_per_seq, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, 0, n_cu, &plan, &err))
     return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
   for (int s = 0; s < n_seq; ++s) {
     if (splits_per_seq) splits_per_seq[s] = plan.splits[s];
@@ -449,37 +475,37 @@ pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t 
   return ok();
 }
 
-size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_page_table* pt,
-                                         int32_t n_seq, int32_t l_d, int32_t h_q,
-                                         int32_t num_splits) {
-  if (check_decode(pool, pt, n_seq, l_d, h_q, num_splits) != PDLLM_OK) return 0;
+size_t pdllm_split_attn_decode_ex_workspace(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                            int32_t n_seq, int32_t l_d, int32_t h_q,
+                                            const pdllm_decode_opts* opts) {
   pdllm::DecodePlan plan;
-  const char* err = "";
-  if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
-                          num_splits, device_cu_count(), &plan, &err))
-    return 0;
+  if (plan_call(pool, pt, n_seq, l_d, h_q, opts, &plan) != PDLLM_OK) return 0;
   return (size_t)plan.workspace_bytes;
 }
 
-pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
-                                     const void* q, const void* k_resp, const void* v_resp,
-                                     int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
-                                     int32_t num_splits, void* o, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
-  pdllm_status st = check_decode(pool, pt, n_seq, l_d, h_q, num_splits);
+size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                         int32_t n_seq, int32_t l_d, int32_t h_q,
+                                         int32_t num_splits) {
+  pdllm_decode_opts o{};
+  o.num_splits = num_splits;
+  return pdllm_split_attn_decode_ex_workspace(pool, pt, n_seq, l_d, h_q, &o);
+}
+
+pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                        const void* q, const void* k_resp, const void* v_resp,
+                                        int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                        const pdllm_decode_opts* opts, void* o, float* lse,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  pdllm::DecodePlan plan;
+  pdllm_status st = plan_call(pool, pt, n_seq, l_d, h_q, opts, &plan);
   if (st != PDLLM_OK) return st;
-  if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
   if ((st = check_tensor(q, "q")) != PDLLM_OK) return st;
   if ((st = check_tensor(k_resp, "k_resp")) != PDLLM_OK) return st;
   if ((st = check_tensor(v_resp, "v_resp")) != PDLLM_OK) return st;
   if ((st = check_tensor(o, "o")) != PDLLM_OK) return st;
   if (lse != nullptr && !aligned16(lse)) return fail(PDLLM_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-
-  pdllm::DecodePlan plan;
-  const char* err = "";
-  if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
-                          num_splits, device_cu_count(), &plan, &err))
-    return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
   if (plan.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < (size_t)plan.workspace_bytes)
       return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %lld bytes needed, %zu given",
@@ -487,6 +513,9 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
     if (!aligned16(workspace)) return fail(PDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
 
+  // Every launch's argument block is built and checked before the first one
+  // is enqueued: a status other than PDLLM_OK from here on can only come
+  // from the HIP runtime.
   pdllm::DecodeArgs a = base_decode_args(pool, pt, q, k_resp, v_resp, l_d, h_q, scale, o, lse);
   a.q_tiles = plan.q_tiles;
   if (plan.workspace_bytes > 0) {
@@ -494,6 +523,8 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
     const int64_t part_bytes = (plan.part_floats * plan.part_elem_bytes + 255) / 256 * 256;
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
   }
+  std::vector<pdllm::DecodeArgs> launches;
+  std::vector<bool> merges;
   for (int s0 = 0; s0 < n_seq; s0 += pdllm::kMaxSeqPerLaunch) {
     const int n_here = std::min(pdllm::kMaxSeqPerLaunch, n_seq - s0);
     a.seq0 = s0;
@@ -509,23 +540,39 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
       q_.n_kv = plan.n_kv[s];
       q_.n_splits = plan.splits[s];
       q_.tiles_per_split = plan.tiles_per_split[s];
-      q_.wg_begin = (int32_t)wg;
+      q_.wg_begin = (int32_t)std::min<int64_t>(wg, INT32_MAX);
       q_.part_off = plan.part_off[s];
       q_.lse_off = plan.lse_off[s];
       wg += (int64_t)pool->h_kv * plan.q_tiles * plan.splits[s];
       merge |= plan.splits[s] > 1;
     }
-    if (wg > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "decode grid too large");
+    if (wg > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "decode grid too large (%lld workgroups)", (long long)wg);
     a.total_wg = (int32_t)wg;
-    const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(a, pool->d, plan.q_rows_per_wg, stream)
-                                             : pdllm::launch_decode_f32(a, pool->d, stream);
+    launches.push_back(a);
+    merges.push_back(merge);
+  }
+  for (size_t i = 0; i < launches.size(); ++i) {
+    const pdllm::DecodeArgs& la = launches[i];
+    const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(la, pool->d, plan.q_rows_per_wg, stream)
+                                             : pdllm::launch_decode_f32(la, pool->d, stream);
     if ((st = hip_status(e, "decode launch")) != PDLLM_OK) return st;
-    if (merge) {
-      st = hip_status(pdllm::launch_lse_merge(a, pool->d, pool->dtype == PDLLM_BF16, stream), "merge launch");
+    if (merges[i]) {
+      st = hip_status(pdllm::launch_lse_merge(la, pool->d, pool->dtype == PDLLM_BF16, stream), "merge launch");
       if (st != PDLLM_OK) return st;
     }
   }
   return ok();
+}
+
+pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                     const void* q, const void* k_resp, const void* v_resp,
+                                     int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                     int32_t num_splits, void* o, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  pdllm_decode_opts opts{};
+  opts.num_splits = num_splits;
+  return pdllm_split_attn_decode_ex(pool, pt, q, k_resp, v_resp, n_seq, l_d, h_q, scale, &opts, o, lse,
+                                    workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -543,7 +590,8 @@ pdllm_status prepare_prefill(const pdllm_pool* pool, const int32_t* chunk_slot, 
     return fail(PDLLM_ERR_INVALID_ARG, "h_q %d must be a positive multiple of h_kv %d", h_q, pool->h_kv);
   if (w < 1 || chunks_per_win < 1)
     return fail(PDLLM_ERR_INVALID_ARG, "w and chunks_per_win must be >= 1 (got %d, %d)", w, chunks_per_win);
-  if (!std::isfinite(scale)) return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
   if (pool->slot_rows > 4097)
     return fail(PDLLM_ERR_UNSUPPORTED, "slot_rows %d > 4097 is not supported", pool->slot_rows);
   if (n_chunks == 0) return ok();

@@ -33,8 +33,10 @@ struct DecodePlan {
 };
 
 // Fills `plan`; returns false (with a message in *err) on invalid input.
+// force_rows > 0 fixes the query rows per workgroup (a shape of the dtype's
+// kernel, checked by the caller); 0 lets the planner choose.
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
-                 int d, int dtype, int num_splits, int n_cu, DecodePlan* plan,
+                 int d, int dtype, int num_splits, int force_rows, int n_cu, DecodePlan* plan,
                  const char** err);
 
 // ---------------------------------------------------------------- decode
@@ -56,6 +58,7 @@ struct DecodeArgs {
   const int32_t* chunk_slot;
   const int32_t* sel_chunk;
   const int32_t* keep_rows;
+  const int32_t* idx_dummy;  // valid device memory read in place of absent index tables
   const void* q;
   const void* k_resp;
   const void* v_resp;

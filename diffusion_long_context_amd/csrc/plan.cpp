@@ -35,7 +35,7 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
-                 int d, int dtype, int num_splits, int n_cu, DecodePlan* plan,
+                 int d, int dtype, int num_splits, int force_rows, int n_cu, DecodePlan* plan,
                  const char** err) {
   if (n_seq < 1 || l_d < 1 || h_q < 1 || h_kv < 1 || d < 1 || b < 0 || num_splits < 0 ||
       n_cu < 1 || h_q % h_kv != 0 || k_per_seq == nullptr || plan == nullptr) {
@@ -74,7 +74,15 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
                                 {kDecodeRowsBf16Small, kResidentBf16Small}};
   const Shape f32_shapes[1] = {{kDecodeRowsF32, kResidentF32}};
   const Shape* shapes = dtype == 1 ? bf16_shapes : f32_shapes;
-  const int n_shapes = dtype == 1 ? 2 : 1;
+  int n_shapes = dtype == 1 ? 2 : 1;
+  if (force_rows > 0) {          // a forced workgroup shape (the caller checked it exists)
+    for (int i = 0; i < n_shapes; ++i)
+      if (shapes[i].rows == force_rows) {
+        shapes += i;
+        break;
+      }
+    n_shapes = 1;
+  }
 
   p.splits.assign(n_seq, 1);
   p.tiles_per_split.assign(n_seq, 1);

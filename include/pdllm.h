@@ -17,15 +17,19 @@
  * - `stream` is a hipStream_t (NULL = the null stream).  All work is
  *   enqueued on it, nothing synchronises with the host, and no device memory
  *   is allocated, so the calls can be captured in a HIP graph.
- * - Arguments are validated on the host before anything is enqueued.  On any
- *   status other than PDLLM_OK nothing was enqueued and the outputs are
- *   untouched; pdllm_last_error() then describes the problem.  The library
- *   never aborts and never throws across this boundary.
+ * - Arguments are validated on the host before anything is enqueued.  On
+ *   PDLLM_ERR_INVALID_ARG, PDLLM_ERR_UNSUPPORTED and
+ *   PDLLM_ERR_WORKSPACE_TOO_SMALL nothing was enqueued and the outputs are
+ *   untouched.  PDLLM_ERR_HIP (the runtime refused a launch) can follow
+ *   earlier launches of the same call, so the outputs are then undefined.
+ *   pdllm_last_error() describes the problem.  The library never aborts and
+ *   never throws across this boundary.
  * - The contents of device index tables are trusted (chunk ids, slots and
  *   rows must be in range); their shapes are checked.
  * - Floating data is PDLLM_F32 (float) or PDLLM_BF16 (bfloat16 bits, round
  *   to nearest even on output).  Softmax, accumulation and merges run in
- *   float32.  The softmax scale is an explicit argument (usually 1/sqrt(d)).
+ *   float32.  The softmax scale is an explicit argument (usually 1/sqrt(d)):
+ *   it must be finite and > 0 (PDLLM_ERR_INVALID_ARG otherwise).
  * - Grouped-query attention: query head h reads KV head h / G with
  *   G = h_q / h_kv, i.e. G consecutive query heads share one KV head.
  * - Tensors are row-major with the last index contiguous.  Pool tensors
@@ -43,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 7
+#define PDLLM_ABI_VERSION 8
 
 typedef enum {
   PDLLM_OK = 0,
@@ -87,8 +91,14 @@ typedef struct {
  *   keep_rows   device [n_seq * n_chunks_per_seq][b]   kept content rows
  *                      (1..C) of every chunk, as written by pdllm_select_topB;
  *                      an entry of -1 is an absent row (a partial last chunk
- *                      with fewer than b content rows) and is not attended
+ *                      with fewer than b content rows) and is not attended.
+ *                      Absent entries must come after every kept row of
+ *                      their chunk's row (pdllm_select_topB writes them so):
+ *                      the decode finds a chunk's absent rows by its last
+ *                      entry
  *   k_per_seq   host   [n_seq]   K_s, 0 <= K_s <= k_max
+ *   (chunk_slot, sel_chunk and keep_rows may be NULL when every K_s is 0:
+ *   they are then not read)
  *   rows_compacted  0: the pool holds whole chunks and keep_rows names the
  *                      kept rows;  1: the pool holds compacted slots (the
  *                      layout pdllm_compact_kept_rows writes), whose kept
@@ -185,7 +195,8 @@ pdllm_status pdllm_select_topB(const float* key_score, const int32_t* chunk_rows
  *   k_per_seq   host   [n_seq]  0 <= K_s <= k_max <= n_chunks
  *   sel_chunk   device [n_seq][k_max] int32 out: the K_s best chunk ids in
  *               ascending order, then -1 up to k_max.
- * Same order and ties as pdllm_select_topB.  n_chunks <= 65536.
+ * Same order and ties as pdllm_select_topB.  1 <= n_chunks <= 8192
+ * (PDLLM_ERR_UNSUPPORTED above).
  */
 pdllm_status pdllm_select_topK(const float* chunk_score, int32_t n_seq, int32_t n_chunks,
                                const int32_t* k_per_seq, int32_t k_max, int32_t* sel_chunk,
@@ -338,6 +349,36 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
                                      int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
                                      int32_t num_splits, void* o, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Options of a decode call.  Zero-initialise the struct: every field's 0 is
+ * the library's choice.
+ *   num_splits     as pdllm_split_attn_decode's (0 = planner)
+ *   q_rows_per_wg  0 = planner; otherwise the query rows (token x grouped
+ *                  head) of one workgroup, a shape of the dtype's kernel:
+ *                  128 or 256 for bf16, 64 for f32 (PDLLM_ERR_UNSUPPORTED
+ *                  for any other).  The result does not depend on it beyond
+ *                  rounding; tests use it to run every kernel instance.
+ */
+typedef struct {
+  int32_t num_splits;
+  int32_t q_rows_per_wg;
+  int32_t reserved[6];              /* must be 0 */
+} pdllm_decode_opts;
+
+/* pdllm_split_attn_decode_workspace with options (0 when invalid). */
+size_t pdllm_split_attn_decode_ex_workspace(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                            int32_t n_seq, int32_t l_d, int32_t h_q,
+                                            const pdllm_decode_opts* opts);
+
+/* pdllm_split_attn_decode with options (same operation, arguments and
+ * errors; opts must not be NULL).  pdllm_split_attn_decode(..., num_splits,
+ * ...) is this call with opts = {num_splits, 0}. */
+pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                        const void* q, const void* k_resp, const void* v_resp,
+                                        int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                        const pdllm_decode_opts* opts, void* o, float* lse,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 

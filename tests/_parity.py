@@ -4,12 +4,11 @@ error metrics, and the tolerances every comparison uses.
 Tolerances:
   bf16 outputs       rel-L2 <= 5e-3 and max-abs <= 2e-2 over the tensor
   f32 outputs        rel-L2 <= 1e-5 and max-abs <= 1e-5
-  lse                max-abs <= 2e-3 (bf16 inputs), 1e-5 (f32 inputs).  The bound
-                     allows a kernel to normalise with the row sum of the
-                     bf16-rounded probabilities it feeds to the PV product:
-                     rounding each p to bf16 moves that sum by at most a factor
-                     (1 +- 2^-9), so |d lse| <= ln(1 + 2^-9) = 1.95e-3.  (The
-                     current kernels sum the unrounded float32 probabilities.)
+  lse                max-abs <= 1e-3 (bf16 inputs), 1e-5 (f32 inputs).  The kernels
+                     take the scores from exact bf16 products summed in float32
+                     and normalise with float32 sums of the unrounded
+                     probabilities, so lse carries only float32 rounding
+                     (about 1e-6 relative on values of order 10).
   key_score          rel-L2 <= 1e-4 (bf16 inputs), 1e-6 (f32 inputs)
   selected indices   bit-exact
 """
@@ -19,7 +18,7 @@ import numpy as np
 import torch
 
 TOL = {
-    "bf16": dict(rel_l2=5e-3, max_abs=2e-2, lse=2e-3, score_rel_l2=1e-4),
+    "bf16": dict(rel_l2=5e-3, max_abs=2e-2, lse=1e-3, score_rel_l2=1e-4),
     "f32": dict(rel_l2=1e-5, max_abs=1e-5, lse=1e-5, score_rel_l2=1e-6),
 }
 

@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 7
+    assert L.lib.pdllm_abi_version() == 8
 
 
 def _pool(**kw):
@@ -95,6 +95,9 @@ def _err():
     (dict(q=0), INVALID, "q is NULL"),
     (dict(o=0x90004), INVALID, "aligned"),
     (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(scale=0.0), INVALID, "scale"),
+    (dict(scale=-0.088), INVALID, "scale"),
+    (dict(scale=float("inf")), INVALID, "scale"),
     (dict(splits=-1), INVALID, "num_splits"),
     (dict(keep_rows=None), INVALID, "keep_rows is NULL"),
     (dict(rows_compacted=2), INVALID, "rows_compacted"),
@@ -110,6 +113,57 @@ def test_decode_validation(mutate, code, msg):
     st = _decode(pool, pt, **call)
     assert st == code, _err()
     assert msg in _err()
+
+
+def test_decode_null_tables_when_no_chunk_is_selected():
+    """With every K_s = 0 the index tables are not read, so NULL is accepted
+    (validation passes and stops at the workspace check); with any K_s > 0
+    NULL chunk_slot / sel_chunk is rejected."""
+    pool = _pool()
+    pt, _keep = _pt([0, 0], chunk_slot=None, sel_chunk=None, keep_rows=None)
+    assert _decode(pool, pt, n_seq=2) == WS_SMALL, _err()
+    pt, _keep = _pt([0, 3], chunk_slot=None, sel_chunk=None, keep_rows=None)
+    assert _decode(pool, pt, n_seq=2) == INVALID and "chunk_slot" in _err()
+
+
+def _decode_ex(pool, pt, opts, ws=None, ws_bytes=0):
+    return L.lib.pdllm_split_attn_decode_ex(ctypes.byref(pool), ctypes.byref(pt), 0x60000, 0x70000, 0x80000,
+                                            1, 256, 28, 0.088, ctypes.byref(opts) if opts is not None else None,
+                                            0x90000, None, ws, ws_bytes, None)
+
+
+def test_decode_options_validation():
+    pool = _pool()
+    pt, _keep = _pt([16])
+    assert _decode_ex(pool, pt, None) == INVALID and "options" in _err()
+    assert _decode_ex(pool, pt, L.DecodeOpts(0, 96)) == UNSUPPORTED and "q_rows_per_wg" in _err()
+    assert _decode_ex(pool, pt, L.DecodeOpts(0, 64)) == UNSUPPORTED          # the f32 kernel's shape
+    bad = L.DecodeOpts(0, 0)
+    bad.reserved[3] = 1
+    assert _decode_ex(pool, pt, bad) == INVALID and "reserved" in _err()
+    for rows in (0, 128, 256):
+        opts = L.DecodeOpts(0, rows)
+        need = L.lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(pool), ctypes.byref(pt), 1, 256, 28,
+                                                          ctypes.byref(opts))
+        assert need > 0
+        assert _decode_ex(pool, pt, opts, 0x100000, need - 1) == WS_SMALL
+    f32 = _pool(dtype=0)
+    assert _decode_ex(f32, pt, L.DecodeOpts(0, 128)) == UNSUPPORTED
+    assert _decode_ex(f32, pt, L.DecodeOpts(0, 64)) == WS_SMALL
+
+
+def test_decode_forced_shape_plans():
+    """q_rows_per_wg fixes the planner's workgroup shape; the plain call's
+    workspace equals the options call's with the same split count."""
+    pool = _pool()
+    pt, _keep = _pt([16])
+    q = lambda rows, ns: L.lib.pdllm_split_attn_decode_ex_workspace(
+        ctypes.byref(pool), ctypes.byref(pt), 1, 256, 28, ctypes.byref(L.DecodeOpts(ns, rows)))
+    for ns in (0, 3):
+        assert q(0, ns) == L.lib.pdllm_split_attn_decode_workspace(ctypes.byref(pool), ctypes.byref(pt), 1, 256,
+                                                                   28, ns)
+    # forced split counts: the workspace does not depend on the workgroup shape
+    assert q(128, 5) == q(256, 5) == q(0, 5)
 
 
 def test_decode_workspace_query_matches_plan():
@@ -142,6 +196,10 @@ def test_prefill_validation():
                    ws_bytes=ws(128, 28, 4, 1025, 64) - 1)) == WS_SMALL
     assert f(*args(pool=_pool(slot_rows=4098, stride_slot=4098 * 512))) == UNSUPPORTED
     assert f(*args(n=0)) == OK                       # nothing to do, nothing enqueued
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        a = args()
+        a[9] = bad
+        assert f(*a) == INVALID and "scale" in _err()
 
 
 def test_select_validation():

@@ -160,3 +160,94 @@ def test_rerun_is_bitwise_identical(device):
     a, la = _run_gpu(inp, sel, keep, cfg, 0)
     b, lb = _run_gpu(inp, sel, keep, cfg, 0)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_many_sequences_take_several_launches(device):
+    """More sequences than one launch carries (16): the later launches
+    address their sequences and split partials by offset.  Mixed K_s,
+    including 0 and N, through the planner and a forced split count."""
+    ks = tuple((3 * s) % 7 for s in range(20))           # 0 .. 6 chunks of 6
+    cfg = synth.Config("seq20", 14, 2, 128, "bf16", 6, 40, ks, 17, 24, 8, n_seq=20)
+    inp = synth.generate(cfg, 4)
+    sel, keep = synth.random_page_table(cfg, 4)
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    for ns in (0, 3):
+        say(f"20 sequences, num_splits={ns}")
+        o, lse = _run_gpu(inp, sel, keep, cfg, ns)
+        _compare(o, lse, ro, rlse, cfg, f"20 sequences splits {ns}")
+
+
+FORCED = [(d, rows) for d in (64, 128) for rows in (128, 256)]
+
+
+@pytest.mark.parametrize("d,rows", FORCED, ids=[f"d{d}_rows{r}" for d, r in FORCED])
+def test_forced_workgroup_shapes(device, d, rows):
+    """Every bf16 kernel instance (4- and 8-wave workgroups, d = 64 and 128)
+    on splits of many tiles: one split of 14 tiles and two of 7 refill the
+    row table (4 tiles for 4-wave workgroups, 8 for 8-wave), and the last
+    chunk is partial, so a split holds absent rows."""
+    from diffusion_long_context_amd import _lib as L
+    import torch
+    cfg = synth.Config("forced", 14, 2, d, "bf16", 8, 100, (8,), 100, 40, 8, last_chunk=60)
+    inp = synth.generate(cfg, 6)
+    sel, keep = synth.random_page_table(cfg, 6)
+    assert (keep == -1).any()
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    for ns in (1, 2, 5):
+        say(f"d={d} rows={rows} num_splits={ns}")
+        call = L.Decode(dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot), dev(sel), dev(keep),
+                        cfg.k_per_seq, dev(inp.q), dev(inp.k_resp), dev(inp.v_resp), cfg.scale,
+                        num_splits=ns, q_rows_per_wg=rows)
+        o, lse = call()
+        torch.cuda.synchronize()
+        _compare(host(o), host(lse), ro, rlse, cfg, f"d={d} rows={rows} splits {ns}")
+
+
+def test_planner_picks_small_workgroups_d64(device):
+    """A shape where the planner itself picks 128-row workgroups at d = 64
+    with 14 tiles per split (48/8 heads, L_d = 64, B = 128, K = 32, 4
+    sequences)."""
+    from diffusion_long_context_amd import _lib as L
+    cfg = synth.Config("d64_auto", 48, 8, 64, "bf16", 32, 128, (32, 32, 32, 32), 128, 64, 8, n_seq=4)
+    splits, tps, _, rows = L.decode_plan(cfg.k_per_seq, cfg.b, cfg.l_d, cfg.h_q, cfg.h_kv, cfg.d, 1,
+                                         with_rows=True)
+    say(f"d64 auto plan: rows {rows}, splits {splits}, tiles per split {tps}")
+    inp = synth.generate(cfg, 7)
+    sel, keep = synth.random_page_table(cfg, 7)
+    heads = [0, 5, 6, 23, 47]
+    ro, rlse = _oracle(inp, sel, keep, cfg, heads=heads)
+    o, lse = _run_gpu(inp, sel, keep, cfg, 0)
+    _compare(o, lse, ro, rlse, cfg, "d64 auto plan", heads=heads)
+
+
+def test_no_chunk_selected_with_null_tables(device):
+    """Every K_s = 0: the decode is attention over the response rows alone,
+    and chunk_slot, sel_chunk and keep_rows may be NULL."""
+    import ctypes
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    cfg = synth.Config("k0null", 28, 4, 128, "bf16", 3, 64, (0, 0), 8, 70, 8, n_seq=2)
+    inp = synth.generate(cfg, 8)
+    sel = np.zeros((2, 0), np.int32)
+    keep = np.zeros((cfg.n_slots, cfg.b), np.int32)
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    pool_k, pool_v = dev(inp.pool_k), dev(inp.pool_v)
+    q, kr, vr = dev(inp.q), dev(inp.k_resp), dev(inp.v_resp)
+    pool = L.make_pool(pool_k, pool_v)
+    ks = (ctypes.c_int32 * 2)(0, 0)
+    pt = L.PageTable(None, None, None, ctypes.cast(ks, ctypes.c_void_p), cfg.n_chunks, 0, cfg.b, 0)
+    for ns in (0, 1, 2):
+        opts = L.DecodeOpts(ns, 0)
+        need = L.lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(pool), ctypes.byref(pt), 2, cfg.l_d,
+                                                          cfg.h_q, ctypes.byref(opts))
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((2, cfg.h_q, cfg.l_d), dtype=torch.float32, device=q.device)
+        say(f"K=0 with NULL index tables, num_splits={ns}")
+        st = L.lib.pdllm_split_attn_decode_ex(ctypes.byref(pool), ctypes.byref(pt), q.data_ptr(), kr.data_ptr(),
+                                              vr.data_ptr(), 2, cfg.l_d, cfg.h_q, cfg.scale, ctypes.byref(opts),
+                                              o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                                              torch.cuda.current_stream().cuda_stream)
+        assert st == 0, L.lib.pdllm_last_error()
+        torch.cuda.synchronize()
+        _compare(host(o), host(lse), ro, rlse, cfg, f"K=0 NULL tables splits {ns}")

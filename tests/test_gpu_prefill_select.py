@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from _parity import dev, say
+from _parity import TOL, assert_close, dev, host, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +129,78 @@ def test_selected_only(device, name, cfg, rows_kind):
     assert torch.equal(full[3], part[3]), "sel_chunk"
     assert (part[1][~pk_t] == -7.0).all() and (part[2][~pk_t] == -9).all(), "unselected chunks were written"
     assert picked.any() or cfg.k_max == 0
+
+
+def _e2e_selection(cfg, chunks, ks_gpu, keep_gpu, rks, what):
+    """End-to-end selection: the GPU's top-B rows (from its float32 key
+    scores) against the oracle's top-B from its float64 scores, exact at
+    every chunk whose fp64 cut gap |s_(B) - s_(B+1)| exceeds four times that
+    chunk's largest score error; near-tie chunks are reported, not failed."""
+    near = []
+    for n, c in enumerate(chunks):
+        err = float(np.abs(ks_gpu[c].astype(np.float64) - rks[n]).max())
+        ref = oracle.select_topb(rks[n:n + 1], cfg.b)[0]
+        srt = np.sort(rks[n, 1:])[::-1]
+        gap = srt[cfg.b - 1] - srt[cfg.b] if cfg.b < cfg.chunk else np.inf
+        if gap > 4 * err:
+            assert np.array_equal(keep_gpu[c], ref), f"{what}: chunk {c} selection differs from the fp64 oracle's"
+        else:
+            near.append((c, gap, err))
+    say(f"  {what}: {len(chunks)} chunks checked end to end, near ties: {near}")
+
+
+SEL_E2E = [("s32", synth.config("s32"), 0), ("s8", synth.config("s8"), 0), ("f32", synth.config("f32"), 0)]
+
+
+@pytest.mark.parametrize("name,cfg,seed", SEL_E2E, ids=[c[0] for c in SEL_E2E])
+def test_selected_only_against_oracle(device, name, cfg, seed):
+    """The benched form of the prefill side, pdllm_prefill_select with
+    selected_only, compared with the oracle directly: o_chunk on sampled
+    chunks (kept and not kept), the key scores of every kept chunk, top-K,
+    top-B on the GPU's own scores (bit-exact) and against the fp64 scores
+    (end to end, exact outside near ties).  S8 and F32 keep B = 128 < C."""
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    say(f"selected_only vs oracle {name}: generating")
+    inp = synth.generate(cfg, seed, with_q_chunk=True)
+    pk, pv, slot = dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot)
+    qc, qw, cs = dev(inp.q_chunk), dev(inp.q_win), dev(inp.chunk_score)
+    say(f"selected_only vs oracle {name}: gpu")
+    o, ks, keep, sel = L.prefill_select(pk, pv, slot, qc, qw, cfg.n_chunks, cfg.scale, cfg.b, cs, cfg.k_per_seq,
+                                        cfg.k_max, selected_only=True)
+    torch.cuda.synchronize()
+    sel_h = sel.cpu().numpy()
+    assert np.array_equal(sel_h, oracle.select_topk(inp.chunk_score, cfg.k_per_seq, cfg.k_max)), "top-K"
+    kept = sorted(int(c) for c in sel_h[0, :cfg.k_per_seq[0]])
+    say(f"selected_only vs oracle {name}: oracle on the {len(kept)} kept chunks")
+    ro, rks = oracle.chunk_prefill_score(inp.pool_k, inp.pool_v, inp.chunk_slot, inp.q_chunk, inp.q_win,
+                                         cfg.n_chunks, cfg.scale, chunks=kept)
+    ks_h, keep_h, o_h = ks.cpu().numpy(), keep.cpu().numpy(), host(o)
+    r = rel_l2(ks_h[kept], rks)
+    assert r <= TOL["bf16"]["score_rel_l2"], f"{name}: key_score rel-L2 {r:.2e}"
+    assert_close(o_h[kept], ro, "bf16", f"{name}: o_chunk of kept chunks")
+    assert np.array_equal(keep_h[kept], oracle.select_topb(ks_h[kept], cfg.b)), "top-B on the GPU's scores"
+    _e2e_selection(cfg, kept, ks_h, keep_h, rks, f"{name} selected_only")
+    others = [c for c in (0, cfg.n_chunks // 2, cfg.n_chunks - 1) if c not in kept][:2]
+    ro2, _ = oracle.chunk_prefill_score(inp.pool_k, inp.pool_v, inp.chunk_slot, inp.q_chunk, inp.q_win,
+                                        cfg.n_chunks, cfg.scale, chunks=others)
+    assert_close(o_h[others], ro2, "bf16", f"{name}: o_chunk of chunks not kept")
+
+
+def test_all_chunks_scored_end_to_end_s8(device):
+    """Every chunk scored (selected_only = 0) at S8: all 32 chunks' top-B
+    rows against the fp64 oracle's, end to end."""
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    cfg = synth.config("s8")
+    inp = synth.generate(cfg, 1, with_q_chunk=True)
+    _, ks, keep, _ = L.prefill_select(dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot), dev(inp.q_chunk),
+                                      dev(inp.q_win), cfg.n_chunks, cfg.scale, cfg.b, dev(inp.chunk_score),
+                                      cfg.k_per_seq, cfg.k_max)
+    torch.cuda.synchronize()
+    say("s8 all chunks: oracle")
+    _, rks = oracle.chunk_prefill_score(inp.pool_k, inp.pool_v, inp.chunk_slot, inp.q_chunk, inp.q_win,
+                                        cfg.n_chunks, cfg.scale)
+    ks_h, keep_h = ks.cpu().numpy(), keep.cpu().numpy()
+    assert rel_l2(ks_h, rks) <= TOL["bf16"]["score_rel_l2"]
+    _e2e_selection(cfg, list(range(cfg.n_slots)), ks_h, keep_h, rks, "s8 all chunks")
