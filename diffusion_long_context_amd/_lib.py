@@ -45,7 +45,8 @@ EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_
            "pdllm_select_topK", "pdllm_decode_plan", "pdllm_split_attn_decode_workspace",
            "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
            "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows",
-           "pdllm_prefill_select", "pdllm_split_attn_decode_ex_workspace", "pdllm_split_attn_decode_ex")
+           "pdllm_prefill_select", "pdllm_split_attn_decode_ex_workspace", "pdllm_split_attn_decode_ex",
+           "pdllm_split_attn_decode_noalloc")
 
 
 def _load() -> ctypes.CDLL:
@@ -80,6 +81,9 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_split_attn_decode_ex.restype = ctypes.c_int
     lib.pdllm_split_attn_decode_ex.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32,
                                                P(DecodeOpts), vp, vp, vp, sz, vp]
+    lib.pdllm_split_attn_decode_noalloc.restype = ctypes.c_int
+    lib.pdllm_split_attn_decode_noalloc.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32, i32,
+                                                    vp, vp, vp]
     lib.pdllm_chunk_score_workspace.restype = sz
     lib.pdllm_chunk_score_workspace.argtypes = [i32, i32, i32]
     lib.pdllm_chunk_score.restype = ctypes.c_int

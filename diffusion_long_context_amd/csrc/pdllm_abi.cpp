@@ -15,6 +15,8 @@
 #include "pdllm.h"
 #include "pdllm_internal.h"
 
+static_assert(pdllm::kNoAllocScratchBytes == PDLLM_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -160,6 +162,20 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
     if (pt->b > 0 && !pt->rows_compacted && pt->keep_rows == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
   }
+  return PDLLM_OK;
+}
+
+// Validation of a decode call's scale and tensor pointers.
+pdllm_status check_decode_io(float scale, const void* q, const void* k_resp, const void* v_resp, const void* o,
+                             const float* lse) {
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  pdllm_status st;
+  if ((st = check_tensor(q, "q")) != PDLLM_OK) return st;
+  if ((st = check_tensor(k_resp, "k_resp")) != PDLLM_OK) return st;
+  if ((st = check_tensor(v_resp, "v_resp")) != PDLLM_OK) return st;
+  if ((st = check_tensor(o, "o")) != PDLLM_OK) return st;
+  if (lse != nullptr && !aligned16(lse)) return fail(PDLLM_ERR_INVALID_ARG, "lse must be 16-byte aligned");
   return PDLLM_OK;
 }
 
@@ -499,13 +515,7 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
   pdllm::DecodePlan plan;
   pdllm_status st = plan_call(pool, pt, n_seq, l_d, h_q, opts, &plan);
   if (st != PDLLM_OK) return st;
-  if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(PDLLM_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
-  if ((st = check_tensor(q, "q")) != PDLLM_OK) return st;
-  if ((st = check_tensor(k_resp, "k_resp")) != PDLLM_OK) return st;
-  if ((st = check_tensor(v_resp, "v_resp")) != PDLLM_OK) return st;
-  if ((st = check_tensor(o, "o")) != PDLLM_OK) return st;
-  if (lse != nullptr && !aligned16(lse)) return fail(PDLLM_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+  if ((st = check_decode_io(scale, q, k_resp, v_resp, o, lse)) != PDLLM_OK) return st;
   if (plan.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < (size_t)plan.workspace_bytes)
       return fail(PDLLM_ERR_WORKSPACE_TOO_SMALL, "workspace of %lld bytes needed, %zu given",
@@ -562,6 +572,29 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
     }
   }
   return ok();
+}
+
+pdllm_status pdllm_split_attn_decode_noalloc(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                             const void* q, const void* k_resp, const void* v_resp,
+                                             int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                             int32_t num_splits, void* o, float* lse, void* stream) {
+  pdllm_decode_opts opts{};
+  opts.num_splits = num_splits;
+  pdllm::DecodePlan plan;
+  pdllm_status st = plan_call(pool, pt, n_seq, l_d, h_q, &opts, &plan);
+  if (st != PDLLM_OK) return st;
+  if ((st = check_decode_io(scale, q, k_resp, v_resp, o, lse)) != PDLLM_OK) return st;
+  if ((size_t)plan.workspace_bytes > pdllm::kNoAllocScratchBytes)
+    return fail(PDLLM_ERR_UNSUPPORTED,
+                "this decode needs %lld bytes of scratch; the no-allocation entry point holds %zu bytes "
+                "(use pdllm_split_attn_decode with a workspace)",
+                (long long)plan.workspace_bytes, pdllm::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (plan.workspace_bytes > 0 &&
+      (st = hip_status(pdllm::noalloc_scratch(&scratch), "scratch lookup")) != PDLLM_OK)
+    return st;
+  return pdllm_split_attn_decode_ex(pool, pt, q, k_resp, v_resp, n_seq, l_d, h_q, scale, &opts, o, lse, scratch,
+                                    scratch != nullptr ? pdllm::kNoAllocScratchBytes : 0, stream);
 }
 
 pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,

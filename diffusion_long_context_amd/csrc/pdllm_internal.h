@@ -39,6 +39,14 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
                  int d, int dtype, int num_splits, int force_rows, int n_cu, DecodePlan* plan,
                  const char** err);
 
+// ---------------------------------------------------------------- scratch
+// Bytes of the library-held device scratch of the no-allocation decode entry
+// point (one copy per GPU, held until the process ends).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of the current device's scratch (looked up once per
+// device); returns a hipError_t value as int.
+int noalloc_scratch(void** ptr);
+
 // ---------------------------------------------------------------- decode
 struct DecodeSeq {
   int32_t k_s;              // selected chunks of this sequence

@@ -380,6 +380,26 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
                                         const pdllm_decode_opts* opts, void* o, float* lse,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pdllm_split_attn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and errors, with num_splits as
+ * there, but no workspace argument.  The split partials live in a scratch
+ * array the library holds on each GPU (64 MiB, PDLLM_NOALLOC_SCRATCH_BYTES,
+ * held until the process ends); the call itself allocates nothing, and the
+ * caller still provides q, k_resp, v_resp, o and lse.  A call whose plan needs
+ * more scratch than that returns PDLLM_ERR_UNSUPPORTED before enqueueing
+ * anything (pdllm_split_attn_decode_workspace gives the need).  Every call on
+ * one GPU shares its scratch: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe.
+ */
+#define PDLLM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pdllm_status pdllm_split_attn_decode_noalloc(const pdllm_pool* pool, const pdllm_page_table* pt,
+                                             const void* q, const void* k_resp, const void* v_resp,
+                                             int32_t n_seq, int32_t l_d, int32_t h_q, float scale,
+                                             int32_t num_splits, void* o, float* lse, void* stream);
+
 /* ------------------------------------------------------------------------ */
 
 /* Message of the calling thread's last non-OK status ("" if none). */

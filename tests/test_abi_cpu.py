@@ -166,6 +166,23 @@ def test_decode_forced_shape_plans():
     assert q(128, 5) == q(256, 5) == q(0, 5)
 
 
+def test_noalloc_decode_validation():
+    """The no-allocation decode validates like the workspace call and
+    rejects, before touching a device, a plan whose partials exceed its
+    64 MiB scratch."""
+    f = L.lib.pdllm_split_attn_decode_noalloc
+    pool = _pool()
+    pt, _keep = _pt([16])
+    call = lambda **kw: f(ctypes.byref(pool), ctypes.byref(kw.get("pt", pt)), kw.get("q", 0x60000), 0x70000,
+                          0x80000, 1, 256, kw.get("h_q", 28), kw.get("scale", 0.088), kw.get("splits", 0),
+                          0x90000, None, None)
+    assert call(h_q=27) == INVALID and "multiple" in _err()
+    assert call(q=0) == INVALID and "q is NULL" in _err()
+    assert call(scale=0.0) == INVALID and "scale" in _err()
+    # 69 splits x 256 rows x 28 heads x 128 d of bf16 partials: about 127 MB
+    assert call(splits=69) == UNSUPPORTED and "scratch" in _err()
+
+
 def test_decode_workspace_query_matches_plan():
     pool = _pool()
     pt, _keep = _pt([16])
