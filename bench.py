@@ -97,6 +97,10 @@ def parse():
                    help="score every chunk (top-B for all chunks), not only the K kept ones")
     p.add_argument("--unfused", action="store_true",
                    help="run the prefill side as three calls (prefill + scoring, top-B, top-K)")
+    p.add_argument("--decode-merge", type=int, default=0, choices=(0, 1, 2, 3),
+                   help="how the decode merges its splits: 0 the library's choice, 1 a separate merge "
+                        "kernel, 2 / 3 inside the decode launch over float32 / bf16 partials "
+                        "(pdllm_decode_opts.merge)")
     p.add_argument("--decode-only", action="store_true",
                    help="time only the decode call (diagnostic; not the headline step)")
     p.add_argument("--full-step", action="store_true",
@@ -338,7 +342,7 @@ def full_step(args):
         k_resp = rnd(cfg.n_seq, cfg.l_d, cfg.h_kv, cfg.d)
         v_resp = rnd(cfg.n_seq, cfg.l_d, cfg.h_kv, cfg.d)
         calls.append(L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp,
-                              cfg.scale))
+                              cfg.scale, merge=args.decode_merge))
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
@@ -600,7 +604,8 @@ def main():
                              dtype=torch.uint8, device=dev)
     keep = torch.empty((cfg.n_slots, cfg.b), dtype=torch.int32, device=dev)
     sel = torch.empty((cfg.n_seq, cfg.k_max), dtype=torch.int32, device=dev)
-    decode = L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp, cfg.scale)
+    decode = L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp, cfg.scale,
+                      merge=args.decode_merge)
 
     def stage_prefill():
         L.chunk_prefill_score(pool_k, pool_v, chunk_slot, q_chunk, q_win, cfg.n_chunks, cfg.scale,

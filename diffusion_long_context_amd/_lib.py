@@ -38,7 +38,7 @@ class PageTable(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("q_rows_per_wg", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_select_topB",
@@ -97,7 +97,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-ABI_VERSION = 8
+ABI_VERSION = 9
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -343,12 +343,13 @@ class Decode:
     partial chunk).  For a pool of compacted slots (pdllm_compact_kept_rows),
     whose kept rows are rows 1..b, pass ``compacted=True`` with ``keep_rows``
     (read only for its -1 entries) or with keep_rows=None and ``b``.
-    ``q_rows_per_wg`` forces the workgroup shape (pdllm_decode_opts; 0 =
-    the planner's choice)."""
+    ``q_rows_per_wg`` forces the workgroup shape and ``merge`` the merge
+    (pdllm_decode_opts; 0 = the library's choice).  The workspace is
+    zero-filled once, as the in-kernel merge requires."""
 
     def __init__(self, pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
                  v_resp, scale, num_splits=0, want_lse=True, out=None, b=None, compacted=False,
-                 q_rows_per_wg=0):
+                 q_rows_per_wg=0, merge=0):
         self.pool = make_pool(pool_k, pool_v)
         compacted = compacted or keep_rows is None
         no_table = keep_rows is None
@@ -377,14 +378,14 @@ class Decode:
         self.n_seq, self.l_d, self.h_q = n_seq, l_d, h_q
         self.scale = float(scale)
         self.num_splits = int(num_splits)
-        self.opts = DecodeOpts(int(num_splits), int(q_rows_per_wg))
+        self.opts = DecodeOpts(int(num_splits), int(q_rows_per_wg), int(merge))
         dev = q.device
         self.device = dev
         self.o = out if out is not None else torch.empty_like(q)
         self.lse = torch.empty((n_seq, h_q, l_d), dtype=torch.float32, device=dev) if want_lse else None
         need = lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(self.pool), ctypes.byref(self.pt),
                                                         n_seq, l_d, h_q, ctypes.byref(self.opts))
-        self.workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(int(need), 256), dtype=torch.uint8, device=dev)
 
     def __call__(self, stream: Optional[int] = None):
         st = lib.pdllm_split_attn_decode_ex(
@@ -397,8 +398,10 @@ class Decode:
 
 
 def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
-                      v_resp, scale, num_splits=0, want_lse=True, b=None, compacted=False, q_rows_per_wg=0):
+                      v_resp, scale, num_splits=0, want_lse=True, b=None, compacted=False, q_rows_per_wg=0,
+                      merge=0):
     """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None).
     compacted=True (or keep_rows=None with ``b``) decodes over a pool of compacted slots."""
     return Decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp, v_resp,
-                  scale, num_splits, want_lse, b=b, compacted=compacted, q_rows_per_wg=q_rows_per_wg)()
+                  scale, num_splits, want_lse, b=b, compacted=compacted, q_rows_per_wg=q_rows_per_wg,
+                  merge=merge)()

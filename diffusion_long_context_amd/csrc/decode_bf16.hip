@@ -7,8 +7,9 @@
 // followed by the sequence's recomputed response rows.  The kv rows are split
 // into runs of 64-row tiles; each workgroup handles one (sequence, kv head,
 // 128 or 256 query rows, split) and emits either the final output (single
-// split) or a partial output (bf16, normalised) and its float32 log-sum-exp
-// for the merge kernel.
+// split) or a partial output (normalised) and its float32 log-sum-exp.  The
+// splits are merged either inside this launch, by the splits themselves
+// (merge_group), or by a second kernel (lse_merge_kernel).
 //
 // Design for CDNA4:
 // * Query rows of one kv head are packed as (token, grouped head) pairs, so
@@ -28,11 +29,15 @@
 #include "attn_tile.h"
 #include "device_common.h"
 #include "pdllm_internal.h"
+#include "xwg_sync.h"
 
 namespace pdllm {
 namespace {
 
 constexpr int kTile = kDecodeTile;         // kv rows per tile
+// Polls of a group's arrival count before a waiting split gives up its merge
+// slices to the group's last arrival (about 20 ms).
+constexpr int kSpinLimit = 1 << 14;
 
 // LDS of one workgroup.  The 8-wave variant (one workgroup per CU) uses the
 // V pitch that keeps the transposing reads conflict-free on the 64-bank LDS
@@ -50,6 +55,7 @@ struct Smem {
   uint64_t absent[kTableTiles];            // per table tile: bit r = row r is an absent kept row
   uint64_t kmask[2];                       // the absent mask of the tile in each K buffer
   int flag[WAVES];                         // per wavefront: the split holds an absent row
+  int xw[4];                               // words broadcast by thread 0 (in-kernel merge)
 };
 
 // Element offset of attended row v of sequence s for kv head g.  Pool rows
@@ -82,8 +88,209 @@ __device__ __forceinline__ int64_t resolve_row(const DecodeArgs& a, int s, int g
   return -1 - ((((int64_t)s * a.l_d + j) * a.h_kv + g) * D);
 }
 
+// The work item of a workgroup: (sequence, kv head, query tile, split).
+// Separate merge: query tiles vary fastest, so the workgroups that share one
+// (kv head, split) -- and therefore its K/V rows -- sit on one XCD and hit its
+// L2.  In-kernel merge: every split of a merge group (sequence, kv head,
+// query tile) runs on one XCD, so that the partials never leave its L2.
+// Workgroups are dispatched round-robin over the XCDs, so workgroup b runs on
+// XCD b % 8 (b % 4, b % 2 with fewer XCDs per device: the same grouping);
+// XCD x takes the groups [xcd_grp[x], xcd_grp[x + 1]), its k-th workgroup the
+// k-th split in that range, and workgroups past the range have no item.
+struct WorkItem {
+  int si, s, g, qt, split, n_splits, gi;
+  bool valid;
+};
+template <bool FUSED, class A>
+__device__ __forceinline__ WorkItem work_item(const A& a, int bid) {
+  WorkItem w;
+  int si = 0, local;
+  w.valid = true;
+  if constexpr (FUSED) {
+    const int x = bid & 7, ge = a.xcd_grp[x + 1];
+    int k = bid >> 3, gi = a.xcd_grp[x];
+    w.valid = false;
+    for (; gi < ge; ++gi) {
+      while (si + 1 < a.n_seq_launch && gi >= a.seq[si + 1].grp_begin) ++si;
+      if (k < a.seq[si].n_splits) {
+        w.valid = true;
+        break;
+      }
+      k -= a.seq[si].n_splits;
+    }
+    gi = min(gi, ge - 1);
+    while (si + 1 < a.n_seq_launch && gi >= a.seq[si + 1].grp_begin) ++si;
+    local = gi - a.seq[si].grp_begin;
+    w.split = k;
+    w.gi = gi;
+    w.qt = local % a.q_tiles;
+    w.g = local / a.q_tiles;
+  } else {
+    const int wg = xcd_remap(bid, a.total_wg);
+    while (si + 1 < a.n_seq_launch && wg >= a.seq[si + 1].wg_begin) ++si;
+    local = wg - a.seq[si].wg_begin;
+    w.qt = local % a.q_tiles;
+    local /= a.q_tiles;
+    w.split = local % a.seq[si].n_splits;
+    w.g = local / a.seq[si].n_splits;
+    w.gi = a.seq[si].grp_begin + w.g * a.q_tiles + w.qt;
+  }
+  w.si = si;
+  w.s = a.seq0 + si;
+  w.n_splits = a.seq[si].n_splits;
+  return w;
+}
+
+// Layout of the in-kernel merge's partials, private to this file: the
+// outputs of one (split, group) are WAVES blocks of 32 rows, one per
+// wavefront, each stored as its lanes hold it -- chunk c = 4 db + m of lane l
+// (d = 32 db + 8 m + 4 (l / 32) + t, t < 4, row l % 32) at (64 c + l) * 4
+// elements -- so that every store instruction writes one contiguous run.
+// Their lse values are [split][group][32 WAVES rows].
 template <int D, int WAVES>
+__device__ __forceinline__ int64_t fused_block(int64_t part_off, int h_kv, int q_tiles, int split, int gl, int wave) {
+  return part_off + ((int64_t)(split * h_kv * q_tiles + gl) * WAVES + wave) * (32 * D);
+}
+
+// Merge slice x (the 32 rows of wavefront x) of a group over its splits.
+// Work item k: row r = k % 32 and d-pair p = k / 32 (d = 8 p .. 8 p + 7: the
+// four values of chunk p in lane r, then the four in lane 32 + r).
+template <int D, int WAVES, bool PBF16, class A>
+__device__ __forceinline__ void merge_slice(const A& a, int tid, int si, int s, int g, int qt, int x,
+                                            int n_splits) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int P = D / 8;                 // d-pairs per row
+  constexpr int KB = PBF16 ? 16 : 8;       // splits whose loads are in flight together
+  constexpr uint32_t EB = PBF16 ? 2 : 4;   // bytes per partial element
+  const int G = a.group;
+  const int64_t part_off = a.seq[si].part_off, lse_off = a.seq[si].lse_off;
+  const int gl = g * a.q_tiles + qt;
+  const int64_t split_stride = (int64_t)a.h_kv * a.q_tiles * WAVES * (32 * D);   // elements
+  const int64_t lse_stride = (int64_t)a.h_kv * a.q_tiles * 32 * WAVES;
+  const auto rp = buffer_rsrc(a.part_o);
+  const auto rl = buffer_rsrc(a.part_lse);
+  for (int k = tid; k < 32 * P; k += kThreads) {
+    const int r = k & 31, pr = k >> 5;
+    const int qrow = qt * (32 * WAVES) + 32 * x + r;
+    if (qrow >= a.l_d * G) continue;
+    const int i = qrow / G, h = g * G + (qrow - i * G);
+    const int64_t b0 = fused_block<D, WAVES>(part_off, a.h_kv, a.q_tiles, 0, gl, x) + (int64_t)(64 * pr + r) * 4;
+    const int64_t l0 = lse_off + (int64_t)gl * 32 * WAVES + 32 * x + r;
+    float mx = -INFINITY, tot = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    for (int j0 = 0; j0 < n_splits; j0 += KB) {
+      float t[KB], xv[KB][8];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int j = min(j0 + u, n_splits - 1);           // past the end: a valid split, weight 0
+        const float lj = load_l2_f32(rl, 4u * (uint32_t)(l0 + j * lse_stride));
+        t[u] = j0 + u < n_splits ? lj * kLog2e : -INFINITY;
+        const uint32_t ob = EB * (uint32_t)(b0 + j * split_stride);
+        if constexpr (PBF16) {
+          const u32x2 w0 = load_l2_b64(rp, ob), w1 = load_l2_b64(rp, ob + 128u * EB);
+          xv[u][0] = bf16_bits_to_f32(w0[0] & 0xffffu);
+          xv[u][1] = bf16_bits_to_f32(w0[0] >> 16);
+          xv[u][2] = bf16_bits_to_f32(w0[1] & 0xffffu);
+          xv[u][3] = bf16_bits_to_f32(w0[1] >> 16);
+          xv[u][4] = bf16_bits_to_f32(w1[0] & 0xffffu);
+          xv[u][5] = bf16_bits_to_f32(w1[0] >> 16);
+          xv[u][6] = bf16_bits_to_f32(w1[1] & 0xffffu);
+          xv[u][7] = bf16_bits_to_f32(w1[1] >> 16);
+        } else {
+          const u32x4 w0 = load_l2_b128(rp, ob), w1 = load_l2_b128(rp, ob + 128u * EB);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xv[u][e] = __uint_as_float(w0[e]);
+            xv[u][4 + e] = __uint_as_float(w1[e]);
+          }
+        }
+      }
+      float m_new = mx;
+#pragma unroll
+      for (int u = 0; u < KB; ++u) m_new = fmaxf(m_new, t[u]);
+      const float ref = m_new == -INFINITY ? 0.f : m_new;  // every split so far empty: all weights 0
+      const float c = __builtin_amdgcn_exp2f(mx - ref);
+      tot *= c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= c;
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const float w = __builtin_amdgcn_exp2f(t[u] - ref);
+        tot += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += w * xv[u][e];
+      }
+      mx = m_new;
+    }
+    const float inv = 1.f / tot;
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * pr) =
+        u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+              pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+    if (a.lse != nullptr && pr == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = (mx + __log2f(tot)) * kLn2;
+  }
+}
+
+// In-kernel LSE merge ("Attention kernel optimization": the splits of a
+// (sequence, kv head, query tile) group are merged by a log-sum-exp
+// reduction).  The rows of a group are cut into WAVES slices of 32 rows;
+// split j owns the slices x with x % n_splits == j.  All splits of a group run
+// on one XCD (work_item) and exchange their partials through its L2
+// (xwg_sync.h).  After publishing its partial, a split adds its arrival to the
+// group's count:
+//  * the last arrival merges its own slices, then every slice that no other
+//    split has claimed;
+//  * an earlier arrival, once every workgroup of the launch has started (so
+//    the group's other splits are running or done), waits (bounded) for the
+//    count to reach n_splits and merges its own slices; on time-out it leaves
+//    them to the last arrival.
+// A slice is merged by whoever claims it first (one counter per slice), so
+// each is merged once, and no wait depends on a workgroup that has not
+// started.
+template <int D, int WAVES, bool PBF16, class A, class Sm>
+__device__ __forceinline__ void merge_group(const A& a, Sm& sm, int tid, int si, int s, int g, int qt,
+                                            int split, int n_splits) {
+  const int gi = a.seq[si].grp_begin + g * a.q_tiles + qt;   // the launch's group index
+  int* done = a.sync + 2 + gi;
+  int* claimed = a.sync + 2 + a.n_groups + (int64_t)gi * WAVES;
+  if (tid == 0) {
+    sm.xw[0] = counter_add(done, 1);
+    sm.xw[1] = counter_load(a.sync);       // workgroups of the launch that have started
+  }
+  __syncthreads();
+  const bool last = sm.xw[0] == n_splits - 1;
+  bool go = last;
+  if (!last && sm.xw[1] >= a.total_wg) {
+    if (tid == 0) {
+      int it = 0;
+      while (counter_load(done) < n_splits && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(8);
+      sm.xw[2] = it < kSpinLimit;
+    }
+    __syncthreads();
+    go = sm.xw[2] != 0;
+  }
+  if (!go) return;
+  // claim (own slices, then -- the last arrival only -- the others), one
+  // atomic per slice from the first WAVES threads, then merge those won
+  for (int pass = 0; pass < (last ? 2 : 1); ++pass) {
+    bool won = false;
+    if (tid < WAVES && ((tid % n_splits == split) == (pass == 0))) won = counter_add(claimed + tid, 1) == 0;
+    const uint64_t mask = __ballot(won);
+    __syncthreads();                       // xw[3] is free
+    if (tid == 0) sm.xw[3] = (int)mask;
+    __syncthreads();
+    const int m = sm.xw[3];
+    for (int x = 0; x < WAVES; ++x)
+      if (m & (1 << x)) merge_slice<D, WAVES, PBF16>(a, tid, si, s, g, qt, x, n_splits);
+  }
+}
+
+// MERGE: 0 = partials for the separate merge kernel (bf16, row-major);
+// 1 / 2 = merged in this launch over float32 / bf16 partials.
+template <int D, int WAVES, int MERGE>
 __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArgs a) {
+  constexpr bool FUSED = MERGE != 0;
+  constexpr bool PBF16 = MERGE == 2;
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 32 * WAVES;        // query rows of the workgroup
   __shared__ Smem<D, WAVES> sm;
@@ -96,21 +303,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   static_assert(RPT == 1 || RPT == 2 || RPT == 4, "loader mapping");
 
   // ---- work item: (sequence, kv head, query tile, split)
-  const int wg = xcd_remap(blockIdx.x, a.total_wg);
-  int si = 0;
-  while (si + 1 < a.n_seq_launch && wg >= a.seq[si + 1].wg_begin) ++si;
+  const WorkItem w0 = work_item<FUSED>(a, blockIdx.x);
+  if (!w0.valid) return;                   // padding of a short XCD range
+  const int si = w0.si, qt = w0.qt, split = w0.split, g = w0.g, s = w0.s;
   const int k_s = a.seq[si].k_s;
   const int n_kv = a.seq[si].n_kv;
-  const int n_splits = a.seq[si].n_splits;
   const int tps = a.seq[si].tiles_per_split;
-  // query tiles vary fastest, so the workgroups that share one (kv head,
-  // split) -- and therefore its K/V rows -- sit on one XCD and hit its L2
-  int local = wg - a.seq[si].wg_begin;
-  const int qt = local % a.q_tiles;
-  local /= a.q_tiles;
-  const int split = local % n_splits;
-  const int g = local / n_splits;
-  const int s = a.seq0 + si;
   const int n_tiles = (n_kv + kTile - 1) / kTile;
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, n_tiles);
@@ -118,6 +316,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 31, lj = lane >> 5;     // query column, kv / d half
   const int G = a.group;
+  if constexpr (FUSED)
+    if (tid == 0) counter_add(a.sync, 1);       // this workgroup has started
   const int rows_total = a.l_d * G;
   const uint16_t* pk = static_cast<const uint16_t*>(a.pool_k);
   const uint16_t* pv = static_cast<const uint16_t*>(a.pool_v);
@@ -365,21 +565,87 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   else
     run(BoolConst<false>{});
 
-  // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row)
+  // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row).
+  // The work item and the lane's row are derived again here from the block
+  // and thread ids (the empty asm hides that they were computed before), so
+  // that none of them stays live in registers across the main loop.
+  int bid = blockIdx.x;
+  asm volatile("" : "+s"(bid));
+  // The kernel arguments are read again from the argument segment, through a
+  // pointer the compiler cannot see through, so that they are loaded here
+  // rather than held in registers across the loop.
+  KernArgs<DecodeArgs> ap = kernarg<DecodeArgs>();
+  {
+  const auto& a = *ap;
+  const WorkItem w = work_item<FUSED>(a, bid);
+  const int si = w.si, s = w.s, g = w.g, qt = w.qt, split = w.split, n_splits = w.n_splits;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lj = (tid & 63) >> 5;
+  const int qrow = qt * kRows + (tid >> 6) * 32 + (tid & 31);
+  const int rows_total = a.l_d * G;
   const float l = at.row_sum();
-  if (qrow < rows_total) {
-    const int i = qrow / G, h = g * G + (qrow - i * G);
-    const float inv = l > 0.f ? 1.f / l : 0.f;   // a split of absent rows only: o = 0, lse = -inf
-    const float lse_v = at.lse(l);
-    if (n_splits == 1) {
+  const float inv = l > 0.f ? 1.f / l : 0.f;     // a split of absent rows only: o = 0, lse = -inf
+  const float lse_v = at.lse(l);
+  const bool row_ok = qrow < rows_total;
+  const int qr = min(qrow, rows_total - 1);
+  const int i = qr / G, h = g * G + (qr - i * G);
+  if (n_splits == 1) {
+    if (row_ok) {
       store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj,
                        at.acc, inv);
       if (a.lse != nullptr && lj == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
-    } else {
+    }
+  } else if constexpr (!FUSED) {
+    if (row_ok) {
       store_o_bf16<DB>(static_cast<uint16_t*>(a.part_o) + a.seq[si].part_off +
                            (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 8 * lj,
                        at.acc, inv);
       if (lj == 0) a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;
+    }
+  } else {
+    // the partial, into this XCD's L2 in the merge's lane-major layout: one
+    // contiguous run per store instruction (rows past the end hold finite
+    // values the merge never reads)
+    {
+      const int gl = g * a.q_tiles + qt, wv = (tid >> 6) & (WAVES - 1), ln = tid & 63;
+      const auto rp = buffer_rsrc(a.part_o);
+      const int64_t blk = fused_block<D, WAVES>(a.seq[si].part_off, a.h_kv, a.q_tiles, split, gl, wv);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float v0 = at.acc[db][4 * m] * inv, v1 = at.acc[db][4 * m + 1] * inv;
+          const float v2 = at.acc[db][4 * m + 2] * inv, v3 = at.acc[db][4 * m + 3] * inv;
+          const uint32_t off = (uint32_t)(blk + (int64_t)(64 * (4 * db + m) + ln) * 4);
+          if constexpr (PBF16)
+            store_l2(rp, 2u * off, u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)});
+          else
+            store_l2(rp, 4u * off, u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2),
+                                               __float_as_uint(v3)});
+        }
+      if (lj == 0)
+        store_l2(buffer_rsrc(a.part_lse),
+                       4u * (uint32_t)(a.seq[si].lse_off + (int64_t)(split * a.h_kv * a.q_tiles + gl) * 32 * WAVES +
+                                       32 * wv + (ln & 31)),
+                       lse_v);
+    }
+    wait_vm_all();                         // this thread's partial is stored
+    __syncthreads();                       // ... and every thread's
+    merge_group<D, WAVES, PBF16>(a, sm, tid, si, s, g, qt, split, n_splits);
+  }
+  }
+  if constexpr (FUSED) {
+    const auto& a = *ap;
+    // The workgroup that leaves last returns the sync words to zero for the
+    // next launch; every other workgroup has made its last access to them
+    // (each waits for its own atomics before counting itself out).
+    __syncthreads();
+    if (tid == 0) sm.xw[0] = counter_add(a.sync + 1, 1);
+    __syncthreads();
+    if (sm.xw[0] == a.total_wg - 1) {
+      const int n = 2 + a.n_groups * (1 + WAVES);
+      for (int k = tid; k < n; k += kThreads) counter_store(a.sync + k, 0);
     }
   }
 }
@@ -489,22 +755,32 @@ int merge_launch(const DecodeArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-}  // namespace
-
-int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream) {
-  const dim3 grid(a.total_wg);
-  const hipStream_t st = (hipStream_t)stream;
+template <int MERGE>
+int launch_decode_bf16_t(const DecodeArgs& a, int d, int q_rows_per_wg, hipStream_t st) {
+  const dim3 grid(a.grid_wg);
   if (d == 128 && q_rows_per_wg == 256)
-    hipLaunchKernelGGL((decode_bf16_kernel<128, 8>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<128, 8, MERGE>), grid, dim3(512), 0, st, a);
   else if (d == 128 && q_rows_per_wg == 128)
-    hipLaunchKernelGGL((decode_bf16_kernel<128, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<128, 4, MERGE>), grid, dim3(256), 0, st, a);
   else if (d == 64 && q_rows_per_wg == 256)
-    hipLaunchKernelGGL((decode_bf16_kernel<64, 8>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<64, 8, MERGE>), grid, dim3(512), 0, st, a);
   else if (d == 64 && q_rows_per_wg == 128)
-    hipLaunchKernelGGL((decode_bf16_kernel<64, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<64, 4, MERGE>), grid, dim3(256), 0, st, a);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream) {
+  const hipStream_t st = (hipStream_t)stream;
+  switch (a.merge_kind) {
+    case 0: return launch_decode_bf16_t<0>(a, d, q_rows_per_wg, st);
+    case 1: return launch_decode_bf16_t<1>(a, d, q_rows_per_wg, st);
+    case 2: return launch_decode_bf16_t<2>(a, d, q_rows_per_wg, st);
+    default: return (int)hipErrorInvalidValue;
+  }
 }
 
 int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_out, void* stream) {

@@ -112,6 +112,18 @@ __device__ __forceinline__ bool chunk_scored(const Args& a, int c) {
   return in_top_k(a.sel_score + (int64_t)s * a.sel_per_seq, a.sel_per_seq, c - s * a.sel_per_seq, a.sel_k[s]);
 }
 
+// The kernel's argument block (its only argument, passed by value) read
+// through the argument segment pointer, hidden from the optimiser so that
+// loads through it are issued where they are written.
+template <class T>
+using KernArgs = __attribute__((address_space(4))) const T*;
+template <class T>
+__device__ __forceinline__ KernArgs<T> kernarg() {
+  KernArgs<T> p = (KernArgs<T>)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 // A compile-time flag passed to a generic lambda (instantiates it twice).
 template <bool B>
 struct BoolConst {

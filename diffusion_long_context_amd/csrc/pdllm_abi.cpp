@@ -196,10 +196,18 @@ pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32
       return fail(PDLLM_ERR_UNSUPPORTED, "q_rows_per_wg %d is not a workgroup shape of the %s kernel", rows,
                   pool->dtype == PDLLM_BF16 ? "bf16 (128, 256)" : "f32 (64)");
   }
+  if (opts->merge < 0 || opts->merge > 3)
+    return fail(PDLLM_ERR_INVALID_ARG, "merge must be 0, 1, 2 or 3 (got %d)", opts->merge);
+  if (opts->merge >= 2 && pool->dtype != PDLLM_BF16)
+    return fail(PDLLM_ERR_UNSUPPORTED, "the in-kernel merge is implemented for bf16 only");
   const char* err = "";
   if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
-                          opts->num_splits, rows, device_cu_count(), plan, &err))
+                          opts->num_splits, rows, opts->merge, device_cu_count(), plan, &err))
     return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
+  // the in-kernel merge addresses its partials with 32-bit byte offsets
+  if (plan->fused && plan->part_floats * plan->part_elem_bytes > (int64_t)INT32_MAX)
+    return fail(PDLLM_ERR_UNSUPPORTED, "in-kernel merge: %lld bytes of partials exceed 2 GiB (use merge = 1)",
+                (long long)(plan->part_floats * plan->part_elem_bytes));
   return PDLLM_OK;
 }
 
@@ -480,7 +488,7 @@ pdllm_status pdllm_decode_plan(const int32_t* k_per_seq, int32_t n_seq, int32_t 
   if (dtype != PDLLM_F32 && dtype != PDLLM_BF16) return fail(PDLLM_ERR_INVALID_ARG, "bad dtype %d", dtype);
   pdllm::DecodePlan plan;
   const char* err = "";
-  if (!pdllm::plan_decode(k_per_seq, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, 0, n_cu, &plan, &err))
+  if (!pdllm::plan_decode(k_per_seq, n_seq, b, l_d, h_q, h_kv, d, dtype, num_splits, 0, 0, n_cu, &plan, &err))
     return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
   for (int s = 0; s < n_seq; ++s) {
     if (splits_per_seq) splits_per_seq[s] = plan.splits[s];
@@ -529,9 +537,12 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
   pdllm::DecodeArgs a = base_decode_args(pool, pt, q, k_resp, v_resp, l_d, h_q, scale, o, lse);
   a.q_tiles = plan.q_tiles;
   if (plan.workspace_bytes > 0) {
-    a.part_o = workspace;
+    char* w = static_cast<char*>(workspace);
+    if (plan.fused) a.sync = reinterpret_cast<int32_t*>(w);
+    a.merge_kind = plan.fused ? (plan.fused_bf16 ? 2 : 1) : 0;
+    a.part_o = w + plan.sync_bytes;
     const int64_t part_bytes = (plan.part_floats * plan.part_elem_bytes + 255) / 256 * 256;
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
+    a.part_lse = reinterpret_cast<float*>(w + plan.sync_bytes + part_bytes);
   }
   std::vector<pdllm::DecodeArgs> launches;
   std::vector<bool> merges;
@@ -551,13 +562,24 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
       q_.n_splits = plan.splits[s];
       q_.tiles_per_split = plan.tiles_per_split[s];
       q_.wg_begin = (int32_t)std::min<int64_t>(wg, INT32_MAX);
+      q_.grp_begin = i * pool->h_kv * plan.q_tiles;
       q_.part_off = plan.part_off[s];
       q_.lse_off = plan.lse_off[s];
       wg += (int64_t)pool->h_kv * plan.q_tiles * plan.splits[s];
       merge |= plan.splits[s] > 1;
     }
-    if (wg > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "decode grid too large (%lld workgroups)", (long long)wg);
+    a.n_groups = n_here * pool->h_kv * plan.q_tiles;
+    int64_t grid = wg;
+    if (plan.fused) {             // every split of a merge group on one XCD
+      std::vector<int> sizes;
+      sizes.reserve(a.n_groups);
+      for (int i = 0; i < n_here; ++i)
+        for (int64_t k = 0; k < (int64_t)pool->h_kv * plan.q_tiles; ++k) sizes.push_back(a.seq[i].n_splits);
+      grid = pdllm::kXcdGroups * pdllm::xcd_partition(sizes, a.xcd_grp);
+    }
+    if (grid > INT32_MAX) return fail(PDLLM_ERR_UNSUPPORTED, "decode grid too large (%lld workgroups)", (long long)grid);
     a.total_wg = (int32_t)wg;
+    a.grid_wg = (int32_t)grid;
     launches.push_back(a);
     merges.push_back(merge);
   }
@@ -566,7 +588,7 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
     const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(la, pool->d, plan.q_rows_per_wg, stream)
                                              : pdllm::launch_decode_f32(la, pool->d, stream);
     if ((st = hip_status(e, "decode launch")) != PDLLM_OK) return st;
-    if (merges[i]) {
+    if (merges[i] && !plan.fused) {
       st = hip_status(pdllm::launch_lse_merge(la, pool->d, pool->dtype == PDLLM_BF16, stream), "merge launch");
       if (st != PDLLM_OK) return st;
     }

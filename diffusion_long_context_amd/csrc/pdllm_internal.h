@@ -25,9 +25,17 @@ struct DecodePlan {
   int q_rows_per_wg = 0;   // query rows per workgroup
   int q_tiles = 0;         // workgroups along the query rows of one (seq, kv head)
   std::vector<int> k_s, n_kv, n_tiles, splits, tiles_per_split;
-  std::vector<int64_t> part_off, lse_off;   // element offsets into the workspace
+  std::vector<int64_t> part_off, lse_off;   // element offsets into the partial regions
   int64_t part_floats = 0, lse_floats = 0;  // element counts (partial O, partial lse)
   int part_elem_bytes = 4;                  // partial O element: bf16 (2) or float32 (4)
+  // In-kernel merge (bf16): the splits of a group merge their float32
+  // partials in the decode launch itself, synchronised through int32 words at
+  // the start of the workspace (started, exited, then per group one arrival
+  // count and one claim count per 32-row slice).
+  bool fused = false;
+  bool fused_bf16 = false;                  // in-kernel merge over bf16 (else float32) partials
+  int64_t sync_words = 0;
+  int64_t sync_bytes = 0;                   // 256-aligned; the partials follow
   int64_t workspace_bytes = 0;
   int64_t total_workgroups = 0;
 };
@@ -35,8 +43,11 @@ struct DecodePlan {
 // Fills `plan`; returns false (with a message in *err) on invalid input.
 // force_rows > 0 fixes the query rows per workgroup (a shape of the dtype's
 // kernel, checked by the caller); 0 lets the planner choose.
+// merge: 0 = the library's choice (in-kernel for bf16), 1 = a separate merge
+// kernel, 2 / 3 = in-kernel over float32 / bf16 partials (bf16 only; the
+// caller checked).
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
-                 int d, int dtype, int num_splits, int force_rows, int n_cu, DecodePlan* plan,
+                 int d, int dtype, int num_splits, int force_rows, int merge, int n_cu, DecodePlan* plan,
                  const char** err);
 
 // ---------------------------------------------------------------- scratch
@@ -48,13 +59,21 @@ constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 int noalloc_scratch(void** ptr);
 
 // ---------------------------------------------------------------- decode
+// Workgroup b runs on XCD b % kXcdGroups (dispatch is round-robin over the
+// XCDs; with fewer XCDs per device, b % 8 still implies the same XCD).
+constexpr int kXcdGroups = 8;
+// Contiguous partition of `sizes` (workgroups per merge group, in order) into
+// kXcdGroups ranges with the smallest largest sum; bounds[x] .. bounds[x + 1]
+// is range x.  Returns that largest sum.
+int64_t xcd_partition(const std::vector<int>& sizes, int32_t* bounds);
+
 struct DecodeSeq {
   int32_t k_s;              // selected chunks of this sequence
   int32_t n_kv;             // attended rows: k_s * (b + 1) + l_d
   int32_t n_splits;
   int32_t tiles_per_split;
   int32_t wg_begin;         // first workgroup of this sequence in the launch
-  int32_t pad_;
+  int32_t grp_begin;        // first merge group (kv head, query tile) of this sequence in the launch
   int64_t part_off;         // element offset of its partial outputs
   int64_t lse_off;          // float offset of its partial lse values
 };
@@ -72,8 +91,13 @@ struct DecodeArgs {
   const void* v_resp;
   void* o;
   float* lse;
-  void* part_o;             // bf16 partials (bf16 kernel) or float32 (f32 kernel)
+  void* part_o;             // partial outputs: bf16 (separate merge) or float32
   float* part_lse;
+  int32_t* sync;            // in-kernel merge: sync words (nullptr: separate merge kernel)
+  int32_t n_groups;         // merge groups of this launch
+  int32_t merge_kind;       // bf16 kernel: 0 separate merge, 1 in-kernel over float32, 2 over bf16 partials
+  int32_t grid_wg;          // workgroups launched (in-kernel merge: 8 x the largest XCD share)
+  int32_t xcd_grp[kXcdGroups + 1];   // in-kernel merge: XCD x runs groups [xcd_grp[x], xcd_grp[x + 1])
   int32_t n_chunks_per_seq, k_max, b;
   int32_t compact;          // 1: a chunk's kept rows are rows 1..b of its slot (keep_rows unused)
   int32_t l_d, h_q, h_kv, group;

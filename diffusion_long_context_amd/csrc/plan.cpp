@@ -27,15 +27,65 @@ namespace {
 constexpr double kFixedTiles = 2.0;        // c0: per-workgroup overhead in tile-times
 constexpr double kMergeBase = 1.0;         // merge launch + pass, in tile-times
 constexpr double kMergePerSplit = 0.25;    // partial write + read per split
+constexpr int kFusedBf16Merge = 3;         // merge option: in-kernel over bf16 partials
+// The library's choice for bf16 inputs: the separate merge kernel.  Merging
+// in the decode launch measured slower on every workload here (32K prefix:
+// 57-59 against 44 us a call), because its tail -- partials through the L2,
+// arrival atomics, a slice merge -- is longer than a kernel boundary plus the
+// merge kernel.
+constexpr int kDefaultBf16Merge = 1;
+constexpr double kFusedMergeBase = 0.75;   // in-kernel merge: arrival, wait and one slice
+constexpr double kFusedMergePerSplit = 0.05;
 constexpr int kResidentBf16Large = 1;      // 8-wave bf16 workgroups per CU
-constexpr int kResidentBf16Small = 2;      // 4-wave bf16 workgroups per CU
+constexpr int kResidentBf16Small = 1;      // 4-wave bf16 workgroups per CU (over 256 registers per lane)
 constexpr int kResidentF32 = 4;
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Ranges needed when no range may sum above `cap` (greedy from the front).
+int ranges_needed(const std::vector<int>& sizes, int64_t cap) {
+  int n = 1;
+  int64_t cur = 0;
+  for (int v : sizes) {
+    if (cur + v > cap) {
+      ++n;
+      cur = 0;
+    }
+    cur += v;
+  }
+  return n;
+}
 }  // namespace
 
+int64_t xcd_partition(const std::vector<int>& sizes, int32_t* bounds) {
+  int64_t lo = 0, hi = 0;
+  for (int v : sizes) {
+    lo = std::max<int64_t>(lo, v);
+    hi += v;
+  }
+  while (lo < hi) {               // smallest cap that kXcdGroups ranges can meet
+    const int64_t mid = (lo + hi) / 2;
+    if (ranges_needed(sizes, mid) <= kXcdGroups)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  int x = 0;
+  int64_t cur = 0;
+  bounds[0] = 0;
+  for (int i = 0; i < (int)sizes.size(); ++i) {
+    if (cur + sizes[i] > lo) {
+      bounds[++x] = i;
+      cur = 0;
+    }
+    cur += sizes[i];
+  }
+  while (x < kXcdGroups) bounds[++x] = (int32_t)sizes.size();
+  return lo;
+}
+
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
-                 int d, int dtype, int num_splits, int force_rows, int n_cu, DecodePlan* plan,
+                 int d, int dtype, int num_splits, int force_rows, int merge, int n_cu, DecodePlan* plan,
                  const char** err) {
   if (n_seq < 1 || l_d < 1 || h_q < 1 || h_kv < 1 || d < 1 || b < 0 || num_splits < 0 ||
       n_cu < 1 || h_q % h_kv != 0 || k_per_seq == nullptr || plan == nullptr) {
@@ -45,6 +95,8 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
   }
   const int group = h_q / h_kv;
   const int64_t q_rows = (int64_t)l_d * group;
+  if (merge == 0) merge = dtype == 1 ? kDefaultBf16Merge : 1;
+  const bool fused = dtype == 1 && merge != 1;
   DecodePlan p;
   p.n_seq = n_seq;
   p.k_s.resize(n_seq);
@@ -109,9 +161,19 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
           longest = std::max(longest, std::min(tps, p.n_tiles[s]));
           n_wg += (int64_t)h_kv * q_tiles * ns;
         }
-        const double rounds = std::ceil((double)n_wg / slots);
+        double rounds = std::ceil((double)n_wg / slots);
+        if (fused) {
+          // every split of a group on one XCD: rounds of the fullest XCD
+          std::vector<int> sizes;
+          for (int s = 0; s < std::min(n_seq, kMaxSeqPerLaunch); ++s)
+            for (int64_t k = 0; k < (int64_t)h_kv * q_tiles; ++k) sizes.push_back(splits_for(s, tps));
+          int32_t bounds[kXcdGroups + 1];
+          const double per_xcd = std::max(1.0, std::floor(slots / kXcdGroups));
+          rounds = std::max(rounds, std::ceil((double)xcd_partition(sizes, bounds) / per_xcd));
+        }
         double t = rounds * (longest + kFixedTiles);
-        if (max_splits > 1) t += kMergeBase + kMergePerSplit * max_splits;
+        if (max_splits > 1)
+          t += fused ? kFusedMergeBase + kFusedMergePerSplit * max_splits : kMergeBase + kMergePerSplit * max_splits;
         if (t < best - 1e-9) {      // strictly better: ties keep fewer splits, larger tiles
           best = t;
           best_tps = tps;
@@ -132,19 +194,31 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
   p.lse_off.assign(n_seq, 0);
   int64_t part = 0, lse = 0;
   p.total_workgroups = 0;
+  // rows of one split's partial: the output rows (separate merge kernel), or
+  // every row of the sequence's workgroups, padding included (in-kernel merge)
+  const int64_t split_rows = fused ? per_split_wg * p.q_rows_per_wg : (int64_t)l_d * h_q;
   for (int s = 0; s < n_seq; ++s) {
     p.total_workgroups += per_split_wg * p.splits[s];
     if (p.splits[s] > 1) {
       p.part_off[s] = part;
       p.lse_off[s] = lse;
-      part += (int64_t)p.splits[s] * l_d * h_q * d;
-      lse += (int64_t)p.splits[s] * l_d * h_q;
+      part += (int64_t)p.splits[s] * split_rows * d;
+      lse += (int64_t)p.splits[s] * split_rows;
     }
   }
   p.part_floats = part;
   p.lse_floats = lse;
-  p.part_elem_bytes = dtype == 1 ? 2 : 4;   // bf16 partial outputs for bf16 inputs
-  p.workspace_bytes = part ? align256(part * p.part_elem_bytes) + align256(lse * 4) : 0;
+  // bf16 partial outputs for a separate merge kernel over bf16 inputs;
+  // float32 or bf16 (merge 3) for the in-kernel merge; float32 for the f32 path
+  p.fused = fused && part > 0;
+  p.fused_bf16 = p.fused && merge == kFusedBf16Merge;
+  p.part_elem_bytes = dtype == 1 && (!p.fused || p.fused_bf16) ? 2 : 4;
+  if (p.fused) {
+    const int64_t groups = (int64_t)std::min(n_seq, kMaxSeqPerLaunch) * h_kv * p.q_tiles;
+    p.sync_words = 2 + groups * (1 + p.q_rows_per_wg / 32);
+    p.sync_bytes = align256(p.sync_words * 4);
+  }
+  p.workspace_bytes = part ? p.sync_bytes + align256(part * p.part_elem_bytes) + align256(lse * 4) : 0;
   *plan = std::move(p);
   return true;
 }

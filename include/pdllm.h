@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 8
+#define PDLLM_ABI_VERSION 9
 
 typedef enum {
   PDLLM_OK = 0,
@@ -338,10 +338,18 @@ size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_pag
  *   lse      device [n_seq][h_q][l_d] float out, nullable: natural-log
  *            normaliser ln sum_a exp(scale <q, k_a>)
  *   workspace device, >= pdllm_split_attn_decode_workspace(...) for the same
- *            arguments (holds the per-split partial outputs -- in the pool dtype, each
- *            normalised by its own softmax sum -- and their float32 log-sum-exps)
- * The result does not depend on num_splits beyond rounding: with bf16 the
- * partials are rounded once to bf16 before the merge.
+ *            arguments, 16-byte aligned: the per-split partial outputs (each
+ *            normalised by its own softmax sum) and their float32
+ *            log-sum-exps.  When the splits are merged inside the decode
+ *            launch (pdllm_decode_opts.merge 2 or 3), the workspace begins
+ *            with synchronisation words that must be zero when a workspace is
+ *            first used -- zero-fill a new workspace once -- and that every
+ *            call returns to zero; keep such a workspace for decode calls, and
+ *            give calls that may overlap (other streams) workspaces of their
+ *            own.
+ * The result does not depend on num_splits beyond rounding: with bf16 inputs
+ * the partials are rounded once to bf16 before the merge (float32 with merge
+ * 2), with f32 inputs they are float32.
  * Supported: f32 with d in {16, 32, 64, 128}; bf16 with d in {64, 128}.
  */
 pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
@@ -359,11 +367,19 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
  *                  128 or 256 for bf16, 64 for f32 (PDLLM_ERR_UNSUPPORTED
  *                  for any other).  The result does not depend on it beyond
  *                  rounding; tests use it to run every kernel instance.
+ *   merge          how the splits are merged: 0 = the library's choice
+ *                  (1); 1 = a second kernel launch over partials stored in
+ *                  the pool dtype; 2 / 3 = inside the decode launch, over
+ *                  float32 / bf16 partials exchanged through the L2 of one
+ *                  XCD (bf16 inputs only, PDLLM_ERR_UNSUPPORTED for f32).
+ *                  With 2 and 3 the workspace holds synchronisation words,
+ *                  see pdllm_split_attn_decode.
  */
 typedef struct {
   int32_t num_splits;
   int32_t q_rows_per_wg;
-  int32_t reserved[6];              /* must be 0 */
+  int32_t merge;
+  int32_t reserved[5];              /* must be 0 */
 } pdllm_decode_opts;
 
 /* pdllm_split_attn_decode_workspace with options (0 when invalid). */

@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 8
+    assert L.lib.pdllm_abi_version() == 9
 
 
 def _pool(**kw):
@@ -157,13 +157,28 @@ def test_decode_forced_shape_plans():
     workspace equals the options call's with the same split count."""
     pool = _pool()
     pt, _keep = _pt([16])
-    q = lambda rows, ns: L.lib.pdllm_split_attn_decode_ex_workspace(
-        ctypes.byref(pool), ctypes.byref(pt), 1, 256, 28, ctypes.byref(L.DecodeOpts(ns, rows)))
+    q = lambda rows, ns, merge=0: L.lib.pdllm_split_attn_decode_ex_workspace(
+        ctypes.byref(pool), ctypes.byref(pt), 1, 256, 28, ctypes.byref(L.DecodeOpts(ns, rows, merge)))
     for ns in (0, 3):
         assert q(0, ns) == L.lib.pdllm_split_attn_decode_workspace(ctypes.byref(pool), ctypes.byref(pt), 1, 256,
                                                                    28, ns)
-    # forced split counts: the workspace does not depend on the workgroup shape
-    assert q(128, 5) == q(256, 5) == q(0, 5)
+    # forced split counts, separate merge kernel: bf16 partials + float32 lse,
+    # independent of the workgroup shape
+    part = 5 * 256 * 28 * 128 * 2
+    lse = 5 * 256 * 28 * 4
+    assert q(128, 5, 1) == q(256, 5, 1) == q(0, 5, 1) == part + lse
+    # in-kernel merge: sync words first -- 2 + one arrival and rows / 32
+    # claim words per (kv head, query tile) group -- then the partials (bf16
+    # by default and with merge 3, float32 with merge 2) and float32 lse
+    for rows in (128, 256):
+        groups = 4 * (256 * 7 // rows)
+        sync = -(-4 * (2 + groups * (1 + rows // 32)) // 256) * 256
+        assert q(rows, 5, 3) == sync + part + lse
+        assert q(rows, 5, 2) == sync + 2 * part + lse
+        assert q(rows, 5) == part + lse                 # the default: a separate merge kernel
+    assert L.lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(_pool(dtype=0)), ctypes.byref(pt), 1, 256, 28,
+                                                      ctypes.byref(L.DecodeOpts(5, 0, 2))) == 0
+    assert "bf16 only" in _err()
 
 
 def test_noalloc_decode_validation():
