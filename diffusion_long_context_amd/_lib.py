@@ -46,7 +46,7 @@ EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_
            "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
            "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows",
            "pdllm_prefill_select", "pdllm_split_attn_decode_ex_workspace", "pdllm_split_attn_decode_ex",
-           "pdllm_split_attn_decode_noalloc")
+           "pdllm_split_attn_decode_noalloc", "pdllm_gather_kept_kv")
 
 
 def _load() -> ctypes.CDLL:
@@ -84,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_split_attn_decode_noalloc.restype = ctypes.c_int
     lib.pdllm_split_attn_decode_noalloc.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32, i32,
                                                     vp, vp, vp]
+    lib.pdllm_gather_kept_kv.restype = ctypes.c_int
+    lib.pdllm_gather_kept_kv.argtypes = [P(Pool), P(PageTable), i32, vp, vp, i64, i64, i64, vp]
     lib.pdllm_chunk_score_workspace.restype = sz
     lib.pdllm_chunk_score_workspace.argtypes = [i32, i32, i32]
     lib.pdllm_chunk_score.restype = ctypes.c_int
@@ -316,6 +318,31 @@ def compact_kept_rows(pool_k, pool_v, chunk_slot, keep_rows, dst_k=None, dst_v=N
                                        dst_v.data_ptr(), dst_k.stride(0), dst_k.stride(1),
                                        dst_k.stride(2), dst_k.shape[1], _stream(pool_k.device)),
            "pdllm_compact_kept_rows")
+    return dst_k, dst_v
+
+
+def gather_kept_kv(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, dst_k=None, dst_v=None):
+    """pdllm_gather_kept_kv: the attended pool rows of each sequence, gathered
+    contiguously -- [n_seq * k_max][b + 1][h_kv][d] tensors (new, or the
+    given dst_k / dst_v), where sequence s's K_s (b + 1) rows start at slot
+    s * k_max.  Returns (dst_k, dst_v)."""
+    pool = make_pool(pool_k, pool_v)
+    for t, name in ((chunk_slot, "chunk_slot"), (sel_chunk, "sel_chunk"), (keep_rows, "keep_rows")):
+        _dense(t, name, torch.int32)
+    n_seq, k_max = sel_chunk.shape
+    b = keep_rows.shape[1]
+    if len(k_per_seq) != n_seq or chunk_slot.numel() % n_seq or keep_rows.shape[0] != chunk_slot.numel():
+        raise ValueError("page table shapes do not agree")
+    if dst_k is None:
+        shape = (max(n_seq * k_max, 1), b + 1, pool.h_kv, pool.d)
+        dst_k = torch.empty(shape, dtype=pool_k.dtype, device=pool_k.device)
+        dst_v = torch.empty(shape, dtype=pool_k.dtype, device=pool_k.device)
+    ks = (ctypes.c_int32 * n_seq)(*[int(x) for x in k_per_seq])
+    pt = PageTable(chunk_slot.data_ptr(), sel_chunk.data_ptr(), keep_rows.data_ptr(), ctypes.cast(ks, ctypes.c_void_p),
+                   chunk_slot.numel() // n_seq, k_max, b, 0)
+    _check(lib.pdllm_gather_kept_kv(ctypes.byref(pool), ctypes.byref(pt), n_seq, dst_k.data_ptr(), dst_v.data_ptr(),
+                                    dst_k.stride(0), dst_k.stride(1), dst_k.stride(2), _stream(pool_k.device)),
+           "pdllm_gather_kept_kv")
     return dst_k, dst_v
 
 

@@ -8,6 +8,13 @@
 // compacted pool then reads each selected chunk's b + 1 rows from
 // consecutive slot rows.
 //
+// The same kernel gathers a decode's attended pool rows into one contiguous
+// run per sequence (sel_chunk set): unit u = s k_max + k copies selected
+// chunk c = sel_chunk[s][k] of sequence s (slot chunk_slot[s N + c]) to
+// destination slot u, so with b + 1 rows per destination slot sequence s's
+// rows sit contiguously, in the decode's order (the gather-to-contiguous
+// copy that reading the pool in place avoids, kept as a comparator).
+//
 // Design for CDNA4: a pure copy, so the bound is HBM bandwidth.  The work of
 // one (chunk, tensor) is a flat run of 16-byte vectors ordered (row, head,
 // vector); each thread moves kCompactVec of them, kCompactThreads apart, with
@@ -25,13 +32,24 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactA
   // adjacent, so one chunk's index row is read by neighbouring workgroups
   const int blk = blockIdx.x % a.blocks;
   const int ct = blockIdx.x / a.blocks;
-  const int c = ct >> 1;
+  const int unit = ct >> 1;
   const bool is_v = ct & 1;
   const char* src = is_v ? a.src_v : a.src_k;
   char* dst = is_v ? a.dst_v : a.dst_k;
   const int per_row = a.h_kv * a.nvec;
   const int total = (a.b + 1) * per_row;
   const int f0 = blk * kCompactThreads * kCompactVec + (int)threadIdx.x;
+  int c = unit;
+  int64_t dslot;
+  if (a.sel_chunk != nullptr) {            // gather: unit = (sequence, selected index)
+    const int s = unit / a.k_max;
+    const int sel = a.sel_chunk[unit];
+    if (sel < 0 || unit - s * a.k_max >= a.k_s[s]) return;   // not selected (uniform)
+    c = s * a.n_chunks_per_seq + sel;
+    dslot = unit;
+  } else {
+    dslot = a.chunk_slot[c];
+  }
   const int64_t slot = a.chunk_slot[c];
   typedef __attribute__((address_space(1))) const u32x4* gvec;
   typedef __attribute__((address_space(1))) const int32_t* gptr32;
@@ -63,7 +81,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(const CompactA
     if (f0 + u * kCompactThreads >= total || (r[u] > 0 && row[u] < 0)) continue;
     const int h = rem[u] / a.nvec;
     const int vv = rem[u] - h * a.nvec;
-    *reinterpret_cast<u32x4*>(dst + slot * a.ds + (int64_t)r[u] * a.dr + (int64_t)h * a.dh + 16 * (int64_t)vv) =
+    *reinterpret_cast<u32x4*>(dst + dslot * a.ds + (int64_t)r[u] * a.dr + (int64_t)h * a.dh + 16 * (int64_t)vv) =
         w[u];
   }
 }

@@ -434,6 +434,56 @@ pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk
   return st != PDLLM_OK ? st : ok();
 }
 
+pdllm_status pdllm_gather_kept_kv(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq, void* dst_k,
+                                  void* dst_v, int64_t dst_stride_slot, int64_t dst_stride_row,
+                                  int64_t dst_stride_head, void* stream) {
+  pdllm_status st = check_decode(pool, pt, n_seq, 1, pool != nullptr ? pool->h_kv : 1, 0);
+  if (st != PDLLM_OK) return st;
+  if (pt->rows_compacted) return fail(PDLLM_ERR_UNSUPPORTED, "gather: the pool must hold whole chunks");
+  if (n_seq > pdllm::kMaxGatherSeq)
+    return fail(PDLLM_ERR_UNSUPPORTED, "gather: %d sequences > %d", n_seq, pdllm::kMaxGatherSeq);
+  // the destination passes the same checks as a pool of n_seq * k_max slots of b + 1 rows
+  pdllm_pool dst = *pool;
+  dst.k = dst_k;
+  dst.v = dst_v;
+  dst.stride_slot = dst_stride_slot;
+  dst.stride_row = dst_stride_row;
+  dst.stride_head = dst_stride_head;
+  dst.slot_rows = pt->b + 1;
+  dst.n_slots = std::max(1, n_seq * pt->k_max);
+  if ((st = check_pool(&dst)) != PDLLM_OK) return st;
+  if (pt->k_max == 0) return ok();
+  const int64_t es = elem_bytes(pool->dtype);
+  pdllm::CompactArgs a{};
+  a.src_k = static_cast<const char*>(pool->k);
+  a.src_v = static_cast<const char*>(pool->v);
+  a.dst_k = static_cast<char*>(dst_k);
+  a.dst_v = static_cast<char*>(dst_v);
+  a.ss = pool->stride_slot * es;
+  a.sr = pool->stride_row * es;
+  a.sh = pool->stride_head * es;
+  a.ds = dst_stride_slot * es;
+  a.dr = dst_stride_row * es;
+  a.dh = dst_stride_head * es;
+  a.chunk_slot = pt->chunk_slot;
+  a.keep_rows = pt->keep_rows;
+  a.n_chunks = n_seq * pt->k_max;
+  a.b = pt->b;
+  a.h_kv = pool->h_kv;
+  a.nvec = (int32_t)(pool->d * es / 16);
+  a.sel_chunk = pt->sel_chunk;
+  a.k_max = pt->k_max;
+  a.n_chunks_per_seq = pt->n_chunks_per_seq;
+  for (int s = 0; s < n_seq; ++s) a.k_s[s] = pt->k_per_seq[s];
+  const int64_t total = (int64_t)(pt->b + 1) * pool->h_kv * a.nvec;
+  const int64_t per_wg = (int64_t)pdllm::kCompactThreads * pdllm::kCompactVec;
+  a.blocks = (int32_t)((total + per_wg - 1) / per_wg);
+  if (total > INT32_MAX / 2 || (int64_t)a.n_chunks * 2 * a.blocks > INT32_MAX)
+    return fail(PDLLM_ERR_UNSUPPORTED, "gather grid too large");
+  st = hip_status(pdllm::launch_compact(a, stream), "gather launch");
+  return st != PDLLM_OK ? st : ok();
+}
+
 size_t pdllm_chunk_score_workspace(int32_t n_chunks, int32_t n_query, int32_t n_pseudo) {
   if (n_chunks < 0 || n_query < 0 || n_pseudo < 0) return 0;
   return (size_t)(((int64_t)n_chunks * (n_query + n_pseudo) * 4 + 255) / 256 * 256);

@@ -192,6 +192,7 @@ struct ChunkScoreArgs {
 int launch_chunk_score(const ChunkScoreArgs& a, void* stream);
 
 // ---------------------------------------------------------------- kept-row compaction
+constexpr int kMaxGatherSeq = 64;        // sequences one gather launch carries
 struct CompactArgs {
   const char* src_k;
   const char* src_v;
@@ -204,7 +205,13 @@ struct CompactArgs {
   int32_t n_chunks, b, h_kv;
   int32_t nvec;             // 16-byte vectors per (row, head)
   int32_t blocks;           // workgroups per (chunk, tensor)
+  // gather (sel_chunk set): n_chunks = n_seq * k_max units, unit s k_max + k
+  // copies selected chunk sel_chunk[unit] of sequence s (if k < k_s[s]) to slot unit
+  const int32_t* sel_chunk;
+  int32_t k_max, n_chunks_per_seq;
+  int32_t k_s[kMaxGatherSeq];
 };
+
 constexpr int kCompactThreads = 256;
 constexpr int kCompactVec = 4;           // 16-byte vectors per thread
 int launch_compact(const CompactArgs& a, void* stream);

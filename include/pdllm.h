@@ -229,6 +229,29 @@ pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk
                                      int64_t dst_stride_head, int32_t dst_slot_rows, void* stream);
 
 /*
+ * Gather-to-contiguous of a decode's attended pool rows: the copy that the
+ * split decode avoids by reading the non-contiguous pool in place
+ * ("Attention kernel optimization"), provided as the comparator that times
+ * it.  For sequence s and its k-th selected chunk c = sel_chunk[s][k]
+ * (k < K_s), in slot chunk_slot[s N + c], destination slot u = s k_max + k
+ * gets the chunk's BOS row, then its b kept rows in keep_rows order --
+ * exactly the rows, and the order, in which the decode attends them:
+ *   dst[u][0] = src[slot][0],   dst[u][1 + i] = src[slot][keep_rows[s N + c][i]].
+ * With dst_stride_slot = (b + 1) dst_stride_row, sequence s's K_s (b + 1) rows
+ * are one contiguous run starting at slot s k_max.  A decode over that run
+ * (one compacted chunk of K_s (b + 1) rows per sequence) attends the same
+ * rows in the same order.  Slots past K_s and rows of absent (-1) entries are
+ * not written.
+ *   pool, pt   as pdllm_split_attn_decode (pt->rows_compacted must be 0)
+ *   dst_k, dst_v  device, [n_seq k_max][b + 1][h_kv][d] with the given
+ *              element strides (the rules of a pdllm_pool's), the pool's dtype
+ * Supported: n_seq <= 64.
+ */
+pdllm_status pdllm_gather_kept_kv(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq, void* dst_k,
+                                  void* dst_v, int64_t dst_stride_slot, int64_t dst_stride_row,
+                                  int64_t dst_stride_head, void* stream);
+
+/*
  * The prefill side in one call: pdllm_chunk_prefill_score, then
  * pdllm_select_topB over its key scores, and pdllm_select_topK over the given
  * chunk scores, with the same outputs bit for bit.  The key-score finalize and
