@@ -53,12 +53,17 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 COPY_BYTES = 1 << 30             # --copy-calibration: bytes read (and written) per copy
 
-# Sources whose code the prefill stage's kernels are built from.
+# Sources whose code each stage's kernels are built from.
 PREFILL_SOURCES = ("diffusion_long_context_amd/csrc/prefill_bf16.hip",
                    "diffusion_long_context_amd/csrc/select.hip",
                    "diffusion_long_context_amd/csrc/attn_tile.h",
                    "diffusion_long_context_amd/csrc/device_common.h",
                    "diffusion_long_context_amd/csrc/pdllm_internal.h")
+DECODE_SOURCES = ("diffusion_long_context_amd/csrc/decode_bf16.hip",
+                  "diffusion_long_context_amd/csrc/attn_tile.h",
+                  "diffusion_long_context_amd/csrc/xwg_sync.h",
+                  "diffusion_long_context_amd/csrc/device_common.h",
+                  "diffusion_long_context_amd/csrc/pdllm_internal.h")
 
 # Kernels each stage launches (one launch of each per step on this workload).
 STAGE_KERNELS = {
@@ -66,22 +71,28 @@ STAGE_KERNELS = {
     "prefill": "prefill_bf16_kernel<128, 18, true> + score_finalize_kernel",
     "select_topb": "topb_kernel",
     "select_topk": "topk_kernel",
-    "decode": "decode_bf16_kernel<128, *> + lse_merge_kernel<128, bf16, *>",
+    "decode": "decode_bf16_kernel<128, 8, 0> + lse_merge_kernel<128, true, 12>",
 }
 
 # rocprofv3 counter readings (KiB per dispatch, mean over the dispatches of
-# the run) of the prefill stage's kernels on this workload, and of the plain
-# copy; None until taken.  Filled from the summaries kept with the profiles.
-PREFILL_COUNTERS = {
-    "sources_sha": "56faf14e1edd9bc8",
-    # the default step (only the kept chunks scored); other forms get no traffic figure
-    "kernels": {
-        "prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149365.95, "write_kib": 231490.18},
-        "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56},
+# the run) of each stage's kernels on this workload, and of the plain copy,
+# recorded with a hash of the sources they were taken on; the summaries are
+# profiles/step_32k_prefix_hbm_counters.md.
+COUNTERS = {
+    "prefill_select": {
+        "sources": PREFILL_SOURCES, "sources_sha": "3d22dea1ad13f786",
+        # the default step (only the kept chunks scored); other forms get no traffic figure
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149344.56, "write_kib": 231592.23},
+                    "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56}},
     },
-    "copy_fetch_kib": 524301.29,      # __amd_rocclr_copyBuffer of COPY_BYTES
-    "copy_write_kib": 1048576.0,
+    "decode": {
+        "sources": DECODE_SOURCES, "sources_sha": "027a9e3bb7e77f27",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7368.25, "write_kib": 17060.00},
+                    "lse_merge_kernel<128, true, 12>": {"fetch_kib": 8351.75, "write_kib": 1992.00}},
+    },
 }
+COPY_COUNTERS = {"copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
+                 "copy_write_kib": 1048576.0}
 
 
 def parse():
@@ -161,21 +172,16 @@ def sources_sha(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def prefill_traffic(fused: bool):
-    """HBM bytes of one prefill-stage launch (the prefill kernel and the
-    finalize of its key scores, fused with the selections or not) from the
-    recorded counters, scaled by the copy kernel's readings; None if not
-    taken on these sources."""
-    rec = PREFILL_COUNTERS
-    if rec is None or rec["sources_sha"] != sources_sha(PREFILL_SOURCES):
+def stage_traffic(stage: str):
+    """HBM bytes of one launch of a stage's kernels from the recorded
+    counters, each scaled by what it reads for the plain copy; None if they
+    were not taken on these sources."""
+    rec = COUNTERS.get(stage)
+    if rec is None or rec["sources_sha"] != sources_sha(rec["sources"]):
         return None
-    f_read = COPY_BYTES / (rec["copy_fetch_kib"] * 1024.0)
-    f_write = COPY_BYTES / (rec["copy_write_kib"] * 1024.0)
-    names = ["prefill_bf16_kernel<128, 18, true>", "finalize_select_kernel" if fused else "score_finalize_kernel"]
-    if any(n not in rec["kernels"] for n in names):
-        return None
-    return sum(rec["kernels"][n]["fetch_kib"] * 1024.0 * f_read + rec["kernels"][n]["write_kib"] * 1024.0 * f_write
-               for n in names)
+    f_read = COPY_BYTES / (COPY_COUNTERS["copy_fetch_kib"] * 1024.0)
+    f_write = COPY_BYTES / (COPY_COUNTERS["copy_write_kib"] * 1024.0)
+    return sum(k["fetch_kib"] * 1024.0 * f_read + k["write_kib"] * 1024.0 * f_write for k in rec["kernels"].values())
 
 
 def copy_calibration():
@@ -807,8 +813,8 @@ def main():
     step_flops = sum(flops[n] for n in names)
     value = step_flops / (step_ms * 1e-3) / 1e12
 
-    traffic = {"prefill_select": prefill_traffic(True) if not args.score_all else None,
-               "prefill": prefill_traffic(False)}
+    traffic = {"prefill_select": stage_traffic("prefill_select") if not args.score_all else None,
+               "decode": stage_traffic("decode") if args.decode_merge in (0, 1) else None}
 
     peaks = measured_peaks()
 
@@ -865,8 +871,9 @@ def main():
                          "frac_of_measured_mfma": d["frac_measured"], "target_frac": 0.5, "target_us": 12.8}
     for r in (out["roofline"], *out["rooflines"].values()):
         if r.get("traffic") is not None:
-            r["traffic_source"] = ("rocprofv3 FETCH_SIZE / WRITE_SIZE passes recorded for these kernel sources "
-                                   "(profiles/step_32k_prefix_hbm_counters.md), scaled by a plain copy's readings")
+            r["traffic_source"] = ("stored rocprofv3 FETCH_SIZE / WRITE_SIZE readings taken on these kernel "
+                                   "sources (profiles/step_32k_prefix_hbm_counters.md), scaled by a plain "
+                                   "copy's readings; null once the sources change")
     if not args.no_extras and "decode" in stage_ms:
         dev_in = (pool_k, pool_v, chunk_slot, sel, keep, q, k_resp, v_resp)
         out["comparators"] = comparators_run(cfg, dev_in, decode, args.seed)
