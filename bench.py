@@ -71,7 +71,7 @@ STAGE_KERNELS = {
     "prefill": "prefill_bf16_kernel<128, 18, true> + score_finalize_kernel",
     "select_topb": "topb_kernel",
     "select_topk": "topk_kernel",
-    "decode": "decode_bf16_kernel<128, 8, 0> + lse_merge_kernel<128, true, 12>",
+    "decode": "decode_bf16_kernel<128, 8, 0> + lse_merge_kernel<128, true, true, 12>",
 }
 
 # rocprofv3 counter readings (KiB per dispatch, mean over the dispatches of
@@ -80,15 +80,15 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "3d22dea1ad13f786",
+        "sources": PREFILL_SOURCES, "sources_sha": "0410efcac58b8453",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149344.56, "write_kib": 231592.23},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149381.17, "write_kib": 231422.48},
                     "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "027a9e3bb7e77f27",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7368.25, "write_kib": 17060.00},
-                    "lse_merge_kernel<128, true, 12>": {"fetch_kib": 8351.75, "write_kib": 1992.00}},
+        "sources": DECODE_SOURCES, "sources_sha": "5b7210ed3ad54e83",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7363.00, "write_kib": 16637.79},
+                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8351.75, "write_kib": 1992.00}},
     },
 }
 COPY_COUNTERS = {"copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
@@ -108,10 +108,10 @@ def parse():
                    help="score every chunk (top-B for all chunks), not only the K kept ones")
     p.add_argument("--unfused", action="store_true",
                    help="run the prefill side as three calls (prefill + scoring, top-B, top-K)")
-    p.add_argument("--decode-merge", type=int, default=0, choices=(0, 1, 2, 3),
+    p.add_argument("--decode-merge", type=int, default=0, choices=(0, 1, 2, 3, 4),
                    help="how the decode merges its splits: 0 the library's choice, 1 a separate merge "
-                        "kernel, 2 / 3 inside the decode launch over float32 / bf16 partials "
-                        "(pdllm_decode_opts.merge)")
+                        "kernel, 2 / 3 inside the decode launch over float32 / bf16 partials, 4 a "
+                        "separate merge kernel over float32 partials (pdllm_decode_opts.merge)")
     p.add_argument("--decode-only", action="store_true",
                    help="time only the decode call (diagnostic; not the headline step)")
     p.add_argument("--full-step", action="store_true",

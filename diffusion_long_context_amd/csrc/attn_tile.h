@@ -306,4 +306,17 @@ __device__ __forceinline__ void store_o_bf16(uint16_t* row_plus_8j, const f32x16
     }
 }
 
+// Store a wavefront's O^T columns (times inv) as float32 rows: lane (c, j)
+// holds d = 32 db + 8 m + 4 j + t (t = 0..3) of row c in registers 4 m + t
+// of block db, 16 bytes per store.  row = &O[row][0].
+template <int DB>
+__device__ __forceinline__ void store_o_f32(float* row, const f32x16 (&acc)[DB], float inv, int j) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<f32x4*>(row + 32 * db + 8 * m + 4 * j) =
+          f32x4{acc[db][4 * m] * inv, acc[db][4 * m + 1] * inv, acc[db][4 * m + 2] * inv, acc[db][4 * m + 3] * inv};
+}
+
 }  // namespace pdllm

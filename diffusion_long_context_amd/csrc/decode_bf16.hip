@@ -285,11 +285,11 @@ __device__ __forceinline__ void merge_group(const A& a, Sm& sm, int tid, int si,
   }
 }
 
-// MERGE: 0 = partials for the separate merge kernel (bf16, row-major);
-// 1 / 2 = merged in this launch over float32 / bf16 partials.
+// MERGE: 0 / 3 = partials for the separate merge kernel (bf16 / float32,
+// row-major); 1 / 2 = merged in this launch over float32 / bf16 partials.
 template <int D, int WAVES, int MERGE>
 __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArgs a) {
-  constexpr bool FUSED = MERGE != 0;
+  constexpr bool FUSED = MERGE == 1 || MERGE == 2;   // the merge runs in this launch
   constexpr bool PBF16 = MERGE == 2;
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 32 * WAVES;        // query rows of the workgroup
@@ -598,9 +598,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     }
   } else if constexpr (!FUSED) {
     if (row_ok) {
-      store_o_bf16<DB>(static_cast<uint16_t*>(a.part_o) + a.seq[si].part_off +
-                           (((int64_t)split * a.l_d + i) * a.h_q + h) * D + 8 * lj,
-                       at.acc, inv);
+      const int64_t prow = a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D;
+      if constexpr (MERGE == 3)
+        store_o_f32<DB>(static_cast<float*>(a.part_o) + prow, at.acc, inv, lj);
+      else
+        store_o_bf16<DB>(static_cast<uint16_t*>(a.part_o) + prow + 8 * lj, at.acc, inv);
       if (lj == 0) a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;
     }
   } else {
@@ -652,11 +654,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
 
 // LSE merge of the per-split partials ("Attention kernel optimization"):
 // lse = M + ln sum_j exp(lse_j - M), o = sum_j exp(lse_j - lse) o_j, summed
-// in float32 and rounded once to the output type.  With BF16 the partial
-// outputs are bf16 (the bf16 decode kernel writes them so) and each thread
-// takes 8 values of a row, otherwise float32 and 4 values.
-template <int D, bool BF16, int kBatch>
+// in float32 and rounded once to the output type.  With PBF16 the partial
+// outputs are bf16 and each thread takes 8 values of a row, otherwise
+// float32 and 4 values; OBF16: o is bf16 (else float32).
+template <int D, bool PBF16, bool OBF16, int kBatch>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
+  constexpr bool BF16 = PBF16;
   constexpr int EPT = BF16 ? 8 : 4;        // values per thread (16 bytes of partial)
   constexpr int TPR = D / EPT;
   constexpr int RPB = 256 / TPR;
@@ -729,6 +732,9 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
     *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + out) =
         u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
               pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+  } else if constexpr (OBF16) {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + out) =
+        u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + out) =
         f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
@@ -736,22 +742,22 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
   if (a.lse != nullptr && e0 == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = (mx + __log2f(tot)) * kLn2;
 }
 
-template <int D, bool BF16>
+template <int D, bool PBF16, bool OBF16>
 int merge_launch(const DecodeArgs& a, void* stream) {
-  constexpr int RPB = 256 / (D / (BF16 ? 8 : 4));
+  constexpr int RPB = 256 / (D / (PBF16 ? 8 : 4));
   const int rows = a.l_d * a.h_q;
   dim3 grid((rows + RPB - 1) / RPB, a.n_seq_launch);
   int ns = 1;
   for (int i = 0; i < a.n_seq_launch; ++i) ns = max(ns, a.seq[i].n_splits);
   const hipStream_t st = (hipStream_t)stream;
   if (ns <= 4)
-    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((lse_merge_kernel<D, PBF16, OBF16, 4>), grid, dim3(256), 0, st, a);
   else if (ns <= 8)
-    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 8>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((lse_merge_kernel<D, PBF16, OBF16, 8>), grid, dim3(256), 0, st, a);
   else if (ns <= 12)
-    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 12>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((lse_merge_kernel<D, PBF16, OBF16, 12>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((lse_merge_kernel<D, BF16, 16>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((lse_merge_kernel<D, PBF16, OBF16, 16>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -779,16 +785,26 @@ int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stre
     case 0: return launch_decode_bf16_t<0>(a, d, q_rows_per_wg, st);
     case 1: return launch_decode_bf16_t<1>(a, d, q_rows_per_wg, st);
     case 2: return launch_decode_bf16_t<2>(a, d, q_rows_per_wg, st);
+    case 3: return launch_decode_bf16_t<3>(a, d, q_rows_per_wg, st);
     default: return (int)hipErrorInvalidValue;
   }
 }
 
-int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_out, void* stream) {
+int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_part, bool bf16_out, void* stream) {
+  if (bf16_part && !bf16_out) return (int)hipErrorInvalidValue;
+  // (bf16 partials, bf16 o) for bf16 inputs, (float32, bf16) for bf16 inputs
+  // with float32 partials, (float32, float32) for float32 inputs
   switch (d) {
-    case 16: return bf16_out ? merge_launch<16, true>(a, stream) : merge_launch<16, false>(a, stream);
-    case 32: return bf16_out ? merge_launch<32, true>(a, stream) : merge_launch<32, false>(a, stream);
-    case 64: return bf16_out ? merge_launch<64, true>(a, stream) : merge_launch<64, false>(a, stream);
-    case 128: return bf16_out ? merge_launch<128, true>(a, stream) : merge_launch<128, false>(a, stream);
+    case 16: return bf16_out ? merge_launch<16, false, true>(a, stream) : merge_launch<16, false, false>(a, stream);
+    case 32: return bf16_out ? merge_launch<32, false, true>(a, stream) : merge_launch<32, false, false>(a, stream);
+    case 64:
+      return bf16_part  ? merge_launch<64, true, true>(a, stream)
+             : bf16_out ? merge_launch<64, false, true>(a, stream)
+                        : merge_launch<64, false, false>(a, stream);
+    case 128:
+      return bf16_part  ? merge_launch<128, true, true>(a, stream)
+             : bf16_out ? merge_launch<128, false, true>(a, stream)
+                        : merge_launch<128, false, false>(a, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -196,9 +196,9 @@ pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32
       return fail(PDLLM_ERR_UNSUPPORTED, "q_rows_per_wg %d is not a workgroup shape of the %s kernel", rows,
                   pool->dtype == PDLLM_BF16 ? "bf16 (128, 256)" : "f32 (64)");
   }
-  if (opts->merge < 0 || opts->merge > 3)
-    return fail(PDLLM_ERR_INVALID_ARG, "merge must be 0, 1, 2 or 3 (got %d)", opts->merge);
-  if (opts->merge >= 2 && pool->dtype != PDLLM_BF16)
+  if (opts->merge < 0 || opts->merge > 4)
+    return fail(PDLLM_ERR_INVALID_ARG, "merge must be 0 .. 4 (got %d)", opts->merge);
+  if ((opts->merge == 2 || opts->merge == 3) && pool->dtype != PDLLM_BF16)
     return fail(PDLLM_ERR_UNSUPPORTED, "the in-kernel merge is implemented for bf16 only");
   const char* err = "";
   if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
@@ -589,7 +589,7 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
   if (plan.workspace_bytes > 0) {
     char* w = static_cast<char*>(workspace);
     if (plan.fused) a.sync = reinterpret_cast<int32_t*>(w);
-    a.merge_kind = plan.fused ? (plan.fused_bf16 ? 2 : 1) : 0;
+    a.merge_kind = plan.fused ? (plan.fused_bf16 ? 2 : 1) : plan.sep_f32 ? 3 : 0;
     a.part_o = w + plan.sync_bytes;
     const int64_t part_bytes = (plan.part_floats * plan.part_elem_bytes + 255) / 256 * 256;
     a.part_lse = reinterpret_cast<float*>(w + plan.sync_bytes + part_bytes);
@@ -639,7 +639,8 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
                                              : pdllm::launch_decode_f32(la, pool->d, stream);
     if ((st = hip_status(e, "decode launch")) != PDLLM_OK) return st;
     if (merges[i] && !plan.fused) {
-      st = hip_status(pdllm::launch_lse_merge(la, pool->d, pool->dtype == PDLLM_BF16, stream), "merge launch");
+      const bool bf16 = pool->dtype == PDLLM_BF16;
+      st = hip_status(pdllm::launch_lse_merge(la, pool->d, bf16 && !plan.sep_f32, bf16, stream), "merge launch");
       if (st != PDLLM_OK) return st;
     }
   }

@@ -34,6 +34,7 @@ struct DecodePlan {
   // count and one claim count per 32-row slice).
   bool fused = false;
   bool fused_bf16 = false;                  // in-kernel merge over bf16 (else float32) partials
+  bool sep_f32 = false;                     // bf16 inputs, separate merge kernel over float32 partials
   int64_t sync_words = 0;
   int64_t sync_bytes = 0;                   // 256-aligned; the partials follow
   int64_t workspace_bytes = 0;
@@ -43,9 +44,10 @@ struct DecodePlan {
 // Fills `plan`; returns false (with a message in *err) on invalid input.
 // force_rows > 0 fixes the query rows per workgroup (a shape of the dtype's
 // kernel, checked by the caller); 0 lets the planner choose.
-// merge: 0 = the library's choice (in-kernel for bf16), 1 = a separate merge
-// kernel, 2 / 3 = in-kernel over float32 / bf16 partials (bf16 only; the
-// caller checked).
+// merge: 0 = the library's choice (1), 1 = a separate merge kernel over
+// partials in the input dtype, 2 / 3 = in-kernel over float32 / bf16
+// partials (bf16 only; the caller checked), 4 = a separate merge kernel over
+// float32 partials (the same as 1 for float32 inputs).
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
                  int d, int dtype, int num_splits, int force_rows, int merge, int n_cu, DecodePlan* plan,
                  const char** err);
@@ -95,7 +97,8 @@ struct DecodeArgs {
   float* part_lse;
   int32_t* sync;            // in-kernel merge: sync words (nullptr: separate merge kernel)
   int32_t n_groups;         // merge groups of this launch
-  int32_t merge_kind;       // bf16 kernel: 0 separate merge, 1 in-kernel over float32, 2 over bf16 partials
+  int32_t merge_kind;       // bf16 kernel: 0 / 3 separate merge over bf16 / float32 partials,
+                            // 1 / 2 in-kernel over float32 / bf16 partials
   int32_t grid_wg;          // workgroups launched (in-kernel merge: 8 x the largest XCD share)
   int32_t xcd_grp[kXcdGroups + 1];   // in-kernel merge: XCD x runs groups [xcd_grp[x], xcd_grp[x + 1])
   int32_t n_chunks_per_seq, k_max, b;
@@ -112,7 +115,8 @@ struct DecodeArgs {
 // Launchers (return a hipError_t value as int).
 int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream);
 int launch_decode_f32(const DecodeArgs& a, int d, void* stream);
-int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_out, void* stream);
+// bf16_part: the partials are bf16 (else float32); bf16_out: so is o.
+int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_part, bool bf16_out, void* stream);
 
 // ---------------------------------------------------------------- prefill
 constexpr int kMaxSelSeq = 64;           // sequences whose K_s a prefill launch carries

@@ -28,6 +28,7 @@ constexpr double kFixedTiles = 2.0;        // c0: per-workgroup overhead in tile
 constexpr double kMergeBase = 1.0;         // merge launch + pass, in tile-times
 constexpr double kMergePerSplit = 0.25;    // partial write + read per split
 constexpr int kFusedBf16Merge = 3;         // merge option: in-kernel over bf16 partials
+constexpr int kSeparateF32Merge = 4;       // merge option: separate kernel over float32 partials
 // The library's choice for bf16 inputs: the separate merge kernel.  Merging
 // in the decode launch measured slower on every workload here (32K prefix:
 // 57-59 against 44 us a call), because its tail -- partials through the L2,
@@ -96,7 +97,7 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
   const int group = h_q / h_kv;
   const int64_t q_rows = (int64_t)l_d * group;
   if (merge == 0) merge = dtype == 1 ? kDefaultBf16Merge : 1;
-  const bool fused = dtype == 1 && merge != 1;
+  const bool fused = dtype == 1 && (merge == 2 || merge == kFusedBf16Merge);
   DecodePlan p;
   p.n_seq = n_seq;
   p.k_s.resize(n_seq);
@@ -212,7 +213,8 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
   // float32 or bf16 (merge 3) for the in-kernel merge; float32 for the f32 path
   p.fused = fused && part > 0;
   p.fused_bf16 = p.fused && merge == kFusedBf16Merge;
-  p.part_elem_bytes = dtype == 1 && (!p.fused || p.fused_bf16) ? 2 : 4;
+  p.sep_f32 = dtype == 1 && merge == kSeparateF32Merge && part > 0;
+  p.part_elem_bytes = dtype == 1 && !p.sep_f32 && (!p.fused || p.fused_bf16) ? 2 : 4;
   if (p.fused) {
     const int64_t groups = (int64_t)std::min(n_seq, kMaxSeqPerLaunch) * h_kv * p.q_tiles;
     p.sync_words = 2 + groups * (1 + p.q_rows_per_wg / 32);

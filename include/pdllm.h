@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 9
+#define PDLLM_ABI_VERSION 10
 
 typedef enum {
   PDLLM_OK = 0,
@@ -372,7 +372,7 @@ size_t pdllm_split_attn_decode_workspace(const pdllm_pool* pool, const pdllm_pag
  *            own.
  * The result does not depend on num_splits beyond rounding: with bf16 inputs
  * the partials are rounded once to bf16 before the merge (float32 with merge
- * 2), with f32 inputs they are float32.
+ * 2 or 4), with f32 inputs they are float32.
  * Supported: f32 with d in {16, 32, 64, 128}; bf16 with d in {64, 128}.
  */
 pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_table* pt,
@@ -394,9 +394,13 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
  *                  (1); 1 = a second kernel launch over partials stored in
  *                  the pool dtype; 2 / 3 = inside the decode launch, over
  *                  float32 / bf16 partials exchanged through the L2 of one
- *                  XCD (bf16 inputs only, PDLLM_ERR_UNSUPPORTED for f32).
- *                  With 2 and 3 the workspace holds synchronisation words,
- *                  see pdllm_split_attn_decode.
+ *                  XCD (bf16 inputs only, PDLLM_ERR_UNSUPPORTED for f32);
+ *                  4 = a second kernel launch over float32 partials (for
+ *                  bf16 inputs the output is then rounded once, at the
+ *                  merge; twice the workspace of 1; for f32 inputs the same
+ *                  as 1).  With 2 and 3 the workspace holds synchronisation
+ *                  words, see pdllm_split_attn_decode.  Other values:
+ *                  PDLLM_ERR_INVALID_ARG.
  */
 typedef struct {
   int32_t num_splits;

@@ -64,7 +64,7 @@ int main() {
          PDLLM_ERR_INVALID_ARG);
   EXPECT(pdllm_split_attn_decode(&pool, &pt, q, q, q, 1, 256, 28, 0.088f, 0, q, nullptr, nullptr, 0, nullptr) ==
          PDLLM_ERR_WORKSPACE_TOO_SMALL);
-  for (int merge = 0; merge <= 3; ++merge)
+  for (int merge = 0; merge <= 4; ++merge)
     for (int rows : {0, 128, 256})
       for (int ns : {0, 1, 3, 69}) {
         pdllm_decode_opts o{};
@@ -82,7 +82,7 @@ int main() {
   for (int s = 0; s < 40; ++s) ks40[s] = (7 * s) % 17;
   pdllm_page_table pt40 = pt;
   pt40.k_per_seq = ks40.data();
-  for (int merge : {1, 3}) {
+  for (int merge : {1, 3, 4}) {
     pdllm_decode_opts o{};
     o.merge = merge;
     const size_t need = pdllm_split_attn_decode_ex_workspace(&pool, &pt40, 40, 64, 28, &o);

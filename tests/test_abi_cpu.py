@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 9
+    assert L.lib.pdllm_abi_version() == 10
 
 
 def _pool(**kw):
@@ -176,9 +176,15 @@ def test_decode_forced_shape_plans():
         assert q(rows, 5, 3) == sync + part + lse
         assert q(rows, 5, 2) == sync + 2 * part + lse
         assert q(rows, 5) == part + lse                 # the default: a separate merge kernel
+        assert q(rows, 5, 4) == 2 * part + lse          # separate merge kernel over float32 partials
     assert L.lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(_pool(dtype=0)), ctypes.byref(pt), 1, 256, 28,
                                                       ctypes.byref(L.DecodeOpts(5, 0, 2))) == 0
     assert "bf16 only" in _err()
+    # float32 inputs keep float32 partials: merge 4 is merge 1
+    f32q = lambda merge: L.lib.pdllm_split_attn_decode_ex_workspace(
+        ctypes.byref(_pool(dtype=0)), ctypes.byref(pt), 1, 256, 28, ctypes.byref(L.DecodeOpts(5, 64, merge)))
+    assert f32q(4) == f32q(1) == 2 * part + lse
+    assert q(0, 5, 5) == 0 and "merge" in _err()
 
 
 def test_noalloc_decode_validation():

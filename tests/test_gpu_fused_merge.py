@@ -69,3 +69,38 @@ def test_in_kernel_merge(device, name, cfg, ns, rows, heads, merge):
     # against the separate merge kernel (bf16 partials): within the bf16 output budget
     r2, m2 = assert_close(o, o_sep, "bf16", f"{name}: merge {merge} against merge 1")
     say(f"  oracle rel-L2 {r:.2e} max-abs {m:.2e} lse {ml:.2e}; vs separate merge rel-L2 {r2:.2e}")
+
+
+@pytest.mark.parametrize("name,cfg,ns,rows,heads", CASES, ids=[c[0] for c in CASES])
+def test_separate_merge_f32_partials(device, name, cfg, ns, rows, heads):
+    """merge 4: the separate merge kernel over float32 partials (the output
+    rounded once, at the merge) -- against the oracle, and against merge 1's
+    bf16 partials; two calls give identical bits."""
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    say(f"separate merge, float32 partials: {name}, num_splits={ns}, rows={rows}")
+    inp = synth.generate(cfg, 1)
+    sel, keep = synth.random_page_table(cfg, 1)
+    args = (dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot), dev(sel), dev(keep), cfg.k_per_seq,
+            dev(inp.q), dev(inp.k_resp), dev(inp.v_resp), cfg.scale)
+    call = L.Decode(*args, num_splits=ns, q_rows_per_wg=rows, merge=4)
+    outs = []
+    for _ in range(2):
+        o, lse = call()
+        torch.cuda.synchronize()
+        outs.append((host(o), host(lse)))
+    (o, lse), (o2, lse2) = outs
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2), "second call differs"
+    o_sep, _ = L.Decode(*args, num_splits=ns, q_rows_per_wg=rows, merge=1)()
+    torch.cuda.synchronize()
+    o_sep = host(o_sep)
+    ro, rlse = oracle.split_attn_decode(inp.pool_k, inp.pool_v, inp.chunk_slot, sel, keep, cfg.k_per_seq, inp.q,
+                                        inp.k_resp, inp.v_resp, cfg.scale, heads=heads)
+    if heads is not None:
+        o, lse, o_sep = o[:, :, heads], lse[:, heads], o_sep[:, :, heads]
+        ro, rlse = ro[:, :, heads], rlse[:, heads]
+    r, m = assert_close(o, ro, "bf16", f"{name} merge 4")
+    ml = max_abs(lse, rlse)
+    assert ml <= TOL["bf16"]["lse"], f"lse {ml:.2e}"
+    r1, m1 = assert_close(o_sep, ro, "bf16", f"{name} merge 1")
+    say(f"  oracle rel-L2: float32 partials {r:.2e} (max-abs {m:.2e}), bf16 partials {r1:.2e} (max-abs {m1:.2e})")
