@@ -112,6 +112,9 @@ def parse():
                    help="how the decode merges its splits: 0 the library's choice, 1 a separate merge "
                         "kernel, 2 / 3 inside the decode launch over float32 / bf16 partials, 4 a "
                         "separate merge kernel over float32 partials (pdllm_decode_opts.merge)")
+    p.add_argument("--gather-batch", action="store_true",
+                   help="diagnostic: the KV gather of decode calls over 16-64 sequences with their own 32K "
+                        "prefixes at L_d 16 and 32 (memory-bound), warm and cold")
     p.add_argument("--decode-only", action="store_true",
                    help="time only the decode call (diagnostic; not the headline step)")
     p.add_argument("--full-step", action="store_true",
@@ -712,6 +715,86 @@ def decode_sweep(args):
             del graph, call
 
 
+def gather_batch(args):
+    """The KV gather where it is memory-bound: decode calls over a batch of
+    sequences, each with its own 32K prefix (128 chunks of 256 + BOS in one
+    shared, permuted pool), K = 16, B = 256, 28/4 heads, d = 128, at L_d in
+    {16, 32} (7 L_d FLOP per byte of K/V) and 16 to 64 sequences per call, so
+    that one call gathers 135 to 540 MB of non-contiguous K/V rows.  Timed like
+    the decode sweep: a HIP graph of one call, replayed warm, and cold (a
+    512 MB write before each call); one JSON line per point."""
+    import torch
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    n_chunks, rows, h_q, h_kv, d, k, b = 128, 257, 28, 4, 128, 16, 256
+    scale = 1.0 / np.sqrt(d)
+    gen = torch.Generator(device=dev)
+    rng = np.random.default_rng(args.seed)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n = max(args.steps, 20)
+    max_seq = 64
+    n_slots = max_seq * n_chunks
+    gen.manual_seed(args.seed)
+    pool_k = torch.randn(n_slots, rows, h_kv, d, generator=gen, device=dev, dtype=torch.bfloat16)
+    pool_v = torch.randn(n_slots, rows, h_kv, d, generator=gen, device=dev, dtype=torch.bfloat16)
+    keep = torch.arange(1, b + 1, dtype=torch.int32, device=dev).repeat(n_slots, 1)
+    slot_all = torch.from_numpy(rng.permutation(n_slots).astype(np.int32)).to(dev)
+    sel_all = torch.from_numpy(np.stack([np.sort(rng.choice(n_chunks, size=k, replace=False))
+                                         for _ in range(max_seq)]).astype(np.int32)).to(dev)
+
+    def stats(ts):
+        ts = np.asarray(ts) * 1e3            # ms -> us
+        return {"median": float(np.median(ts)), "p10": float(np.percentile(ts, 10)),
+                "p90": float(np.percentile(ts, 90))}
+
+    for n_seq in (16, 32, 64):
+        for l_d in (16, 32):
+            q = torch.randn(n_seq, l_d, h_q, d, generator=gen, device=dev, dtype=torch.bfloat16)
+            k_resp = torch.randn(n_seq, l_d, h_kv, d, generator=gen, device=dev, dtype=torch.bfloat16)
+            v_resp = torch.randn(n_seq, l_d, h_kv, d, generator=gen, device=dev, dtype=torch.bfloat16)
+            # sequence s owns chunks [s * 128, (s + 1) * 128) of chunk_slot
+            call = L.Decode(pool_k, pool_v, slot_all[:n_seq * n_chunks].contiguous(), sel_all[:n_seq].contiguous(),
+                            keep[:n_seq * n_chunks].contiguous(), [k] * n_seq, q, k_resp, v_resp, scale)
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.current_stream(dev).wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                call()
+            times = {}
+            for mode in ("warm", "cold"):
+                for _ in range(args.warmup):
+                    graph.replay()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+                for e0, e1 in ev:
+                    if mode == "cold":
+                        flush.fill_(1)
+                    e0.record()
+                    graph.replay()
+                    e1.record()
+                torch.cuda.synchronize()
+                times[mode] = stats([e0.elapsed_time(e1) for e0, e1 in ev])
+            n_kv = k * (b + 1) + l_d
+            flops = n_seq * 4.0 * l_d * h_q * d * n_kv
+            kv_bytes = n_seq * 2.0 * n_kv * h_kv * d * 2
+            nbytes = kv_bytes + n_seq * 2.0 * l_d * h_q * d * 2          # + q and o
+            splits, tps, _ws, qrows = L.decode_plan([k] * n_seq, b, l_d, h_q, h_kv, d, 1, 0, with_rows=True)
+            rec = {"diagnostic": "KV gather, batch of 32K-prefix sequences (own pool slots each), K=16, B=256, "
+                                 "28/4 heads, d=128, one call per replay",
+                   "n_seq": n_seq, "l_d": l_d, "n_kv_per_seq": n_kv, "splits": splits[0], "tiles_per_split": tps[0],
+                   "q_rows_per_wg": qrows, "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                   "kv_gather_bytes": kv_bytes, "flop_per_byte": flops / nbytes}
+            for mode, st in times.items():
+                t = st["median"] * 1e-6
+                rec[mode] = dict(st, tflops=flops / t / 1e12, gbs=nbytes / t / 1e9,
+                                 hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS)
+            print(json.dumps(rec), flush=True)
+            del graph, call
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -740,6 +823,9 @@ def main():
         return
     if args.decode_sweep:
         decode_sweep(args)
+        return
+    if args.gather_batch:
+        gather_batch(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L

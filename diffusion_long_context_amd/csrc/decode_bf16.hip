@@ -421,10 +421,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   for (int w = 0; w < WAVES; ++w) has_absent = has_absent || sm.flag[w];
   has_absent = __builtin_amdgcn_readfirstlane((int)has_absent) != 0;
 
-  // The tile loader, prologue and main loop, in two instances: ABS for a
-  // split that holds an absent kept row, and the plain one.
-  auto run = [&](auto abs_flag) {
+  // The tile loader, prologue and main loop, in instances: ABS for a split
+  // that holds an absent kept row, and the plain one; and IDLE for a
+  // wavefront whose 32 query rows all lie past the last one (L_d * G not a
+  // multiple of the workgroup's rows), which only loads tiles and meets the
+  // same barriers, with no attention arithmetic.
+  auto run = [&](auto abs_flag, auto idle_flag) {
     constexpr bool ABS = decltype(abs_flag)::value;
+    constexpr bool IDLE = decltype(idle_flag)::value;
     // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values
     // of a tile.  K runs one tile ahead of V: load unit a carries K of tile a
     // and V of tile a-1 (local tile numbers u = t - t_begin, clamped to the
@@ -504,12 +508,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     fetch_ptrs(2 + STAGES, 1 + STAGES);
     __syncthreads();
     f32x16 sc_a[NK], sc_b[NK];
-    at.template qk<NK>(sc_a, k_base, qf);
-    uint64_t am0 = 0;                        // the absent mask of tile 0
-    if constexpr (ABS) am0 = uniform_u64(sm.kmask[0]);
-    // each tile's mask and scaled row max are taken one iteration ahead,
-    // after the previous tile's PV MFMAs (ms_a / ms_b go with sc_a / sc_b)
-    float ms_a = at.template block_max<NK>(sc_a, sl2, n_kv - t_begin * kTile, lj, 0, am0), ms_b = 0.f;
+    float ms_a = 0.f, ms_b = 0.f;
+    if constexpr (!IDLE) {
+      at.template qk<NK>(sc_a, k_base, qf);
+      uint64_t am0 = 0;                      // the absent mask of tile 0
+      if constexpr (ABS) am0 = uniform_u64(sm.kmask[0]);
+      // each tile's mask and scaled row max are taken one iteration ahead,
+      // after the previous tile's PV MFMAs (ms_a / ms_b go with sc_a / sc_b)
+      ms_a = at.template block_max<NK>(sc_a, sl2, n_kv - t_begin * kTile, lj, 0, am0);
+    }
     __syncthreads();                         // K buffer 0 is rewritten in iteration 0
 
     // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
@@ -536,17 +543,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
         fetch_ptrs(un, un - 1);
       }
       const int t = t_begin + u;
-      bf16x8 pf[2 * NK];
-      at.rescale(ms_cur);
-      uint64_t am_nxt = 0;
-      if (u + 1 < n_loc) {
-        if constexpr (ABS) am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
-        at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
-      } else {
-        at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
+      if constexpr (!IDLE) {
+        bf16x8 pf[2 * NK];
+        at.rescale(ms_cur);
+        uint64_t am_nxt = 0;
+        if (u + 1 < n_loc) {
+          if constexpr (ABS) am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
+          at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
+        } else {
+          at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
+        }
+        at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
+        if (u + 1 < n_loc) ms_nxt = at.template block_max<NK>(nxt, sl2, n_kv - (t + 1) * kTile, lj, 0, am_nxt);
       }
-      at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
-      if (u + 1 < n_loc) ms_nxt = at.template block_max<NK>(nxt, sl2, n_kv - (t + 1) * kTile, lj, 0, am_nxt);
       __syncthreads();
     };
     {
@@ -560,10 +569,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       if (u < n_loc) iter(u, sc_a, sc_b, ms_a, ms_b);
     }
   };
-  if (has_absent)
-    run(BoolConst<true>{});
+  const bool idle = __builtin_amdgcn_readfirstlane(qt * kRows + wave * 32 >= rows_total ? 1 : 0) != 0;
+  if (idle)
+    run(BoolConst<false>{}, BoolConst<true>{});
+  else if (has_absent)
+    run(BoolConst<true>{}, BoolConst<false>{});
   else
-    run(BoolConst<false>{});
+    run(BoolConst<false>{}, BoolConst<false>{});
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row).
   // The work item and the lane's row are derived again here from the block

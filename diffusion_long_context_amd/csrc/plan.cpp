@@ -8,13 +8,15 @@
 // a workgroup computes one (sequence, kv head, query tile, split).
 //
 // With num_splits = 0 the planner picks one tiles-per-split value for the
-// call by a small cost model measured in tile-times.  Workgroups of one call
-// have nearly equal length, so they run in rounds of `slots` (compute units
-// times the workgroups resident per CU):
-//   time(tps) = ceil(n_wg / slots) * (tps + c0) + merge(max_splits)
+// call by a small cost model measured in tile-times.  Workgroups of one
+// launch have nearly equal length, so they run in rounds of `slots` (compute
+// units times the workgroups resident per CU):
+//   time(tps) = sum over launches of ceil(n_wg / slots) * (tps + c0) + merge(max_splits)
 // where c0 is a workgroup's fixed cost (index table, query load, epilogue)
-// and merge() charges the extra merge pass and its partial-output traffic.
-// Ties go to fewer splits.
+// and merge() charges the extra merge pass and its partial-output traffic;
+// a call of more than kMaxSeqPerLaunch sequences runs as several launches,
+// one after the other, each of which must fill the GPU on its own.  Ties go
+// to fewer splits.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -154,27 +156,33 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
       const int64_t q_tiles = (q_rows + shapes[si].rows - 1) / shapes[si].rows;
       const double slots = (double)n_cu * shapes[si].resident;
       for (int tps = max_tiles; tps >= 1; --tps) {
-        int64_t n_wg = 0;
-        int max_splits = 1, longest = 1;
-        for (int s = 0; s < n_seq; ++s) {
-          const int ns = splits_for(s, tps);
-          max_splits = std::max(max_splits, ns);
-          longest = std::max(longest, std::min(tps, p.n_tiles[s]));
-          n_wg += (int64_t)h_kv * q_tiles * ns;
+        // the sequences run in launches of kMaxSeqPerLaunch, one after the
+        // other: each launch's rounds, longest split and merge add up
+        double t = 0.0;
+        for (int s0 = 0; s0 < n_seq; s0 += kMaxSeqPerLaunch) {
+          const int s1 = std::min(n_seq, s0 + kMaxSeqPerLaunch);
+          int64_t n_wg = 0;
+          int max_splits = 1, longest = 1;
+          for (int s = s0; s < s1; ++s) {
+            const int ns = splits_for(s, tps);
+            max_splits = std::max(max_splits, ns);
+            longest = std::max(longest, std::min(tps, p.n_tiles[s]));
+            n_wg += (int64_t)h_kv * q_tiles * ns;
+          }
+          double rounds = std::ceil((double)n_wg / slots);
+          if (fused) {
+            // every split of a group on one XCD: rounds of the fullest XCD
+            std::vector<int> sizes;
+            for (int s = s0; s < s1; ++s)
+              for (int64_t k = 0; k < (int64_t)h_kv * q_tiles; ++k) sizes.push_back(splits_for(s, tps));
+            int32_t bounds[kXcdGroups + 1];
+            const double per_xcd = std::max(1.0, std::floor(slots / kXcdGroups));
+            rounds = std::max(rounds, std::ceil((double)xcd_partition(sizes, bounds) / per_xcd));
+          }
+          t += rounds * (longest + kFixedTiles);
+          if (max_splits > 1)
+            t += fused ? kFusedMergeBase + kFusedMergePerSplit * max_splits : kMergeBase + kMergePerSplit * max_splits;
         }
-        double rounds = std::ceil((double)n_wg / slots);
-        if (fused) {
-          // every split of a group on one XCD: rounds of the fullest XCD
-          std::vector<int> sizes;
-          for (int s = 0; s < std::min(n_seq, kMaxSeqPerLaunch); ++s)
-            for (int64_t k = 0; k < (int64_t)h_kv * q_tiles; ++k) sizes.push_back(splits_for(s, tps));
-          int32_t bounds[kXcdGroups + 1];
-          const double per_xcd = std::max(1.0, std::floor(slots / kXcdGroups));
-          rounds = std::max(rounds, std::ceil((double)xcd_partition(sizes, bounds) / per_xcd));
-        }
-        double t = rounds * (longest + kFixedTiles);
-        if (max_splits > 1)
-          t += fused ? kFusedMergeBase + kFusedMergePerSplit * max_splits : kMergeBase + kMergePerSplit * max_splits;
         if (t < best - 1e-9) {      // strictly better: ties keep fewer splits, larger tiles
           best = t;
           best_tps = tps;
