@@ -39,6 +39,23 @@ constexpr int kTile = kDecodeTile;         // kv rows per tile
 // slices to the group's last arrival (about 20 ms).
 constexpr int kSpinLimit = 1 << 14;
 
+// Roles of a wavefront in the tile loop (see the kernel).
+constexpr int kRunAll = 0, kRunIdle = 1, kRunCons = 2, kRunProd = 3;
+constexpr int kProdStages = 3;             // staging sets of the loader wavefronts
+
+template <int N>
+struct IntConst {
+  static constexpr int value = N;
+};
+// f(IntConst<I>{}), ..., f(IntConst<N - 1>{}) in order
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntConst<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // LDS of one workgroup.  The 8-wave variant (one workgroup per CU) uses the
 // V pitch that keeps the transposing reads conflict-free on the 64-bank LDS
 // (4 rows x 64 B per 32 lanes) and an 8-tile row table; the 4-wave variant
@@ -127,7 +144,7 @@ __device__ __forceinline__ WorkItem work_item(const A& a, int bid) {
     w.g = local / a.q_tiles;
   } else {
     const int wg = xcd_remap(bid, a.total_wg);
-    while (si + 1 < a.n_seq_launch && wg >= a.seq[si + 1].wg_begin) ++si;
+    si = last_index_le(a.n_seq_launch, wg, [&](int i) { return a.seq[i].wg_begin; });
     local = wg - a.seq[si].wg_begin;
     w.qt = local % a.q_tiles;
     local /= a.q_tiles;
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   // point at the sequence's last row (finite data, masked scores).  Thread
   // tid fills row tid, so wavefront w fills table tile w and its ballot is
   // that tile's absent mask.
-  auto build_table = [&](int tw) {
+  auto build_table = [&](int tw) __attribute__((always_inline)) {
     const int nrow = (min(tw + kTableTiles, t_end) - tw) * kTile;
     bool absent = false;
     if (tid < nrow) {
@@ -421,73 +438,105 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   for (int w = 0; w < WAVES; ++w) has_absent = has_absent || sm.flag[w];
   has_absent = __builtin_amdgcn_readfirstlane((int)has_absent) != 0;
 
-  // The tile loader, prologue and main loop, in instances: ABS for a split
-  // that holds an absent kept row, and the plain one; and IDLE for a
-  // wavefront whose 32 query rows all lie past the last one (L_d * G not a
-  // multiple of the workgroup's rows), which only loads tiles and meets the
-  // same barriers, with no attention arithmetic.
-  auto run = [&](auto abs_flag, auto idle_flag) {
+  // The tile loader, prologue and main loop, in instances (compile-time):
+  // ABS for a split that holds an absent kept row, and the plain one; and a
+  // MODE:
+  //   kRunAll   every wavefront loads its share of each tile and computes;
+  //   kRunIdle  a wavefront whose 32 query rows all lie past the last one
+  //             (L_d * G not a multiple of the workgroup's rows): it loads
+  //             its share and meets the barriers, with no attention
+  //             arithmetic;
+  //   kRunCons / kRunProd  when the last four wavefronts of an 8-wave
+  //             workgroup hold no query rows (L_d * G <= 128 past the tile's
+  //             first row): waves 0-3 only compute, and waves 4-7 load every
+  //             row of every tile, with kProdStages staging sets, so that three
+  //             load units (96 KB of K/V for d = 128) are in flight per CU
+  //             instead of two -- the small-L_d decode is bound by the bytes
+  //             it keeps in flight.  Both run the same loop control and
+  //             barriers.  (Four sets measured no different in registers but
+  //             made the compiler copy the argument block to scratch.)
+  auto run = [&](auto abs_flag, auto mode_c) __attribute__((always_inline)) {
     constexpr bool ABS = decltype(abs_flag)::value;
-    constexpr bool IDLE = decltype(idle_flag)::value;
-    // ---- tile loader.  A thread owns RPT consecutive kv rows x 8 d values
-    // of a tile.  K runs one tile ahead of V: load unit a carries K of tile a
-    // and V of tile a-1 (local tile numbers u = t - t_begin, clamped to the
-    // split, so a unit past its end re-reads valid rows that are never
-    // stored).  STAGES staging register sets let a unit's loads be issued
-    // STAGES iterations before its LDS store.
-    // The prologue fetches the row pointers of units up to 2 + STAGES
-    // without a refill check, so they must lie in the first table fill: the
-    // 4-wave table (4 tiles) allows one staging set only.
-    constexpr int STAGES = (RPT <= 2 && 2 + 2 < kTableTiles) ? 2 : 1;
-    static_assert(2 + STAGES < kTableTiles, "prologue units must lie in the first row table");
-    const int ld_d0 = 8 * (tid % TPR);
-    const int ld_r0 = RPT * (tid / TPR);
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr bool SPLIT = MODE == kRunCons || MODE == kRunProd;
+    constexpr bool LOADS = MODE != kRunCons;            // this wavefront loads tiles
+    constexpr bool COMPUTES = MODE == kRunAll || MODE == kRunCons;
+    // ---- tile loader.  A loader thread owns LRPT consecutive kv rows x 8 d
+    // values of a tile.  K runs one tile ahead of V: load unit a carries K
+    // of tile a and V of tile a-1 (local tile numbers u = t - t_begin,
+    // clamped to the split, so a unit past its end re-reads valid rows that
+    // are never stored).  ST staging register sets let a unit's loads be
+    // issued ST iterations before its LDS store.
+    // The prologue fetches the row pointers of units up to 2 + ST without a
+    // refill check, so they must lie in the first table fill: the 4-wave
+    // table (4 tiles) allows one staging set only.
+    constexpr int LTHREADS = SPLIT ? kThreads / 2 : kThreads;   // loader threads
+    constexpr int LRPT = kTile * TPR / LTHREADS;
+    constexpr int ST = SPLIT ? kProdStages : (RPT <= 2 && 2 + 2 < kTableTiles) ? 2 : 1;
+    // loop unroll: a multiple of ST (staging sets are compile-time indices)
+    // and of 2 (the score buffers alternate with the parity of u)
+    constexpr int UNR = ST % 2 == 0 ? ST : 2 * ST;
+    static_assert(LRPT == 1 || LRPT == 2 || LRPT == 4, "loader mapping");
+    static_assert(2 + ST < kTableTiles, "prologue units must lie in the first row table");
+    static_assert(UNR % ST == 0 && UNR % 2 == 0, "unroll");
+    const int ltid = SPLIT ? tid - kThreads / 2 : tid;   // loader thread index (loaders only)
+    const bool lead = ltid == 0;               // the loader thread that writes tile masks
+    const int ld_d0 = 8 * (ltid % TPR);
+    const int ld_r0 = LRPT * (ltid / TPR);
     const int n_loc = t_end - t_begin;
-    u32x4 kreg[STAGES][RPT], vreg[STAGES][RPT];
-    gptr16 kp_next[RPT], vp_next[RPT];       // row pointers of the next unit to load
+    constexpr int NSET = LOADS ? ST : 1;
+    u32x4 kreg[NSET][LRPT], vreg[NSET][LRPT];
+    gptr16 kp_next[LRPT], vp_next[LRPT];     // row pointers of the next unit to load
     // A K tile's absent mask (bit r: row r is an absent kept row) travels with
     // its rows: read from the table with the pointers, held with the staged
     // registers, written beside the tile into LDS, read back with the tile's
     // S^T (wave-uniform values; ABS instance only).
-    uint64_t km_next = 0, km_set[STAGES];
-    auto fetch_ptrs = [&](int uk, int uv) {  // local tiles of the K and V rows
-      const int tk = t_begin + min(uk, n_loc - 1) - tw;
-      const int ik = tk * kTile + ld_r0;
-      const int iv = (t_begin + min(max(uv, 0), n_loc - 1) - tw) * kTile + ld_r0;
-  #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        kp_next[i] = sm.kptr[ik + i];
-        vp_next[i] = sm.vptr[iv + i];
+    uint64_t km_next = 0, km_set[NSET];
+    auto fetch_ptrs = [&](int uk, int uv) __attribute__((always_inline)) {   // local tiles of K and V rows
+      if constexpr (LOADS) {
+        const int tk = t_begin + min(uk, n_loc - 1) - tw;
+        const int ik = tk * kTile + ld_r0;
+        const int iv = (t_begin + min(max(uv, 0), n_loc - 1) - tw) * kTile + ld_r0;
+#pragma unroll
+        for (int i = 0; i < LRPT; ++i) {
+          kp_next[i] = sm.kptr[ik + i];
+          vp_next[i] = sm.vptr[iv + i];
+        }
+        if constexpr (ABS) km_next = uniform_u64(sm.absent[tk]);
       }
-      if constexpr (ABS) km_next = uniform_u64(sm.absent[tk]);
     };
-    auto load_unit = [&](int set) {
-  #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        kreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(kp_next[i] + ld_d0);
-        vreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(vp_next[i] + ld_d0);
+    auto load_unit = [&](int set) __attribute__((always_inline)) {
+      if constexpr (LOADS) {
+#pragma unroll
+        for (int i = 0; i < LRPT; ++i) {
+          kreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(kp_next[i] + ld_d0);
+          vreg[set][i] = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(vp_next[i] + ld_d0);
+        }
+        if constexpr (ABS) km_set[set] = km_next;
       }
-      if constexpr (ABS) km_set[set] = km_next;
     };
-    auto store_k = [&](int buf, int set) {
-  #pragma unroll
-      for (int i = 0; i < RPT; ++i)
-        *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[set][i];
-      if constexpr (ABS)
-        if (tid == 0) sm.kmask[buf] = km_set[set];
+    auto store_k = [&](int buf, int set) __attribute__((always_inline)) {
+      if constexpr (LOADS) {
+#pragma unroll
+        for (int i = 0; i < LRPT; ++i)
+          *reinterpret_cast<u32x4*>(&sm.k[buf][(ld_r0 + i) * KP + ld_d0]) = kreg[set][i];
+        if constexpr (ABS)
+          if (lead) sm.kmask[buf] = km_set[set];
+      }
     };
-    auto store_v = [&](int buf, int set) {
-  #pragma unroll
-      for (int i = 0; i < RPT; ++i)
-        *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[set][i];
+    auto store_v = [&](int buf, int set) __attribute__((always_inline)) {
+      if constexpr (LOADS) {
+#pragma unroll
+        for (int i = 0; i < LRPT; ++i)
+          *reinterpret_cast<u32x4*>(&sm.v[buf][(ld_r0 + i) * VP + ld_d0]) = vreg[set][i];
+      }
     };
-
 
     // ---- prologue: K and V of tile 0 and K of tile 1 into LDS, units 2 ..
-    // 1 + STAGES in flight, S^T of tile 0 computed
+    // 1 + ST in flight, S^T of tile 0 computed
     fetch_ptrs(0, 0);
     load_unit(0);
-    if constexpr (STAGES == 2) {             // tiles 0 and 1 in one memory round trip
+    if constexpr (ST >= 2) {                 // tiles 0 and 1 in one memory round trip
       fetch_ptrs(1, 1);
       load_unit(1);
       store_k(0, 0);
@@ -500,16 +549,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       load_unit(0);
       store_k(1, 0);
     }
-  #pragma unroll
-    for (int i = 0; i < STAGES; ++i) {
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
       fetch_ptrs(2 + i, 1 + i);
-      load_unit((2 + i) % STAGES);
+      load_unit((2 + i) % ST);
     }
-    fetch_ptrs(2 + STAGES, 1 + STAGES);
+    fetch_ptrs(2 + ST, 1 + ST);
     __syncthreads();
     f32x16 sc_a[NK], sc_b[NK];
     float ms_a = 0.f, ms_b = 0.f;
-    if constexpr (!IDLE) {
+    if constexpr (COMPUTES) {
       at.template qk<NK>(sc_a, k_base, qf);
       uint64_t am0 = 0;                      // the absent mask of tile 0
       if constexpr (ABS) am0 = uniform_u64(sm.kmask[0]);
@@ -522,17 +571,18 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
     // ---- main loop.  Iteration u stores unit u+2 (K of tile u+2 into K buffer
     // u & 1, whose tile u was last read in iteration u-1; V of tile u+1 into V
     // buffer (u+1) & 1, last read by tile u-1), issues the loads of unit
-    // u+2+STAGES into the staging set just freed, then runs the softmax of
-    // tile u with the S^T MFMAs of tile u+1 interleaved, and the PV of tile u.
+    // u+2+ST into the staging set just freed, then runs the softmax of tile u
+    // with the S^T MFMAs of tile u+1 interleaved, and the PV of tile u.
     // Every iteration issues exactly one unit's loads, so the wait before a
-    // store covers only loads issued STAGES iterations earlier.  One barrier
-    // per tile.
-    auto iter = [&](int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], float ms_cur, float& ms_nxt) {
-      const int set = u % STAGES;
+    // store covers only loads issued ST iterations earlier.  One barrier per
+    // tile.  R = u % UNR (compile-time): unit u+2 sits in set (R + 2) % ST.
+    auto iter = [&](auto r_c, int u, f32x16 (&cur)[NK], f32x16 (&nxt)[NK], float ms_cur,
+                    float& ms_nxt) __attribute__((always_inline)) {
+      constexpr int set = (decltype(r_c)::value + 2) % ST;
       if (u + 2 < n_loc) store_k(u & 1, set);
       if (u + 1 < n_loc) store_v((u + 1) & 1, set);
       load_unit(set);
-      const int un = u + 3 + STAGES;         // the unit the next iteration loads
+      const int un = u + 3 + ST;             // the unit the next iteration loads
       if (un <= n_loc) {                     // beyond, the clamped pointers stay valid
         if (t_begin + min(un, n_loc - 1) - tw >= kTableTiles) {   // refill the row table (rare)
           __syncthreads();                   // every wave has read the old table
@@ -543,7 +593,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
         fetch_ptrs(un, un - 1);
       }
       const int t = t_begin + u;
-      if constexpr (!IDLE) {
+      if constexpr (COMPUTES) {
         bf16x8 pf[2 * NK];
         at.rescale(ms_cur);
         uint64_t am_nxt = 0;
@@ -559,23 +609,55 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       __syncthreads();
     };
     {
-      // both halves unconditional inside the loop, so the loop head is reached
-      // only after the second half's loads (exact wait counts before stores)
+      // the UNR copies are unconditional inside the loop, so the loop head is
+      // reached only after the last copy's loads (exact wait counts before
+      // stores); the remaining iterations follow, each under its bound
       int u = 0;
-      for (; u + 1 < n_loc; u += 2) {
-        iter(u, sc_a, sc_b, ms_a, ms_b);
-        iter(u + 1, sc_b, sc_a, ms_b, ms_a);
-      }
-      if (u < n_loc) iter(u, sc_a, sc_b, ms_a, ms_b);
+      for (; u + UNR - 1 < n_loc; u += UNR)
+        static_for<0, UNR>([&](auto r_c) __attribute__((always_inline)) {
+          constexpr int R = decltype(r_c)::value;
+          if constexpr (R % 2 == 0)
+            iter(r_c, u + R, sc_a, sc_b, ms_a, ms_b);
+          else
+            iter(r_c, u + R, sc_b, sc_a, ms_b, ms_a);
+        });
+      static_for<0, UNR - 1>([&](auto r_c) __attribute__((always_inline)) {
+        constexpr int R = decltype(r_c)::value;
+        if (u + R < n_loc) {
+          if constexpr (R % 2 == 0)
+            iter(r_c, u + R, sc_a, sc_b, ms_a, ms_b);
+          else
+            iter(r_c, u + R, sc_b, sc_a, ms_b, ms_a);
+        }
+      });
     }
   };
+  // whole workgroup: the last four wavefronts hold no query rows
+  const bool split_roles =
+      WAVES == 8 && __builtin_amdgcn_readfirstlane(qt * kRows + (WAVES / 2) * 32 >= rows_total ? 1 : 0) != 0;
   const bool idle = __builtin_amdgcn_readfirstlane(qt * kRows + wave * 32 >= rows_total ? 1 : 0) != 0;
-  if (idle)
-    run(BoolConst<false>{}, BoolConst<true>{});
-  else if (has_absent)
-    run(BoolConst<true>{}, BoolConst<false>{});
-  else
-    run(BoolConst<false>{}, BoolConst<false>{});
+  if constexpr (WAVES == 8) {
+    if (split_roles) {
+      if (wave >= WAVES / 2) {
+        if (has_absent)
+          run(BoolConst<true>{}, IntConst<kRunProd>{});
+        else
+          run(BoolConst<false>{}, IntConst<kRunProd>{});
+      } else if (has_absent) {
+        run(BoolConst<true>{}, IntConst<kRunCons>{});
+      } else {
+        run(BoolConst<false>{}, IntConst<kRunCons>{});
+      }
+    }
+  }
+  if (!split_roles) {
+    if (idle)
+      run(BoolConst<false>{}, IntConst<kRunIdle>{});
+    else if (has_absent)
+      run(BoolConst<true>{}, IntConst<kRunAll>{});
+    else
+      run(BoolConst<false>{}, IntConst<kRunAll>{});
+  }
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row).
   // The work item and the lane's row are derived again here from the block

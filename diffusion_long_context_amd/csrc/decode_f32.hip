@@ -46,8 +46,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeArgs a) {
   __shared__ int64_t rowoff[kTile];
 
   const int wg = xcd_remap(blockIdx.x, a.total_wg);
-  int si = 0;
-  while (si + 1 < a.n_seq_launch && wg >= a.seq[si + 1].wg_begin) ++si;
+  const int si = last_index_le(a.n_seq_launch, wg, [&](int i) { return a.seq[i].wg_begin; });
   const int k_s = a.seq[si].k_s, n_kv = a.seq[si].n_kv;
   const int n_splits = a.seq[si].n_splits, tps = a.seq[si].tiles_per_split;
   int local = wg - a.seq[si].wg_begin;

@@ -137,6 +137,21 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The last index i in [0, n) with key(i) <= v, for a non-decreasing key
+// with key(0) <= v (binary search; wave-uniform arguments stay scalar).
+template <class F>
+__device__ __forceinline__ int last_index_le(int n, int v, F key) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (key(mid) <= v)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id % 8).  Remap
 // them so that each XCD receives one contiguous range of logical work items;
 // neighbouring items share K/V tiles, which then stay in that XCD's L2.

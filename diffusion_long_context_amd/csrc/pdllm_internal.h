@@ -17,8 +17,10 @@ constexpr int kDecodeTile = 64;
 constexpr int kDecodeRowsBf16Small = 128;
 constexpr int kDecodeRowsBf16Large = 256;
 constexpr int kDecodeRowsF32 = 64;
-// sequences whose per-sequence plan travels in one launch's arguments
-constexpr int kMaxSeqPerLaunch = 16;
+// sequences whose per-sequence plan travels in one launch's arguments (the
+// argument block is then about 2.7 KB); a batch of small-window decodes
+// gathers its K/V in one launch, with no split merge, up to this many
+constexpr int kMaxSeqPerLaunch = 64;
 
 struct DecodePlan {
   int n_seq = 0;

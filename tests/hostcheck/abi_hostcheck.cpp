@@ -78,15 +78,15 @@ int main() {
         EXPECT(pdllm::g_launches > before);
       }
   // many sequences: several launches, mixed K_s, the in-kernel merge's XCD partition
-  std::vector<int32_t> ks40(40);
-  for (int s = 0; s < 40; ++s) ks40[s] = (7 * s) % 17;
-  pdllm_page_table pt40 = pt;
-  pt40.k_per_seq = ks40.data();
+  std::vector<int32_t> ks_many(70);
+  for (int s = 0; s < 70; ++s) ks_many[s] = (7 * s) % 17;
+  pdllm_page_table pt_many = pt;
+  pt_many.k_per_seq = ks_many.data();
   for (int merge : {1, 3, 4}) {
     pdllm_decode_opts o{};
     o.merge = merge;
-    const size_t need = pdllm_split_attn_decode_ex_workspace(&pool, &pt40, 40, 64, 28, &o);
-    EXPECT(pdllm_split_attn_decode_ex(&pool, &pt40, q, q, q, 40, 64, 28, 0.088f, &o, q, nullptr, P(0x1000000), need,
+    const size_t need = pdllm_split_attn_decode_ex_workspace(&pool, &pt_many, 70, 64, 28, &o);
+    EXPECT(pdllm_split_attn_decode_ex(&pool, &pt_many, q, q, q, 70, 64, 28, 0.088f, &o, q, nullptr, P(0x1000000), need,
                                       nullptr) == PDLLM_OK);
   }
   // no selected chunk: NULL index tables are accepted
@@ -155,7 +155,7 @@ int main() {
   EXPECT(pdllm_compact_kept_rows(&pool, pt.chunk_slot, 128, pt.keep_rows, 128, q, q, 129 * 512, 512, 128, 129,
                                  nullptr) == PDLLM_OK);
   EXPECT(pdllm_gather_kept_kv(&pool, &pt, 1, q, q, 257 * 512, 512, 128, nullptr) == PDLLM_OK);
-  EXPECT(pdllm_gather_kept_kv(&pool, &pt40, 40, q, q, 257 * 512, 512, 128, nullptr) == PDLLM_OK);
+  EXPECT(pdllm_gather_kept_kv(&pool, &pt_many, 40, q, q, 257 * 512, 512, 128, nullptr) == PDLLM_OK);
   EXPECT(pdllm_chunk_score(q, PDLLM_BF16, 152064, 152064, pt.chunk_slot, 128, 64, 64, nullptr, nullptr, (float*)q,
                            P(0x1000000), pdllm_chunk_score_workspace(128, 64, 64), nullptr) == PDLLM_OK);
   EXPECT(pdllm_abi_version() == PDLLM_ABI_VERSION);

@@ -163,18 +163,18 @@ def test_rerun_is_bitwise_identical(device):
 
 
 def test_many_sequences_take_several_launches(device):
-    """More sequences than one launch carries (16): the later launches
+    """More sequences than one launch carries (64): the later launches
     address their sequences and split partials by offset.  Mixed K_s,
     including 0 and N, through the planner and a forced split count."""
-    ks = tuple((3 * s) % 7 for s in range(20))           # 0 .. 6 chunks of 6
-    cfg = synth.Config("seq20", 14, 2, 128, "bf16", 6, 40, ks, 17, 24, 8, n_seq=20)
+    ks = tuple((3 * s) % 7 for s in range(70))           # 0 .. 6 chunks of 6
+    cfg = synth.Config("seq70", 14, 2, 128, "bf16", 6, 40, ks, 17, 24, 8, n_seq=70)
     inp = synth.generate(cfg, 4)
     sel, keep = synth.random_page_table(cfg, 4)
     ro, rlse = _oracle(inp, sel, keep, cfg)
     for ns in (0, 3):
-        say(f"20 sequences, num_splits={ns}")
+        say(f"70 sequences, num_splits={ns}")
         o, lse = _run_gpu(inp, sel, keep, cfg, ns)
-        _compare(o, lse, ro, rlse, cfg, f"20 sequences splits {ns}")
+        _compare(o, lse, ro, rlse, cfg, f"70 sequences splits {ns}")
 
 
 FORCED = [(d, rows) for d in (64, 128) for rows in (128, 256)]
@@ -251,3 +251,33 @@ def test_no_chunk_selected_with_null_tables(device):
         assert st == 0, L.lib.pdllm_last_error()
         torch.cuda.synchronize()
         _compare(host(o), host(lse), ro, rlse, cfg, f"K=0 NULL tables splits {ns}")
+
+
+SMALL_LD = [
+    # (name, config, forced split counts): a workgroup of 256 query rows whose
+    # last four wavefronts hold none (L_d * G <= 128) splits into computing
+    # and loading wavefronts; splits of 17 tiles refill the row table
+    ("ld16", synth.Config("ld16", 14, 2, 128, "bf16", 8, 128, (8,), 128, 16, 8), (0, 1, 3)),
+    ("ld9_partial", synth.Config("ld9", 14, 2, 128, "bf16", 8, 100, (8,), 100, 9, 8, last_chunk=60), (0, 1, 2)),
+    ("ld16_d64_seq70", synth.Config("ld16s", 14, 2, 64, "bf16", 6, 64, tuple(1 + (5 * s) % 6 for s in range(70)),
+                                    64, 16, 8, n_seq=70), (0, 2)),
+    ("ld40_two_tiles", synth.Config("ld40", 14, 2, 128, "bf16", 6, 64, (6,), 64, 40, 8), (0, 1)),
+]
+
+
+@pytest.mark.parametrize("name,cfg,splits", SMALL_LD, ids=[c[0] for c in SMALL_LD])
+def test_small_window_loader_wavefronts(device, name, cfg, splits):
+    """Small L_d: the workgroup's wavefronts without query rows load the
+    tiles for the others (three staging sets), with absent rows (a partial
+    last chunk), d = 64, more sequences than one launch, and a second query
+    tile of 24 rows (L_d = 40: the first tile computes on all wavefronts,
+    the second splits).  Two calls give identical bits."""
+    inp = synth.generate(cfg, 11)
+    sel, keep = synth.random_page_table(cfg, 11)
+    ro, rlse = _oracle(inp, sel, keep, cfg)
+    for ns in splits:
+        say(f"{name}: num_splits={ns}")
+        o, lse = _run_gpu(inp, sel, keep, cfg, ns)
+        _compare(o, lse, ro, rlse, cfg, f"{name} splits {ns}")
+        o2, lse2 = _run_gpu(inp, sel, keep, cfg, ns)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2), "second call differs"

@@ -26,7 +26,7 @@ def _calls(cfg, seed, merge, num_splits=0, rows=0):
     # sync words: started, exited, one arrival count per (sequence, kv head,
     # query tile) group of a launch, then the claim counts (checked: the words
     # that are sync words whichever workgroup shape the planner picks)
-    groups = min(cfg.n_seq, 16) * cfg.h_kv * -(-cfg.l_d * (cfg.h_q // cfg.h_kv) // 256)
+    groups = min(cfg.n_seq, 64) * cfg.h_kv * -(-cfg.l_d * (cfg.h_q // cfg.h_kv) // 256)
     outs = []
     for _ in range(2):
         o, lse = call()
@@ -46,8 +46,8 @@ CASES = [
     ("forced128_partial", synth.Config("p", 14, 2, 128, "bf16", 8, 100, (8,), 100, 40, 8, last_chunk=60), 5, 128,
      None),
     ("d64", synth.Config("d64", 8, 2, 64, "bf16", 6, 64, (5,), 40, 50, 8), 3, 0, None),
-    ("seq20", synth.Config("seq20", 14, 2, 128, "bf16", 6, 40, tuple((3 * s) % 7 for s in range(20)), 17, 24, 8,
-                           n_seq=20), 3, 0, None),
+    ("seq70", synth.Config("seq70", 14, 2, 128, "bf16", 6, 40, tuple((3 * s) % 7 for s in range(70)), 17, 24, 8,
+                           n_seq=70), 3, 0, None),
 ]
 
 
