@@ -80,15 +80,15 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "0410efcac58b8453",
+        "sources": PREFILL_SOURCES, "sources_sha": "4d263641aa52ced2",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149381.17, "write_kib": 231422.48},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149380.83, "write_kib": 231448.70},
                     "finalize_select_kernel": {"fetch_kib": 312.12, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "5b7210ed3ad54e83",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7363.00, "write_kib": 16637.79},
-                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8351.75, "write_kib": 1992.00}},
+        "sources": DECODE_SOURCES, "sources_sha": "11dba8dd2e5e2873",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7384.50, "write_kib": 16637.80},
+                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8351.50, "write_kib": 1992.00}},
     },
 }
 COPY_COUNTERS = {"copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
