@@ -8,8 +8,12 @@
 // order-preserving 32-bit key (-0 and +0 share one key, NaN gets the lowest
 // key), and candidate i gets the 64-bit key (key << 32) | ~i so that equal
 // scores rank the lower index first and all keys differ.  A candidate is kept
-// iff fewer than `count` candidates have a larger key (its rank); the kept
-// ones are written in ascending index order with a workgroup prefix count.
+// iff fewer than `count` candidates have a larger key (its rank).  Up to
+// kRankMax candidates each count the larger keys directly; above that a
+// radix select finds the count-th largest 32-bit score key in four 8-bit
+// histogram passes, and ties at that key go to the lowest indices.  Either
+// way the kept ones are written in ascending index order with a workgroup
+// prefix count, and the two give the same set.
 #include "device_common.h"
 #include "pdllm_internal.h"
 
@@ -17,6 +21,76 @@ namespace pdllm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRankMax = 256;               // candidates up to which ranks are counted directly
+static_assert(kThreads == 256, "one radix histogram bin per thread");
+
+// Workgroup-wide prefix count of a per-thread flag over one round of
+// kThreads candidates, in index order: returns the number of flagged threads
+// before this one, and the round's total in `total` (all threads).
+__device__ __forceinline__ int round_prefix(bool flag, int* wave_counts, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t mask = __ballot(flag);
+  if (lane == 0) wave_counts[wave] = __popcll(mask);
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_counts[w];
+  total = 0;
+  for (int w = 0; w < kThreads / 64; ++w) total += wave_counts[w];
+  __syncthreads();
+  return before + __popcll(mask & ((1ull << lane) - 1ull));
+}
+
+// The count-th largest 32-bit score key among n keys (the high halves of
+// keys[]) by radix select, 0 < count < n: returns it, and in *need how many
+// of the candidates equal to it are kept (the others above it all are).
+// hist: 256 words of LDS.
+__device__ uint32_t radix_threshold(const uint64_t* keys, int n, int count, uint32_t* hist, int* need) {
+  const int tid = threadIdx.x;
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  uint32_t prefix = 0, mask = 0;
+  int want = count;                          // keys still to take among those matching the prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;                           // kThreads == 256 bins
+    __syncthreads();
+    for (int i = tid; i < n; i += kThreads) {
+      const uint32_t k = (uint32_t)(keys[i] >> 32);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // the digit where the count from the top reaches want: lane l holds
+      // digits 255 - 4 l - j (j = 0..3), a prefix sum over the lanes gives the
+      // count above each lane's digits, and one lane's range holds want
+      int h[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = (int)hist[255 - 4 * tid - j];
+        sum += h[j];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        if (tid >= off) incl += t;
+      }
+      int above = incl - sum;
+      if (above < want && want <= incl) {
+        int j = 0;
+        for (; j < 3 && above + h[j] < want; ++j) above += h[j];
+        s_prefix = prefix | ((uint32_t)(255 - 4 * tid - j) << shift);
+        s_need = want - above;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    want = s_need;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  *need = want;
+  return prefix;
+}
 
 // Select the `count` best of the n keys in `keys` (LDS) and write their
 // indices + `index_base`, ascending, to out[0..count).
@@ -25,6 +99,27 @@ __device__ void select_sorted(const uint64_t* keys, int n, int count, int index_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (count >= n) {                         // every candidate is kept
     for (int i = tid; i < n; i += kThreads) out[i] = i + index_base;
+    return;
+  }
+  if (count <= 0) return;
+  if (n > kRankMax) {
+    __shared__ uint32_t hist[kThreads];
+    int need = 0;
+    const uint32_t thr = radix_threshold(keys, n, count, hist, &need);
+    int written = 0, equal_seen = 0;
+    for (int base = 0; base < n; base += kThreads) {
+      const int i = base + tid;
+      const uint32_t k = i < n ? (uint32_t)(keys[i] >> 32) : 0u;
+      const bool eq = i < n && k == thr;
+      int eq_total;
+      const int eq_rank = equal_seen + round_prefix(eq, wave_counts, eq_total);
+      equal_seen += eq_total;
+      const bool keep = i < n && (k > thr || (eq && eq_rank < need));
+      int keep_total;
+      const int at = written + round_prefix(keep, wave_counts, keep_total);
+      if (keep) out[at] = i + index_base;
+      written += keep_total;
+    }
     return;
   }
   int written = 0;

@@ -68,3 +68,24 @@ def test_topk_bit_exact(device, n_seq, n, seed):
     got = _topk(cs, kps, k_max)
     want = oracle.select_topk(cs, kps, k_max)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("n,seed", [(1025, 0), (6000, 1), (8192, 2)])
+def test_topk_radix_select_ties(device, n, seed):
+    """Above 1024 candidates the selection runs a radix select over the score
+    keys: heavy ties (a few distinct scores, so the threshold falls inside a
+    tie group, which the lower indices win), NaN, +-0 and +-inf, at K from 1
+    to n - 1 -- bit-exact against the oracle."""
+    rng = np.random.default_rng(300 + seed)
+    cs = rng.integers(0, 6, size=(3, n)).astype(np.float32)
+    cs[0, 7::11] = np.nan
+    cs[1, 5::13] = -0.0
+    cs[1, 6::13] = 0.0
+    cs[2, 9::17] = np.inf
+    cs[2, 10::19] = -np.inf
+    for k in (1, 17, n // 3, n // 2, n - 2, n - 1):
+        kps = [k, max(k - 5, 0), min(k + 5, n)]
+        say(f"radix top-K n={n} k={kps}")
+        got = _topk(cs, kps, max(kps))
+        want = oracle.select_topk(cs, kps, max(kps))
+        assert np.array_equal(got, want), f"n {n} k {kps}"
