@@ -158,10 +158,60 @@ struct WaveAttn {
   // PV: fragment 2 kb + h holds the lane's registers 8 h .. 8 h + 7 of block
   // kb).  With NXT, the S^T MFMAs of the next block (K at k_next) are issued
   // interleaved with that VALU work, about five VALU ops per MFMA.
-  template <int NK, bool NXT>
+  //
+  // FENCE > 0 (with NXT): the same work in a fixed order, fenced from the
+  // scheduler: the K fragment of MFMA m + 2 is read before MFMA m, and each
+  // MFMA is followed by its share of the exp work (16 / DC elements) and the
+  // P fragments that share completes.  For callers whose register pressure
+  // makes the scheduler drop the grouped order above, which leaves every
+  // MFMA waiting on its own K read and the exp work after the last MFMA.
+  // FENCE == 2 also pins each exp result and P fragment to its slot with an
+  // empty asm statement, for callers where instruction selection otherwise
+  // moves that arithmetic past the fences (it can cost registers).
+  template <int NK, bool NXT, int FENCE = 0>
   __device__ __forceinline__ void exp_qk(f32x16 (&sc)[NK], bf16x8 (&pf)[2 * NK], f32x16 (&sn)[NK],
                                          const uint16_t* __restrict__ k_next,
                                          const bf16x8 (&qf)[DC], float sl2) {
+    if constexpr (NXT && FENCE > 0) {
+      constexpr int M = NK * DC;             // S^T MFMAs, dc outer
+      constexpr int EPM = 16 * NK / M;       // exp elements per MFMA
+      static_assert(EPM * M == 16 * NK && M >= 2, "exp work must split evenly over the MFMAs");
+      const float neg_m = -m_run;
+      float ps = 0.f;
+      auto kfrag = [&](int m) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(k_next + 32 * (m % NK) * KP + 16 * (m / NK));
+      };
+      bf16x8 k0 = kfrag(0), k1 = kfrag(1);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        bf16x8 k2;
+        if (m + 2 < M) k2 = kfrag(m + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        sn[m % NK] = mfma32x32x16(k0, qf[m / NK], m < NK ? f32x16{} : sn[m % NK]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = m * EPM; e < (m + 1) * EPM; ++e) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[e / 16][e % 16], sl2, neg_m));
+          if constexpr (FENCE == 2) asm volatile("" : "+v"(p));
+          sc[e / 16][e % 16] = p;
+          ps += p;
+        }
+#pragma unroll
+        for (int p = 0; p < 2 * NK; ++p)
+          if (8 * p + 7 >= m * EPM && 8 * p + 7 < (m + 1) * EPM) {
+            const f32x16& v = sc[p / 2];
+            const int o = 8 * (p % 2);
+            pf[p] = bf16x8{(__bf16)v[o + 0], (__bf16)v[o + 1], (__bf16)v[o + 2], (__bf16)v[o + 3],
+                           (__bf16)v[o + 4], (__bf16)v[o + 5], (__bf16)v[o + 6], (__bf16)v[o + 7]};
+            if constexpr (FENCE == 2) asm volatile("" : "+v"(pf[p]));
+          }
+        __builtin_amdgcn_sched_barrier(0);
+        k0 = k1;
+        k1 = k2;
+      }
+      l_run += ps;
+      return;
+    }
     const float neg_m = -m_run;
     float ps = 0.f;
 #pragma unroll
@@ -198,9 +248,35 @@ struct WaveAttn {
   // pitch VP).  Only the first n16 16-row pieces are accumulated: the caller
   // passes fewer when the rest hold only masked rows (p = 0 against zero V
   // rows, so skipping them changes nothing).
-  template <int NK>
+  //
+  // AHEAD (every piece, no n16): the V reads of MFMA m + 1 are issued before
+  // MFMA m, fenced from the scheduler, so their LDS latency overlaps the MFMA
+  // before them (left alone, the compiler short of registers issues each
+  // MFMA's reads just before it and waits for them).
+  template <int NK, bool AHEAD = false>
   __device__ __forceinline__ void pv(const bf16x8 (&pf)[2 * NK], const uint16_t* __restrict__ v_lane,
                                      int n16 = 2 * NK) {
+    if constexpr (AHEAD) {
+      constexpr int M = 2 * NK * DB;
+      auto read_v = [&](int m) __attribute__((always_inline)) {
+        const int piece = m / DB, db = m % DB;
+        const uint16_t* vp = v_lane + 16 * piece * VP + 32 * db;
+        const bf16x4 lo = lds_read_tr16(vp);
+        const bf16x4 hi = lds_read_tr16(vp + 8 * VP);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      bf16x8 va = read_v(0);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        bf16x8 vn;
+        if (m + 1 < M) vn = read_v(m + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[m % DB] = mfma32x32x16(va, pf[m / DB], acc[m % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m + 1 < M) va = vn;
+      }
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
 #pragma unroll

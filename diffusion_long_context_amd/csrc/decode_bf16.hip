@@ -599,11 +599,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
         uint64_t am_nxt = 0;
         if (u + 1 < n_loc) {
           if constexpr (ABS) am_nxt = uniform_u64(sm.kmask[(u + 1) & 1]);
-          at.template exp_qk<NK, true>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
+          at.template exp_qk<NK, true, LOADS ? 1 : 0>(cur, pf, nxt, k_base + ((u + 1) & 1) * (kTile * KP), qf, sl2);
         } else {
           at.template exp_qk<NK, false>(cur, pf, nxt, nullptr, qf, sl2);
         }
-        at.template pv<NK>(pf, v_base + (u & 1) * (kTile * VP), min(2 * NK, (n_kv - t * kTile + 15) >> 4));
+        // every 16-row piece, the last tile's too: its rows past n_kv hold
+        // finite data (the last row) and p = 0, so they add exactly zero, and
+        // with no branch between the pieces the V reads can run ahead of the
+        // MFMAs
+        at.template pv<NK, true>(pf, v_base + (u & 1) * (kTile * VP));
         if (u + 1 < n_loc) ms_nxt = at.template block_max<NK>(nxt, sl2, n_kv - (t + 1) * kTile, lj, 0, am_nxt);
       }
       __syncthreads();

@@ -161,10 +161,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     // layout has a single row there (R = C + 1 for C a multiple of 64), as a
     // one-row update.  A step wholly past Rc (a partial chunk) is masked
     // throughout; a one-row update past Rc is skipped.
+    //
+    // The 64-row steps are software-pipelined: step st's softmax runs with
+    // the S^T MFMAs of step st + 1 interleaved (in a fixed, fenced order),
+    // then its PV over all four 16-row pieces.  Pieces past Rc hold zero V
+    // rows (staged so up to rpad) and p = 0, so they add exactly nothing.
     constexpr int n_full = NKB / 4;
-#pragma unroll 1
-    for (int st = 0; st < n_full; ++st)
-      at.template step<2>(k_lane + st * 64 * KP, v_lane + st * 64 * VP, qf, sl2, max(Rc - st * 64, 0), lh);
+    if constexpr (n_full > 0) {
+      f32x16 sc[2][2];
+      at.template qk<2>(sc[0], k_lane, qf);
+#pragma unroll
+      for (int st = 0; st < n_full; ++st) {
+        f32x16 (&cur)[2] = sc[st & 1];
+        f32x16 (&nxt)[2] = sc[(st + 1) & 1];
+        bf16x8 pf[4];
+        at.template prep<2>(cur, sl2, max(Rc - st * 64, 0), lh);
+        if (st + 1 < n_full)
+          at.template exp_qk<2, true, 2>(cur, pf, nxt, k_lane + (st + 1) * 64 * KP, qf, sl2);
+        else
+          at.template exp_qk<2, false>(cur, pf, nxt, nullptr, qf, sl2);
+        at.template pv<2, true>(pf, v_lane + st * 64 * VP);
+      }
+    }
     if constexpr (NKB % 4 == 2) {
       constexpr int kv0 = 64 * n_full;
       if constexpr (ONE_ROW) {
