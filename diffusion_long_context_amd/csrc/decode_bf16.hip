@@ -73,6 +73,17 @@ struct Smem {
   uint64_t kmask[2];                       // the absent mask of the tile in each K buffer
   int flag[WAVES];                         // per wavefront: the split holds an absent row
   int xw[4];                               // words broadcast by thread 0 (in-kernel merge)
+  // The separate-merge epilogue's scalars, written by thread 0 before the
+  // loop: reading them back here after the loop costs an LDS read, where
+  // the argument segment would cost dependent scalar-cache misses.
+  struct Epi {
+    void* o;
+    float* lse;
+    void* part_o;
+    float* part_lse;
+    int64_t part_off, lse_off;
+    int s, g, qt, split, n_splits, l_d, h_q, group;
+  } epi;
 };
 
 // Element offset of attended row v of sequence s for kv head g.  Pool rows
@@ -333,6 +344,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 31, lj = lane >> 5;     // query column, kv / d half
   const int G = a.group;
+  if (!FUSED && tid == 0)
+    sm.epi = typename Smem<D, WAVES>::Epi{a.o, a.lse, a.part_o, a.part_lse, a.seq[si].part_off, a.seq[si].lse_off,
+                                          s, g, qt, split, w0.n_splits, a.l_d, a.h_q, G};
   if constexpr (FUSED)
     if (tid == 0) counter_add(a.sync, 1);       // this workgroup has started
   const int rows_total = a.l_d * G;
@@ -664,24 +678,48 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   }
 
   // ---- epilogue (lanes lc and lc + 32 hold halves of the same query row).
-  // The work item and the lane's row are derived again here from the block
-  // and thread ids (the empty asm hides that they were computed before), so
-  // that none of them stays live in registers across the main loop.
+  // None of the work item's scalars stays live in registers across the main
+  // loop: the separate-merge path reads them back from LDS (sm.epi); the
+  // in-kernel merge derives the work item again from the block id (the empty
+  // asm hides that it was computed before) and reads the kernel arguments
+  // again from the argument segment, through a pointer the compiler cannot
+  // see through.  The lane's row is derived again from the thread id.
   int bid = blockIdx.x;
   asm volatile("" : "+s"(bid));
-  // The kernel arguments are read again from the argument segment, through a
-  // pointer the compiler cannot see through, so that they are loaded here
-  // rather than held in registers across the loop.
   KernArgs<DecodeArgs> ap = kernarg<DecodeArgs>();
   {
   const auto& a = *ap;
-  const WorkItem w = work_item<FUSED>(a, bid);
-  const int si = w.si, s = w.s, g = w.g, qt = w.qt, split = w.split, n_splits = w.n_splits;
+  typename Smem<D, WAVES>::Epi e;
+  int si = 0;
+  if constexpr (!FUSED) {
+    auto rf = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    auto rp = [](auto* p) { return reinterpret_cast<decltype(p)>(uniform_u64(reinterpret_cast<uint64_t>(p))); };
+    e.o = rp(sm.epi.o);
+    e.lse = rp(sm.epi.lse);
+    e.part_o = rp(sm.epi.part_o);
+    e.part_lse = rp(sm.epi.part_lse);
+    e.part_off = (int64_t)uniform_u64((uint64_t)sm.epi.part_off);
+    e.lse_off = (int64_t)uniform_u64((uint64_t)sm.epi.lse_off);
+    e.s = rf(sm.epi.s);
+    e.g = rf(sm.epi.g);
+    e.qt = rf(sm.epi.qt);
+    e.split = rf(sm.epi.split);
+    e.n_splits = rf(sm.epi.n_splits);
+    e.l_d = rf(sm.epi.l_d);
+    e.h_q = rf(sm.epi.h_q);
+    e.group = rf(sm.epi.group);
+  } else {
+    const WorkItem w = work_item<FUSED>(a, bid);
+    si = w.si;
+    e = typename Smem<D, WAVES>::Epi{a.o, a.lse, a.part_o, a.part_lse, 0, 0, w.s, w.g, w.qt, w.split,
+                                     w.n_splits, a.l_d, a.h_q, a.group};
+  }
+  const int s = e.s, g = e.g, qt = e.qt, split = e.split, n_splits = e.n_splits, G = e.group;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lj = (tid & 63) >> 5;
   const int qrow = qt * kRows + (tid >> 6) * 32 + (tid & 31);
-  const int rows_total = a.l_d * G;
+  const int rows_total = e.l_d * G;
   const float l = at.row_sum();
   const float inv = l > 0.f ? 1.f / l : 0.f;     // a split of absent rows only: o = 0, lse = -inf
   const float lse_v = at.lse(l);
@@ -690,18 +728,18 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   const int i = qr / G, h = g * G + (qr - i * G);
   if (n_splits == 1) {
     if (row_ok) {
-      store_o_bf16<DB>(static_cast<uint16_t*>(a.o) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj,
+      store_o_bf16<DB>(static_cast<uint16_t*>(e.o) + (((int64_t)s * e.l_d + i) * e.h_q + h) * D + 8 * lj,
                        at.acc, inv);
-      if (a.lse != nullptr && lj == 0) a.lse[((int64_t)s * a.h_q + h) * a.l_d + i] = lse_v;
+      if (e.lse != nullptr && lj == 0) e.lse[((int64_t)s * e.h_q + h) * e.l_d + i] = lse_v;
     }
   } else if constexpr (!FUSED) {
     if (row_ok) {
-      const int64_t prow = a.seq[si].part_off + (((int64_t)split * a.l_d + i) * a.h_q + h) * D;
+      const int64_t prow = e.part_off + (((int64_t)split * e.l_d + i) * e.h_q + h) * D;
       if constexpr (MERGE == 3)
-        store_o_f32<DB>(static_cast<float*>(a.part_o) + prow, at.acc, inv, lj);
+        store_o_f32<DB>(static_cast<float*>(e.part_o) + prow, at.acc, inv, lj);
       else
-        store_o_bf16<DB>(static_cast<uint16_t*>(a.part_o) + prow + 8 * lj, at.acc, inv);
-      if (lj == 0) a.part_lse[a.seq[si].lse_off + ((int64_t)split * a.l_d + i) * a.h_q + h] = lse_v;
+        store_o_bf16<DB>(static_cast<uint16_t*>(e.part_o) + prow + 8 * lj, at.acc, inv);
+      if (lj == 0) e.part_lse[e.lse_off + ((int64_t)split * e.l_d + i) * e.h_q + h] = lse_v;
     }
   } else {
     // the partial, into this XCD's L2 in the merge's lane-major layout: one
