@@ -43,18 +43,6 @@ constexpr int kSpinLimit = 1 << 14;
 constexpr int kRunAll = 0, kRunIdle = 1, kRunCons = 2, kRunProd = 3;
 constexpr int kProdStages = 3;             // staging sets of the loader wavefronts
 
-template <int N>
-struct IntConst {
-  static constexpr int value = N;
-};
-// f(IntConst<I>{}), ..., f(IntConst<N - 1>{}) in order
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(IntConst<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 // LDS of one workgroup.  The 8-wave variant (one workgroup per CU) uses the
 // V pitch that keeps the transposing reads conflict-free on the 64-bank LDS

@@ -96,7 +96,16 @@ __device__ __forceinline__ bool in_top_k(const float* row, int n, int c, int k) 
   const int lane = threadIdx.x & 63;
   const uint64_t mine = rank_key(row[c], (uint32_t)c);
   int larger = 0;
-  for (int j = lane; j < n; j += 64) larger += rank_key(row[j], (uint32_t)j) > mine ? 1 : 0;
+  // four loads per lane in flight before the comparisons (one memory round
+  // trip per 256 candidates)
+  for (int j0 = lane; j0 < n; j0 += 256) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = j0 + 64 * u < n ? row[j0 + 64 * u] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      larger += j0 + 64 * u < n && rank_key(v[u], (uint32_t)(j0 + 64 * u)) > mine ? 1 : 0;
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) larger += __shfl_xor(larger, off, 64);
   return __builtin_amdgcn_readfirstlane(larger) < k;
@@ -129,6 +138,18 @@ template <bool B>
 struct BoolConst {
   static constexpr bool value = B;
 };
+template <int N>
+struct IntConst {
+  static constexpr int value = N;
+};
+// f(IntConst<I>{}), ..., f(IntConst<N - 1>{}) in order
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntConst<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // A wave-uniform 64-bit value (e.g. read from LDS) moved to scalar registers.
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
