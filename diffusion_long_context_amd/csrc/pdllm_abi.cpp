@@ -302,7 +302,14 @@ pdllm_status pdllm_prefill_select(const pdllm_pool* pool, const int32_t* chunk_s
   if (sel) {
     a.sel_score = chunk_score;
     a.sel_per_seq = n_per_seq;
-    for (int s = 0; s < n_seq; ++s) a.sel_k[s] = k_max > 0 ? k_per_seq[s] : 0;
+    int64_t scored = 0;
+    for (int s = 0; s < n_seq; ++s) {
+      a.sel_k[s] = k_max > 0 ? k_per_seq[s] : 0;
+      scored += a.sel_k[s];
+    }
+    const int64_t n_cu = device_cu_count();
+    a.rank_order = n_per_seq <= pdllm::kPrefillRankChunks && (int64_t)n_chunks * pool->h_kv > n_cu &&
+                   scored * pool->h_kv <= n_cu;
   }
   if ((st = launch_prefill_kernels(a, pool, stream)) != PDLLM_OK) return st;
   pdllm::FinalizeSelectArgs f{};

@@ -122,6 +122,9 @@ int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_part, bool bf16_out, 
 
 // ---------------------------------------------------------------- prefill
 constexpr int kMaxSelSeq = 64;           // sequences whose K_s a prefill launch carries
+// Chunks per sequence up to which the resident prefill kernel can take
+// chunks in score order (ranks counted directly in LDS).
+constexpr int kPrefillRankChunks = 256;
 struct PrefillArgs {
   const void* pool_k;
   const void* pool_v;
@@ -143,6 +146,12 @@ struct PrefillArgs {
   const float* sel_score;   // [n_seq][sel_per_seq] or nullptr (score every chunk)
   int32_t sel_per_seq;
   int32_t sel_k[kMaxSelSeq];
+  // With sel_score: workgroups take chunks in descending score order (the
+  // resident bf16 kernel), so that the scored chunks run first.  Set when
+  // the scored workgroups fit in one round on the device and the launch has
+  // more than one round (then no CU draws two scored chunks), and the
+  // sequences have at most kPrefillRankChunks chunks.
+  int32_t rank_order;
 };
 
 

@@ -42,7 +42,9 @@ struct PSmem {
   uint16_t k[kMaxRows * KP];                // both row-major
   uint16_t v[kMaxRows * VP];
   int next_item;                            // dynamic hand-out of chunk-row items
+  int chunk_pick;                           // the workgroup's chunk, when chosen by rank
 };
+
 
 // NKB = 16-row kv blocks of the chunk padded to 32 rows (compile-time, so
 // every loop over keys is static).  ONE_ROW: the layout has a single row
@@ -57,15 +59,62 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   constexpr int TPR = D / 8;
   static_assert(kThreads % TPR == 0, "loader mapping");
 
-  const int c = blockIdx.x / a.h_kv;
-  const int g = blockIdx.x - c * a.h_kv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // ---- the work item (chunk, kv head).  When only the chunks top-K keeps
+  // are scored and a.rank_order is set, workgroups take chunks in
+  // descending score order --
+  // workgroup (r n_seq + s) h_kv + g takes the chunk of rank r in sequence s
+  // (rank_key order, the order top-K selects by) -- so the scored chunks,
+  // which carry the window work, all run in the first round of workgroups
+  // and no CU draws two of them.  A chunk's work does not depend on which
+  // workgroup runs it.  The ranks are counted in LDS (the K and V areas,
+  // before the staging), with up to four threads per candidate, each over a
+  // share of the keys.
+  const int g = blockIdx.x % a.h_kv;
+  int c = blockIdx.x / a.h_kv;
+  bool scored = true;
+  if (a.sel_score != nullptr) {
+    const int nps = a.sel_per_seq;
+    if (a.rank_order) {
+      const int n_seq = a.n_chunks / nps;
+      const int r = c / n_seq, sq = c - r * n_seq;
+      const float* row = a.sel_score + (int64_t)sq * nps;
+      uint64_t* keys = reinterpret_cast<uint64_t*>(&sm.k[0]);
+      int* cnt = reinterpret_cast<int*>(&sm.v[0]);
+      for (int j = tid; j < nps; j += kThreads) {
+        keys[j] = rank_key(row[j], (uint32_t)j);
+        cnt[j] = 0;
+      }
+      __syncthreads();
+      static_assert(kPrefillRankChunks <= kThreads, "one thread per candidate at least");
+      {
+        const int P = nps <= kThreads / 4 ? 4 : nps <= kThreads / 2 ? 2 : 1;   // threads per candidate
+        const int nj = kThreads / P;
+        const int j = tid % nj, part = tid / nj;
+        if (j < nps) {
+          const uint64_t mine = keys[j];
+          const int lo = part * nps / P, hi = (part + 1) * nps / P;
+          int larger = 0;
+          for (int i = lo; i < hi; ++i) larger += keys[i] > mine ? 1 : 0;
+          atomicAdd(&cnt[j], larger);
+        }
+      }
+      __syncthreads();
+      for (int j = tid; j < nps; j += kThreads)
+        if (cnt[j] == r) sm.chunk_pick = j;
+      __syncthreads();
+      c = sq * nps + sm.chunk_pick;        // (the K / V areas' last reads were before the barrier)
+      scored = r < a.sel_k[sq];
+    } else {
+      scored = chunk_scored(a, c);
+    }
+  }
   const int R = a.slot_rows;               // the layout's rows per chunk
   // rows this chunk holds (a partial last chunk holds fewer): keys and
   // query rows past Rc take no part
   const int Rc = a.chunk_rows != nullptr ? min(max(a.chunk_rows[c], 1), R) : R;
   constexpr int rpad = 16 * NKB;
   const int slot = a.chunk_slot[c];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lj = lane >> 4;  // 16x16 layout (window items)
   const int G = a.group;
   const float sl2 = a.scale_log2;
@@ -88,7 +137,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   bf16x8 qw_cur[2][DC];
   if (n_wb > 0) fetch_w(min(wave, n_wb - 1), qw_cur);
 
-  bool scored = true;
   // ---- stage the chunk's K and V (rows >= Rc are zero); every load is issued
   // before the first LDS store so the staging costs one memory round trip
   {
@@ -113,9 +161,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           kr[ps][i] = vr[ps][i] = u32x4{0, 0, 0, 0};
         }
       }
-    // whether this chunk is scored (its score loads queue behind the
-    // staging loads, which the stores below wait for anyway)
-    scored = chunk_scored(a, c);
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps)
 #pragma unroll
