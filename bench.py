@@ -80,14 +80,14 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "fb5b071925142209",
+        "sources": PREFILL_SOURCES, "sources_sha": "86143e29b048bc1c",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 152452.16, "write_kib": 233318.54},
-                    "finalize_select_kernel": {"fetch_kib": 319.88, "write_kib": 32.56}},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149531.83, "write_kib": 231387.66},
+                    "finalize_select_kernel": {"fetch_kib": 319.83, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "1a9a9f3c7b59c0ee",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7391.25, "write_kib": 16660.16},
+        "sources": DECODE_SOURCES, "sources_sha": "9d16fb6977647c4f",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7391.25, "write_kib": 16663.34},
                     "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8351.50, "write_kib": 1992.00}},
     },
 }
