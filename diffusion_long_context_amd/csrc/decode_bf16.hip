@@ -318,7 +318,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
   constexpr int RPT = kTile * TPR / kThreads;   // kv rows per loader thread
   static_assert(RPT == 1 || RPT == 2 || RPT == 4, "loader mapping");
 
-  // ---- work item: (sequence, kv head, query tile, split)
+  // ---- work item: (sequence, kv head, query tile, split).  The launch
+  // header and the first two sequence plans are read in one batch first.
+  warm_args<0, __builtin_offsetof(DecodeArgs, seq) + 2 * sizeof(DecodeSeq)>(a);
   const WorkItem w0 = work_item<FUSED>(a, blockIdx.x);
   if (!w0.valid) return;                   // padding of a short XCD range
   const int si = w0.si, qt = w0.qt, split = w0.split, g = w0.g, s = w0.s;
@@ -787,30 +789,32 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
   constexpr int EPT = BF16 ? 8 : 4;        // values per thread (16 bytes of partial)
   constexpr int TPR = D / EPT;
   constexpr int RPB = 256 / TPR;
-  const int si = blockIdx.y;
-  if (si >= a.n_seq_launch) return;
+  const int si = blockIdx.y;                // the grid has one row per sequence of the launch
+  // this sequence's plan and the launch header, read in one batch
   const int n_splits = a.seq[si].n_splits;
+  const int64_t part_off = a.seq[si].part_off, lse_off = a.seq[si].lse_off;
+  warm_args<0, __builtin_offsetof(DecodeArgs, seq)>(a);
+  asm volatile("" ::"s"(n_splits), "s"(part_off), "s"(lse_off));
   if (n_splits <= 1) return;
   const int rows = a.l_d * a.h_q;
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int e0 = EPT * (threadIdx.x % TPR);
-  const float* pl = a.part_lse + a.seq[si].lse_off + row;
-  const int64_t po = a.seq[si].part_off + (int64_t)row * D + e0;   // element offset
+  const float* pl = a.part_lse + lse_off + row;
+  const int64_t po = part_off + (int64_t)row * D + e0;   // element offset
   const int64_t sl = rows, so = (int64_t)rows * D;
-  auto load = [&](int j, float (&x)[EPT]) {
-    if constexpr (BF16) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + po + j * so);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
-        x[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
-      }
-    } else {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + po + j * so);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = w[q];
-    }
+  // A split's 16 bytes of partial output are held as loaded and widened to
+  // float32 only where they are summed: widening at the load made the
+  // compiler wait for each load in turn (to keep the wider values' registers
+  // few), one memory round trip per split.
+  auto load = [&](int j) {
+    return *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.part_o) + (po + j * so) * (BF16 ? 2 : 4));
+  };
+  auto value = [&](const u32x4& w, int e) {
+    if constexpr (BF16)
+      return bf16_bits_to_f32(e % 2 ? w[e / 2] >> 16 : w[e / 2] & 0xffffu);
+    else
+      return __uint_as_float(w[e]);
   };
   // Splits are visited in groups of kBatch (4 to 16, fitted at launch to
   // the largest split count) whose lse and partial loads are all in flight
@@ -823,13 +827,18 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
   for (int e = 0; e < EPT; ++e) o[e] = 0.f;
   for (int j0 = 0; j0 < n_splits; j0 += kBatch) {
     float t[kBatch];
-    float x[kBatch][EPT];
+    u32x4 x[kBatch];
+    // every load is unconditional (past the end: a valid split, weight 0 by
+    // the select below), so no branch splits them and the compiler waits
+    // once for the whole group rather than after each lse load
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int j = min(j0 + u, n_splits - 1);   // past the end: a valid split, weight 0
-      t[u] = j0 + u < n_splits ? pl[j * sl] * kLog2e : -INFINITY;
-      load(j, x[u]);
+      const int j = min(j0 + u, n_splits - 1);
+      t[u] = pl[j * sl];
+      x[u] = load(j);
     }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) t[u] = j0 + u < n_splits ? t[u] * kLog2e : -INFINITY;
     float m_new = mx;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) m_new = fmaxf(m_new, t[u]);
@@ -844,7 +853,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const DecodeArgs a) {
       const float w = __builtin_amdgcn_exp2f(t[u] - ref);   // 0 for an empty split and past the end
       tot += w;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) o[e] += w * x[u][e];
+      for (int e = 0; e < EPT; ++e) o[e] += w * value(x[u], e);
     }
     mx = m_new;
   }

@@ -151,6 +151,28 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Kernel arguments reach a wavefront through the scalar cache, and a
+// workgroup's first read of each 64-byte line of them misses it.  Code that
+// branches on one argument before it reads the next pays one miss per step.
+// warm_args reads one dword every 64 bytes of [BEGIN, END) of an argument
+// block, and its last dword (so every line the range overlaps, whatever the
+// block's alignment), all in flight together, and waits for them once: the
+// later reads of those lines hit the cache.
+template <int BEGIN, int END, class T>
+__device__ __forceinline__ void warm_args(const T& a) {
+  static_assert(BEGIN % 4 == 0 && END % 4 == 0 && BEGIN < END && END <= (int)sizeof(T), "argument range");
+  const char* p = reinterpret_cast<const char*>(&a);
+  constexpr int N = (END - BEGIN - 4) / 64 + 2;
+  int v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int o = BEGIN + 64 * i;
+    v[i] = *reinterpret_cast<const int*>(p + (i + 1 < N ? o : END - 4));
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"s"(v[i]));
+}
+
 // A wave-uniform 64-bit value (e.g. read from LDS) moved to scalar registers.
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
