@@ -80,15 +80,15 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "86143e29b048bc1c",
+        "sources": PREFILL_SOURCES, "sources_sha": "47d4eafce2425f95",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149531.83, "write_kib": 231387.66},
-                    "finalize_select_kernel": {"fetch_kib": 319.83, "write_kib": 32.56}},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149494.83, "write_kib": 231355.17},
+                    "finalize_select_kernel": {"fetch_kib": 319.84, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "9d16fb6977647c4f",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7391.25, "write_kib": 16663.34},
-                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8351.50, "write_kib": 1992.00}},
+        "sources": DECODE_SOURCES, "sources_sha": "3113a5ffdc0b0710",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.75, "write_kib": 16662.27},
+                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8350.50, "write_kib": 1992.00}},
     },
 }
 COPY_COUNTERS = {"copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
