@@ -599,6 +599,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
       const int t = t_begin + u;
       if constexpr (COMPUTES) {
         bf16x8 pf[2 * NK];
+        // softmax at raised wave priority, PV at the default (as in the
+        // prefill's chunk items)
+        __builtin_amdgcn_s_setprio(3);
         at.rescale(ms_cur);
         uint64_t am_nxt = 0;
         if (u + 1 < n_loc) {
@@ -611,6 +614,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArg
         // finite data (the last row) and p = 0, so they add exactly zero, and
         // with no branch between the pieces the V reads can run ahead of the
         // MFMAs
+        __builtin_amdgcn_s_setprio(0);
         at.template pv<NK, true>(pf, v_base + (u & 1) * (kTile * VP));
         if (u + 1 < n_loc) ms_nxt = at.template block_max<NK>(nxt, sl2, n_kv - (t + 1) * kTile, lj, 0, am_nxt);
       }

@@ -220,11 +220,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         f32x16 (&cur)[2] = sc[st & 1];
         f32x16 (&nxt)[2] = sc[(st + 1) & 1];
         bf16x8 pf[4];
+        // the softmax (with the next step's S^T MFMAs) at raised wave
+        // priority, the PV MFMAs at the default: a wave in its softmax
+        // issues first, so its VALU work fills the other wave's MFMA time
+        __builtin_amdgcn_s_setprio(3);
         at.template prep<2>(cur, sl2, max(Rc - st * 64, 0), lh);
         if (st + 1 < n_full)
           at.template exp_qk<2, true, 2>(cur, pf, nxt, k_lane + (st + 1) * 64 * KP, qf, sl2);
         else
           at.template exp_qk<2, false>(cur, pf, nxt, nullptr, qf, sl2);
+        __builtin_amdgcn_s_setprio(0);
         at.template pv<2, true>(pf, v_lane + st * 64 * VP);
       }
     }
