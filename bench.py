@@ -82,12 +82,12 @@ COUNTERS = {
     "prefill_select": {
         "sources": PREFILL_SOURCES, "sources_sha": "acb64a2170f68362",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149420.19, "write_kib": 231282.69},
-                    "finalize_select_kernel": {"fetch_kib": 319.81, "write_kib": 32.56}},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149457.88, "write_kib": 231206.84},
+                    "finalize_select_kernel": {"fetch_kib": 319.84, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "d751ee406cd5ecf3",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.50, "write_kib": 16661.55},
+        "sources": DECODE_SOURCES, "sources_sha": "5538770e840f35c4",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.56, "write_kib": 16662.84},
                     "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8350.50, "write_kib": 1992.00}},
     },
 }

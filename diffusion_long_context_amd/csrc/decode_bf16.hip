@@ -303,8 +303,13 @@ __device__ __forceinline__ void merge_group(const A& a, Sm& sm, int tid, int si,
 
 // MERGE: 0 / 3 = partials for the separate merge kernel (bf16 / float32,
 // row-major); 1 / 2 = merged in this launch over float32 / bf16 partials.
+//
+// The 4-wave instance is compiled for two workgroups per CU (at most 256
+// registers per lane; the few values spilled are reloaded outside the tile
+// loop or in its row-table refill): left at one, it
+// took 384 and ran 7-11% slower per call even with one workgroup per CU.
 template <int D, int WAVES, int MERGE>
-__global__ __launch_bounds__(64 * WAVES) void decode_bf16_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void decode_bf16_kernel(const DecodeArgs a) {
   constexpr bool FUSED = MERGE == 1 || MERGE == 2;   // the merge runs in this launch
   constexpr bool PBF16 = MERGE == 2;
   constexpr int kThreads = 64 * WAVES;

@@ -117,11 +117,11 @@ def test_decode_validation(mutate, code, msg):
 
 def test_decode_null_tables_when_no_chunk_is_selected():
     """With every K_s = 0 the index tables are not read, so NULL is accepted
-    (validation passes and stops at the workspace check); with any K_s > 0
-    NULL chunk_slot / sel_chunk is rejected."""
+    (validation passes and stops at the workspace check of a two-split plan);
+    with any K_s > 0 NULL chunk_slot / sel_chunk is rejected."""
     pool = _pool()
     pt, _keep = _pt([0, 0], chunk_slot=None, sel_chunk=None, keep_rows=None)
-    assert _decode(pool, pt, n_seq=2) == WS_SMALL, _err()
+    assert _decode(pool, pt, n_seq=2, splits=2) == WS_SMALL, _err()
     pt, _keep = _pt([0, 3], chunk_slot=None, sel_chunk=None, keep_rows=None)
     assert _decode(pool, pt, n_seq=2) == INVALID and "chunk_slot" in _err()
 

@@ -203,10 +203,11 @@ def test_forced_workgroup_shapes(device, d, rows):
         _compare(host(o), host(lse), ro, rlse, cfg, f"d={d} rows={rows} splits {ns}")
 
 
-def test_planner_picks_small_workgroups_d64(device):
-    """A shape where the planner itself picks 128-row workgroups at d = 64
-    with 14 tiles per split (48/8 heads, L_d = 64, B = 128, K = 32, 4
-    sequences)."""
+def test_planner_plan_d64(device):
+    """The planner's own plan at d = 64 on a multi-sequence shape (48/8
+    heads, L_d = 64, B = 128, K = 32, 4 sequences: 256-row workgroups, 4
+    splits of 17 tiles).  Both workgroup shapes at d = 64, forced, run in
+    test_forced_workgroup_shapes."""
     from diffusion_long_context_amd import _lib as L
     cfg = synth.Config("d64_auto", 48, 8, 64, "bf16", 32, 128, (32, 32, 32, 32), 128, 64, 8, n_seq=4)
     splits, tps, _, rows = L.decode_plan(cfg.k_per_seq, cfg.b, cfg.l_d, cfg.h_q, cfg.h_kv, cfg.d, 1,
