@@ -190,11 +190,12 @@ pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32
   const int rows = opts->q_rows_per_wg;
   if (rows != 0) {
     const bool ok_rows = pool->dtype == PDLLM_BF16
-                             ? rows == pdllm::kDecodeRowsBf16Small || rows == pdllm::kDecodeRowsBf16Large
+                             ? rows == pdllm::kDecodeRowsBf16Small || rows == pdllm::kDecodeRowsBf16Large ||
+                                   rows == pdllm::kDecodeRowsBf16Ws
                              : rows == pdllm::kDecodeRowsF32;
     if (!ok_rows)
       return fail(PDLLM_ERR_UNSUPPORTED, "q_rows_per_wg %d is not a workgroup shape of the %s kernel", rows,
-                  pool->dtype == PDLLM_BF16 ? "bf16 (128, 256)" : "f32 (64)");
+                  pool->dtype == PDLLM_BF16 ? "bf16 (32, 128, 256)" : "f32 (64)");
   }
   if (opts->merge < 0 || opts->merge > 4)
     return fail(PDLLM_ERR_INVALID_ARG, "merge must be 0 .. 4 (got %d)", opts->merge);
@@ -204,6 +205,14 @@ pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32
   if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
                           opts->num_splits, rows, opts->merge, device_cu_count(), plan, &err))
     return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
+  // the 32-row decode keeps pool element offsets / 8 in 32 bits
+  if (plan->ws) {
+    const int64_t extent = (int64_t)(pool->n_slots - 1) * pool->stride_slot +
+                           (int64_t)(pool->slot_rows - 1) * pool->stride_row +
+                           (int64_t)(pool->h_kv - 1) * pool->stride_head + pool->d;
+    if ((extent >> 3) > (int64_t)UINT32_MAX)
+      return fail(PDLLM_ERR_UNSUPPORTED, "32-row decode: the pool spans more than 2^35 elements");
+  }
   // the in-kernel merge addresses its partials with 32-bit byte offsets
   if (plan->fused && plan->part_floats * plan->part_elem_bytes > (int64_t)INT32_MAX)
     return fail(PDLLM_ERR_UNSUPPORTED, "in-kernel merge: %lld bytes of partials exceed 2 GiB (use merge = 1)",
@@ -627,6 +636,7 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
     }
     a.n_groups = n_here * pool->h_kv * plan.q_tiles;
     int64_t grid = wg;
+    if (plan.ws) grid = (wg + pdllm::kXcdGroups - 1) / pdllm::kXcdGroups * pdllm::kXcdGroups;
     if (plan.fused) {             // every split of a merge group on one XCD
       std::vector<int> sizes;
       sizes.reserve(a.n_groups);
@@ -642,8 +652,9 @@ pdllm_status pdllm_split_attn_decode_ex(const pdllm_pool* pool, const pdllm_page
   }
   for (size_t i = 0; i < launches.size(); ++i) {
     const pdllm::DecodeArgs& la = launches[i];
-    const int e = pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(la, pool->d, plan.q_rows_per_wg, stream)
-                                             : pdllm::launch_decode_f32(la, pool->d, stream);
+    const int e = plan.ws                     ? pdllm::launch_decode_ws(la, pool->d, stream)
+                  : pool->dtype == PDLLM_BF16 ? pdllm::launch_decode_bf16(la, pool->d, plan.q_rows_per_wg, stream)
+                                              : pdllm::launch_decode_f32(la, pool->d, stream);
     if ((st = hip_status(e, "decode launch")) != PDLLM_OK) return st;
     if (merges[i] && !plan.fused) {
       const bool bf16 = pool->dtype == PDLLM_BF16;

@@ -16,6 +16,11 @@ constexpr int kDecodeTile = 64;
 // kernel runs 4 or 8 wavefronts of 32 rows, the planner picks per call
 constexpr int kDecodeRowsBf16Small = 128;
 constexpr int kDecodeRowsBf16Large = 256;
+// bf16 decode without kv splits (decode_ws.hip): 32 query rows per
+// workgroup, every kv row of the sequence, pool rows through an LDS row table
+// of at most kWsMaxPoolRows entries.
+constexpr int kDecodeRowsBf16Ws = 32;
+constexpr int kWsMaxPoolRows = 4864;
 constexpr int kDecodeRowsF32 = 64;
 // sequences whose per-sequence plan travels in one launch's arguments (the
 // argument block is then about 2.7 KB); a batch of small-window decodes
@@ -37,6 +42,7 @@ struct DecodePlan {
   bool fused = false;
   bool fused_bf16 = false;                  // in-kernel merge over bf16 (else float32) partials
   bool sep_f32 = false;                     // bf16 inputs, separate merge kernel over float32 partials
+  bool ws = false;                          // bf16 decode without splits (decode_ws.hip)
   int64_t sync_words = 0;
   int64_t sync_bytes = 0;                   // 256-aligned; the partials follow
   int64_t workspace_bytes = 0;
@@ -117,6 +123,7 @@ struct DecodeArgs {
 // Launchers (return a hipError_t value as int).
 int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream);
 int launch_decode_f32(const DecodeArgs& a, int d, void* stream);
+int launch_decode_ws(const DecodeArgs& a, int d, void* stream);
 // bf16_part: the partials are bf16 (else float32); bf16_out: so is o.
 int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_part, bool bf16_out, void* stream);
 

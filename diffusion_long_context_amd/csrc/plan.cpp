@@ -42,6 +42,15 @@ constexpr double kFusedMergePerSplit = 0.05;
 constexpr int kResidentBf16Large = 1;      // 8-wave bf16 workgroups per CU
 constexpr int kResidentBf16Small = 1;      // 4-wave bf16 workgroups per CU (over 256 registers per lane)
 constexpr int kResidentF32 = 4;
+// Measured on MI355X (fits over graph-replayed decode calls at the 8K, 32K
+// and full-step shapes), in microseconds: the split decode costs a
+// workgroup's fixed part plus its tiles, then the merge kernel and the
+// partials' round trip; the decode without splits costs its fixed part (row
+// table, first tile, the wavefronts' merge in LDS) plus one step per round of
+// eight 32-row tiles.  They decide between the two designs only.
+constexpr double kSplitWgUs = 3.7, kSplitTileUs = 1.71, kSplitTileSmallUs = 1.43;
+constexpr double kSplitMergeUs = 6.6, kSplitMergePerSplitUs = 1.0;
+constexpr double kWsFixedUs = 10.5, kWsRoundUs = 1.8;
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
@@ -122,6 +131,47 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
     max_tiles = std::max(max_tiles, p.n_tiles[s]);
   }
   auto splits_for = [&](int s, int tps) { return (p.n_tiles[s] + tps - 1) / tps; };
+  bool ws_fits = dtype == 1;
+  for (int s = 0; s < n_seq; ++s) ws_fits = ws_fits && (int64_t)p.k_s[s] * (b + 1) <= kWsMaxPoolRows;
+  // the decode without splits, costed like the split plan below (per launch
+  // of kMaxSeqPerLaunch sequences, rounds of one workgroup per CU)
+  auto ws_cost_us = [&]() {
+    const int64_t q_blocks = (q_rows + kDecodeRowsBf16Ws - 1) / kDecodeRowsBf16Ws;
+    double t = 0.0;
+    for (int s0 = 0; s0 < n_seq; s0 += kMaxSeqPerLaunch) {
+      const int s1 = std::min(n_seq, s0 + kMaxSeqPerLaunch);
+      int longest = 1;
+      for (int s = s0; s < s1; ++s) longest = std::max(longest, (p.n_kv[s] + 31) / 32);
+      const double rounds = std::ceil((double)(s1 - s0) * h_kv * q_blocks / n_cu);
+      t += rounds * (kWsFixedUs + kWsRoundUs * ((longest + 7) / 8));
+    }
+    return t;
+  };
+  // the decode without kv splits: one workgroup per (sequence, kv head, 32
+  // query rows) over every kv row, no partials and no workspace
+  auto ws_plan = [&]() {
+    p.ws = true;
+    p.q_rows_per_wg = kDecodeRowsBf16Ws;
+    p.q_tiles = (int)((q_rows + kDecodeRowsBf16Ws - 1) / kDecodeRowsBf16Ws);
+    p.splits.assign(n_seq, 1);
+    p.tiles_per_split = p.n_tiles;
+    p.part_off.assign(n_seq, 0);
+    p.lse_off.assign(n_seq, 0);
+    p.total_workgroups = (int64_t)n_seq * h_kv * p.q_tiles;
+    *plan = std::move(p);
+    return true;
+  };
+  if (force_rows == kDecodeRowsBf16Ws) {
+    if (dtype != 1 || num_splits > 1 || (merge != 0 && merge != 1)) {
+      *err = "plan: the 32-row decode is bf16 only, without splits or a merge option";
+      return false;
+    }
+    if (!ws_fits) {
+      *err = "plan: the 32-row decode holds at most 4864 pool rows per sequence";
+      return false;
+    }
+    return ws_plan();
+  }
 
   // (query rows per workgroup, workgroups resident per CU) candidates
   struct Shape { int rows, resident; };
@@ -194,6 +244,26 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
     for (int s = 0; s < n_seq; ++s) {
       p.tiles_per_split[s] = best_tps;
       p.splits[s] = splits_for(s, best_tps);
+    }
+    // the chosen split plan in microseconds, against the decode without
+    // splits (bf16, default merge, nothing forced)
+    if (ws_fits && force_rows == 0 && merge == kDefaultBf16Merge) {
+      const int64_t q_tiles = (q_rows + best_rows - 1) / best_rows;
+      const double tile_us = best_rows == kDecodeRowsBf16Large ? kSplitTileUs : kSplitTileSmallUs;
+      double split_us = 0.0;
+      for (int s0 = 0; s0 < n_seq; s0 += kMaxSeqPerLaunch) {
+        const int s1 = std::min(n_seq, s0 + kMaxSeqPerLaunch);
+        int64_t n_wg = 0;
+        int max_splits = 1, longest = 1;
+        for (int s = s0; s < s1; ++s) {
+          max_splits = std::max(max_splits, p.splits[s]);
+          longest = std::max(longest, std::min(best_tps, p.n_tiles[s]));
+          n_wg += (int64_t)h_kv * q_tiles * p.splits[s];
+        }
+        split_us += std::ceil((double)n_wg / n_cu) * (kSplitWgUs + tile_us * longest);
+        if (max_splits > 1) split_us += kSplitMergeUs + kSplitMergePerSplitUs * max_splits;
+      }
+      if (ws_cost_us() < split_us) return ws_plan();
     }
   }
   p.q_tiles = (int)((q_rows + p.q_rows_per_wg - 1) / p.q_rows_per_wg);

@@ -324,7 +324,11 @@ pdllm_status pdllm_chunk_score(const void* logits, int32_t dtype, int64_t row_st
  * split is a run of consecutive tiles.  num_splits = 0 lets the planner pick
  * the split count from the work and n_cu (the device's compute units);
  * num_splits > 0 forces that many splits per sequence (capped at the
- * sequence's tile count).
+ * sequence's tile count).  For bf16 with num_splits = 0 the planner may
+ * choose the decode without kv splits (q_rows_per_wg = 32: one workgroup per
+ * 32 query rows over every kv row of the sequence, no partials, no
+ * workspace) when a cost model measured on MI355X rates it faster, which
+ * happens when each sequence attends few kv rows.
  *   splits_per_seq  host [n_seq] out   tiles_per_split host [n_seq] out
  *   q_rows_per_wg   host out: query rows (token x grouped head) per workgroup
  *   workspace_bytes host out: the workspace the call needs
@@ -388,8 +392,13 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
  *   q_rows_per_wg  0 = planner; otherwise the query rows (token x grouped
  *                  head) of one workgroup, a shape of the dtype's kernel:
  *                  128 or 256 for bf16, 64 for f32 (PDLLM_ERR_UNSUPPORTED
- *                  for any other).  The result does not depend on it beyond
- *                  rounding; tests use it to run every kernel instance.
+ *                  for any other).  32 (bf16) selects the decode without kv
+ *                  splits: num_splits must be 0 or 1 and merge 0 or 1, and
+ *                  each sequence may attend at most 4864 pool rows
+ *                  (K_s (b + 1)); otherwise PDLLM_ERR_INVALID_ARG.  It needs
+ *                  no workspace.  The result does not depend on the shape
+ *                  beyond rounding; tests use it to run every kernel
+ *                  instance.
  *   merge          how the splits are merged: 0 = the library's choice
  *                  (1); 1 = a second kernel launch over partials stored in
  *                  the pool dtype; 2 / 3 = inside the decode launch, over

@@ -351,3 +351,24 @@ def test_prefill_select_validation():
     assert f(*args(so=2)) == INVALID and "selected_only" in _err()
     assert f(*args(so=1, cs=None, k_max=0)) == INVALID and "chunk_score" in _err()
     assert f(*args(n=0, n_seq=1, k_max=0)) == OK        # nothing to do, nothing enqueued
+
+
+def test_decode_no_split_shape_validation():
+    """q_rows_per_wg = 32 (the decode without kv splits) needs no workspace,
+    takes bf16 only, no split count above 1, no merge option other than the
+    default, and at most 4864 pool rows per sequence."""
+    pool = _pool()
+    pt, _keep = _pt([16])
+    ws = lambda opts, p=pool, t=pt: L.lib.pdllm_split_attn_decode_ex_workspace(
+        ctypes.byref(p), ctypes.byref(t), 1, 256, 28, ctypes.byref(opts))
+    assert ws(L.DecodeOpts(0, 32)) == 0 and ws(L.DecodeOpts(1, 32)) == 0
+    assert ws(L.DecodeOpts(2, 32)) == 0 and "32-row" in _err()
+    assert ws(L.DecodeOpts(0, 32, 4)) == 0 and "32-row" in _err()
+    assert _decode_ex(_pool(dtype=0), pt, L.DecodeOpts(0, 32)) == UNSUPPORTED
+    big, _keep2 = _pt([20], b=255, k_max=20)              # 20 x 256 pool rows > 4864
+    assert ws(L.DecodeOpts(0, 32), t=big) == 0 and "4864" in _err()
+    # a plan with no workspace validates up to the launch; this one stops at
+    # the NULL output check
+    assert L.lib.pdllm_split_attn_decode_ex(ctypes.byref(pool), ctypes.byref(pt), 0x60000, 0x70000, 0x80000, 1,
+                                            256, 28, 0.088, ctypes.byref(L.DecodeOpts(0, 32)), None, None, None,
+                                            0, None) == INVALID

@@ -1,6 +1,7 @@
 """The decode entry point that allocates nothing
 (pdllm_split_attn_decode_noalloc), through the C ABI on the GPU: two calls
-in a row -- the 8K-prefix workload, then a smaller one -- each give the same
+in a row -- the 8K-prefix workload, then a smaller one, both with split
+partials, then the 8K workload's own plan without splits -- each give the same
 output and lse as pdllm_split_attn_decode with a caller workspace (bit for
 bit: the same kernels and plan) and agree with the fp64 oracle."""
 import ctypes
@@ -34,14 +35,18 @@ def _noalloc(inp, sel, keep, cfg, num_splits=0):
 
 def test_noalloc_two_calls_match_workspace_call(device):
     import torch
-    cases = [(synth.config("s8"), 1, 0),
-             (synth.Config("small", 14, 2, 128, "bf16", 6, 40, (4,), 17, 33, 8), 2, 3)]
-    for cfg, seed, ns in cases:
+    # split partials in the scratch array (the 8K workload, 9 forced splits,
+    # then a smaller case), then the planner's plan for the 8K workload, the
+    # decode without splits, which uses no scratch
+    cases = [(synth.config("s8"), 1, 9, True),
+             (synth.Config("small", 14, 2, 128, "bf16", 6, 40, (4,), 17, 33, 8), 2, 3, True),
+             (synth.config("s8"), 1, 0, False)]
+    for cfg, seed, ns, partials in cases:
         inp = synth.generate(cfg, seed)
         sel, keep = synth.random_page_table(cfg, seed)
         say(f"no-allocation decode: {cfg.name}, num_splits={ns}")
         o, lse, o_ref, lse_ref, ws_bytes = _noalloc(inp, sel, keep, cfg, ns)
-        assert ws_bytes > 256, "the case must use split partials"
+        assert (ws_bytes > 256) == partials, "the case must (not) use split partials"
         assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), f"{cfg.name}: differs from the workspace call"
         ro, rlse = oracle.split_attn_decode(inp.pool_k, inp.pool_v, inp.chunk_slot, sel, keep, cfg.k_per_seq,
                                             inp.q, inp.k_resp, inp.v_resp, cfg.scale)
