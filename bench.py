@@ -80,13 +80,13 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "acb64a2170f68362",
+        "sources": PREFILL_SOURCES, "sources_sha": "8b98780355f61afc",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149457.88, "write_kib": 231206.84},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149433.45, "write_kib": 231236.26},
                     "finalize_select_kernel": {"fetch_kib": 319.84, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "5538770e840f35c4",
+        "sources": DECODE_SOURCES, "sources_sha": "df9781f5355994d5",
         "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.56, "write_kib": 16662.84},
                     "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8350.50, "write_kib": 1992.00}},
     },
@@ -133,6 +133,11 @@ def parse():
     p.add_argument("--decode-sweep", action="store_true",
                    help="diagnostic: decode calls at the 32K prefix over K in {4, 8, 16, 32} and "
                         "L_d in {16, 32, 256}, warm and with the caches flushed, median / p10 / p90")
+    p.add_argument("--decode-config", default="", choices=("", "s8", "f32", "s32", "s128"),
+                   help="diagnostic: time only decode calls of this configuration (seeded page table), "
+                        "with the planner's plan (or --rows), eager launches between HIP events")
+    p.add_argument("--rows", type=int, default=0,
+                   help="with --decode-config: force the workgroup shape (pdllm_decode_opts.q_rows_per_wg)")
     p.add_argument("--chunk", type=int, default=0,
                    help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
                         "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
@@ -410,6 +415,46 @@ def full_step_run(args):
             "us_per_layer": t * 1e6 / cfg.layers, "tflops": step_flops / t / 1e12,
             "mfma_frac": step_flops / t / 1e12 / BF16_PEAK_TFLOPS, "target_us_per_step": 190.7,
             "us_per_run": t * 1e6 * cfg.steps, "algorithmic_flops_per_step": step_flops}
+
+
+def decode_config_run(args):
+    """Decode calls of one configuration alone (diagnostic): the seeded inputs
+    and page table of the config, the planner's plan unless --rows forces the
+    workgroup shape; --warmup untimed calls, then --steps calls between HIP
+    events on the launch stream."""
+    import torch
+    import synth
+    from diffusion_long_context_amd import _lib as L
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.decode_config)
+    inp = synth.generate(cfg, args.seed)
+    sel_h, keep_h = synth.random_page_table(cfg, args.seed)
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    call = L.Decode(to_dev(inp.pool_k), to_dev(inp.pool_v), to_dev(inp.chunk_slot), to_dev(sel_h), to_dev(keep_h),
+                    cfg.k_per_seq, to_dev(inp.q), to_dev(inp.k_resp), to_dev(inp.v_resp), cfg.scale,
+                    q_rows_per_wg=args.rows)
+    splits, tps, ws, rows = L.decode_plan(cfg.k_per_seq, cfg.b, cfg.l_d, cfg.h_q, cfg.h_kv, cfg.d, 1,
+                                          with_rows=True) if not args.rows else (None, None, None, args.rows)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    flops = 4.0 * cfg.l_d * cfg.h_q * cfg.d * sum(k * (cfg.b + 1) + cfg.l_d for k in cfg.k_per_seq)
+    print(json.dumps({"diagnostic": f"decode calls alone, config {cfg.name}, eager launches",
+                      "q_rows_per_wg": rows, "splits": splits, "tiles_per_split": tps, "us_per_call": us,
+                      "tflops": flops / us / 1e6, "frac_of_bf16_peak": flops / us / 1e6 / BF16_PEAK_TFLOPS}),
+          flush=True)
 
 
 def timed_us(fn, reps, warmup=2):
@@ -826,6 +871,9 @@ def main():
         return
     if args.gather_batch:
         gather_batch(args)
+        return
+    if args.decode_config:
+        decode_config_run(args)
         return
     import synth
     from diffusion_long_context_amd import _lib as L
