@@ -372,3 +372,24 @@ def test_decode_no_split_shape_validation():
     assert L.lib.pdllm_split_attn_decode_ex(ctypes.byref(pool), ctypes.byref(pt), 0x60000, 0x70000, 0x80000, 1,
                                             256, 28, 0.088, ctypes.byref(L.DecodeOpts(0, 32)), None, None, None,
                                             0, None) == INVALID
+
+
+def test_planner_takes_the_no_split_decode_where_it_measured_faster():
+    """The planner's choice between the split decode and the decode without
+    splits (q_rows_per_wg = 32) on the workloads it was measured on: the 8K
+    workload (1,288 attended rows) takes no splits; the 32K and full-step
+    layers, the 128K batch and small windows (few query rows) keep splits;
+    f32 and a forced split count never take it."""
+    import synth
+    for name, rows in (("s8", 32), ("s32", 256), ("f32", 256), ("s128", 256)):
+        c = synth.config(name)
+        splits, tps, ws, got = L.decode_plan(c.k_per_seq, c.b, c.l_d, c.h_q, c.h_kv, c.d, 1, with_rows=True)
+        assert got == rows, f"{name}: planner chose {got}-row workgroups"
+        if rows == 32:
+            assert ws == 0 and splits == [1] * len(c.k_per_seq)
+    for l_d in (16, 32):
+        c = synth.config("s32", l_d=l_d)
+        assert L.decode_plan(c.k_per_seq, c.b, c.l_d, c.h_q, c.h_kv, c.d, 1, with_rows=True)[3] == 256
+    c = synth.config("s8")
+    assert L.decode_plan(c.k_per_seq, c.b, c.l_d, c.h_q, c.h_kv, c.d, 1, num_splits=3, with_rows=True)[3] == 256
+    assert L.decode_plan(c.k_per_seq, c.b, c.l_d, c.h_q, c.h_kv, c.d, 0, with_rows=True)[3] == 64
