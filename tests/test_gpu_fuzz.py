@@ -1,6 +1,7 @@
 """Seeded random shapes through the whole path, GPU against the fp64 oracle:
 chunk prefill with scoring, top-B over the GPU's own key scores, top-K, and
-the split decode (the planner's split count and a random forced one).  Each
+the decode (the planner's plan, a random forced split count, and the decode
+without splits).  Each
 case draws its sizes from its own seed: GQA group, head count, d, dtype,
 chunk size (some past the 288 rows held on chip, so the streamed path runs,
 and some multiples of 64, so one row is left past the last 64-row block),
@@ -77,12 +78,17 @@ def test_random_shapes(device, i):
     # split decode over those selections
     rd, rl = oracle.split_attn_decode(inp.pool_k, inp.pool_v, inp.chunk_slot, sel_h, keep_h, cfg.k_per_seq,
                                       inp.q, inp.k_resp, inp.v_resp, cfg.scale)
-    for ns in (0, forced):
+    # the planner's plan, a forced split count, and (bf16, pool rows within
+    # its table) the decode without splits
+    runs = [(0, 0), (forced, 0)]
+    if cfg.dtype == "bf16" and max(cfg.k_per_seq) * (cfg.b + 1) <= 4864:
+        runs.append((0, 32))
+    for ns, qrows in runs:
         od, ld = L.split_attn_decode(dev(inp.pool_k), dev(inp.pool_v), dev(inp.chunk_slot), sel, keep,
                                      cfg.k_per_seq, dev(inp.q), dev(inp.k_resp), dev(inp.v_resp), cfg.scale,
-                                     num_splits=ns)
+                                     num_splits=ns, q_rows_per_wg=qrows)
         torch.cuda.synchronize()
-        assert_close(host(od), rd, cfg.dtype, f"fuzz {i} decode splits {ns}")
+        assert_close(host(od), rd, cfg.dtype, f"fuzz {i} decode splits {ns} rows {qrows}")
         m = max_abs(host(ld), rl)
-        assert m <= TOL[cfg.dtype]["lse"], f"fuzz {i} splits {ns}: lse {m:.2e}"
+        assert m <= TOL[cfg.dtype]["lse"], f"fuzz {i} splits {ns} rows {qrows}: lse {m:.2e}"
     say(f"  fuzz {i} ok")
