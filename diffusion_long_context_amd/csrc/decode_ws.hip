@@ -28,6 +28,8 @@
 //   O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 (attn_tile.h).
 // * The pool rows' addresses come from a row table built once per workgroup
 //   in LDS (element offsets / 8, and per-tile masks of absent kept rows).
+//   Loads take a scalar base and a 32-bit byte offset, so the pool and the
+//   response rows must each span under 4 GiB (the library checks).
 // * At the end the 8 online-softmax states are merged in LDS: reference max
 //   M = max_w m_w, O = sum_w 2^(m_w - M) O_w, l = sum_w 2^(m_w - M) l_w.
 #include "attn_tile.h"
@@ -148,42 +150,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws_kernel(const DecodeArgs
   u32x4 ks[NU], vs[NU];
   auto issue = [&](int tt) {
     const int v0 = kT * tt;
-    const uint16_t* kp[NU];
-    const uint16_t* vp[NU];
+    // K and V of a row sit at the same offset from their bases: when a whole
+    // tile comes from one source, each row costs one 32-bit byte offset from
+    // a scalar base (the pool and the response rows each span under 4 GiB)
+    auto load2 = [&](const uint16_t* kb, const uint16_t* vb, uint32_t off_bytes, int u) __attribute__((always_inline)) {
+      ks[u] = *(const __attribute__((address_space(1))) u32x4*)(reinterpret_cast<const char*>(kb) + off_bytes);
+      vs[u] = *(const __attribute__((address_space(1))) u32x4*)(reinterpret_cast<const char*>(vb) + off_bytes);
+    };
     if (v0 + kT <= n_pool) {                 // pool rows only: the row table
-      const int32_t* e = &sm.rows[v0 + lrow * NU];
+      const uint32_t* e = reinterpret_cast<const uint32_t*>(&sm.rows[v0 + lrow * NU]);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int64_t off = ((int64_t)(uint32_t)e[u] << 3) + lch;
-        kp[u] = pk + off;
-        vp[u] = pv + off;
-      }
+      for (int u = 0; u < NU; ++u) load2(pk, pv, (e[u] << 4) + 2u * (uint32_t)lch, u);
     } else if (v0 >= n_pool && v0 + kT <= n_kv) {   // response rows only
+      const uint32_t off0 = (uint32_t)(2 * (resp0 + (int64_t)(v0 + lrow) * resp_row));
+      const uint32_t step = (uint32_t)(2 * RPI * resp_row);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int64_t off = resp0 + (int64_t)(v0 + RPI * u + lrow) * resp_row;
-        kp[u] = rk + off;
-        vp[u] = rv + off;
-      }
+      for (int u = 0; u < NU; ++u) load2(rk, rv, off0 + (uint32_t)u * step, u);
     } else {                                  // mixed, or past the last row (clamped to it)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int v = min(v0 + RPI * u + lrow, n_kv - 1);
-        if (v < n_pool) {
-          const int64_t off = ((int64_t)(uint32_t)sm.rows[row_pos<D>(v)] << 3) + lch;
-          kp[u] = pk + off;
-          vp[u] = pv + off;
-        } else {
-          const int64_t off = resp0 + (int64_t)v * resp_row;
-          kp[u] = rk + off;
-          vp[u] = rv + off;
-        }
+        const bool pool = v < n_pool;
+        const uint32_t off = pool ? (((uint32_t)sm.rows[row_pos<D>(v)]) << 4) + 2u * (uint32_t)lch
+                                  : (uint32_t)(2 * (resp0 + (int64_t)v * resp_row));
+        load2(pool ? pk : rk, pool ? pv : rv, off, u);
       }
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      ks[u] = *(const __attribute__((address_space(1))) u32x4*)(kp[u]);
-      vs[u] = *(const __attribute__((address_space(1))) u32x4*)(vp[u]);
     }
   };
 

@@ -179,6 +179,16 @@ pdllm_status check_decode_io(float scale, const void* q, const void* k_resp, con
   return PDLLM_OK;
 }
 
+// Whether the decode without splits can address the pool and the response
+// rows with 32-bit byte offsets (bf16).
+bool ws_addressable(const pdllm_pool* pool, int32_t n_seq, int32_t l_d) {
+  const int64_t pool_elems = (int64_t)(pool->n_slots - 1) * pool->stride_slot +
+                             (int64_t)(pool->slot_rows - 1) * pool->stride_row +
+                             (int64_t)(pool->h_kv - 1) * pool->stride_head + pool->d;
+  const int64_t resp_elems = (int64_t)n_seq * l_d * pool->h_kv * pool->d;
+  return 2 * pool_elems <= (int64_t)UINT32_MAX && 2 * resp_elems <= (int64_t)UINT32_MAX;
+}
+
 // Validation of a decode call's shapes and options, then its split plan.
 pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq, int32_t l_d,
                        int32_t h_q, const pdllm_decode_opts* opts, pdllm::DecodePlan* plan) {
@@ -203,16 +213,13 @@ pdllm_status plan_call(const pdllm_pool* pool, const pdllm_page_table* pt, int32
     return fail(PDLLM_ERR_UNSUPPORTED, "the in-kernel merge is implemented for bf16 only");
   const char* err = "";
   if (!pdllm::plan_decode(pt->k_per_seq, n_seq, pt->b, l_d, h_q, pool->h_kv, pool->d, pool->dtype,
-                          opts->num_splits, rows, opts->merge, device_cu_count(), plan, &err))
+                          opts->num_splits, rows, opts->merge, device_cu_count(), plan, &err,
+                          pool->dtype == PDLLM_BF16 && ws_addressable(pool, n_seq, l_d)))
     return fail(PDLLM_ERR_INVALID_ARG, "%s", err);
-  // the 32-row decode keeps pool element offsets / 8 in 32 bits
-  if (plan->ws) {
-    const int64_t extent = (int64_t)(pool->n_slots - 1) * pool->stride_slot +
-                           (int64_t)(pool->slot_rows - 1) * pool->stride_row +
-                           (int64_t)(pool->h_kv - 1) * pool->stride_head + pool->d;
-    if ((extent >> 3) > (int64_t)UINT32_MAX)
-      return fail(PDLLM_ERR_UNSUPPORTED, "32-row decode: the pool spans more than 2^35 elements");
-  }
+  // the 32-row decode addresses the pool and the response rows with 32-bit
+  // byte offsets
+  if (plan->ws && !ws_addressable(pool, n_seq, l_d))
+    return fail(PDLLM_ERR_UNSUPPORTED, "32-row decode: the pool or the response rows span 4 GiB or more");
   // the in-kernel merge addresses its partials with 32-bit byte offsets
   if (plan->fused && plan->part_floats * plan->part_elem_bytes > (int64_t)INT32_MAX)
     return fail(PDLLM_ERR_UNSUPPORTED, "in-kernel merge: %lld bytes of partials exceed 2 GiB (use merge = 1)",

@@ -58,7 +58,7 @@ struct DecodePlan {
 // float32 partials (the same as 1 for float32 inputs).
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
                  int d, int dtype, int num_splits, int force_rows, int merge, int n_cu, DecodePlan* plan,
-                 const char** err);
+                 const char** err, bool ws_allowed = true);
 
 // ---------------------------------------------------------------- scratch
 // Bytes of the library-held device scratch of the no-allocation decode entry

@@ -98,7 +98,7 @@ int64_t xcd_partition(const std::vector<int>& sizes, int32_t* bounds) {
 
 bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, int h_kv,
                  int d, int dtype, int num_splits, int force_rows, int merge, int n_cu, DecodePlan* plan,
-                 const char** err) {
+                 const char** err, bool ws_allowed) {
   if (n_seq < 1 || l_d < 1 || h_q < 1 || h_kv < 1 || d < 1 || b < 0 || num_splits < 0 ||
       n_cu < 1 || h_q % h_kv != 0 || k_per_seq == nullptr || plan == nullptr) {
     *err = "plan: invalid sizes (need n_seq, l_d, h_q, h_kv, d, n_cu >= 1, b >= 0, "
@@ -131,7 +131,7 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
     max_tiles = std::max(max_tiles, p.n_tiles[s]);
   }
   auto splits_for = [&](int s, int tps) { return (p.n_tiles[s] + tps - 1) / tps; };
-  bool ws_fits = dtype == 1;
+  bool ws_fits = dtype == 1 && ws_allowed;
   for (int s = 0; s < n_seq; ++s) ws_fits = ws_fits && (int64_t)p.k_s[s] * (b + 1) <= kWsMaxPoolRows;
   // the decode without splits, costed like the split plan below (per launch
   // of kMaxSeqPerLaunch sequences, rounds of one workgroup per CU)
@@ -167,7 +167,8 @@ bool plan_decode(const int32_t* k_per_seq, int n_seq, int b, int l_d, int h_q, i
       return false;
     }
     if (!ws_fits) {
-      *err = "plan: the 32-row decode holds at most 4864 pool rows per sequence";
+      *err = "plan: the 32-row decode holds at most 4864 pool rows per sequence, and a pool and response "
+             "rows of under 4 GiB each";
       return false;
     }
     return ws_plan();
