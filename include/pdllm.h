@@ -393,9 +393,10 @@ pdllm_status pdllm_split_attn_decode(const pdllm_pool* pool, const pdllm_page_ta
  *                  head) of one workgroup, a shape of the dtype's kernel:
  *                  128 or 256 for bf16, 64 for f32 (PDLLM_ERR_UNSUPPORTED
  *                  for any other).  32 (bf16) selects the decode without kv
- *                  splits: num_splits must be 0 or 1 and merge 0 or 1, and
- *                  each sequence may attend at most 4864 pool rows
- *                  (K_s (b + 1)); otherwise PDLLM_ERR_INVALID_ARG.  It needs
+ *                  splits: num_splits must be 0 or 1 and merge 0 or 1, each
+ *                  sequence may attend at most 4864 pool rows (K_s (b + 1)),
+ *                  and the pool and the response rows must each span under
+ *                  4 GiB; otherwise PDLLM_ERR_INVALID_ARG.  It needs
  *                  no workspace.  The result does not depend on the shape
  *                  beyond rounding; tests use it to run every kernel
  *                  instance.
