@@ -80,14 +80,14 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "8b98780355f61afc",
+        "sources": PREFILL_SOURCES, "sources_sha": "33aafd047319149b",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149433.45, "write_kib": 231236.26},
-                    "finalize_select_kernel": {"fetch_kib": 319.84, "write_kib": 32.56}},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149409.78, "write_kib": 231221.39},
+                    "finalize_select_kernel": {"fetch_kib": 319.81, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "df9781f5355994d5",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.56, "write_kib": 16662.84},
+        "sources": DECODE_SOURCES, "sources_sha": "84467a10f4dda044",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.50, "write_kib": 16662.60},
                     "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8350.50, "write_kib": 1992.00}},
     },
 }
