@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 10
+#define PDLLM_ABI_VERSION 11   /* 11: pdllm_decode_opts.q_rows_per_wg = 32, the decode without kv splits */
 
 typedef enum {
   PDLLM_OK = 0,

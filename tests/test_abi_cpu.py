@@ -46,7 +46,7 @@ def test_calibration_library_exports_its_header():
 
 
 def test_abi_version():
-    assert L.lib.pdllm_abi_version() == 10
+    assert L.lib.pdllm_abi_version() == 11
 
 
 def _pool(**kw):
