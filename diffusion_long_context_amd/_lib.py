@@ -99,7 +99,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-ABI_VERSION = 10
+ABI_VERSION = 11
 if lib.pdllm_abi_version() != ABI_VERSION:
     raise ImportError(f"libpdllm ABI {lib.pdllm_abi_version()} != binding ABI {ABI_VERSION}")
 
