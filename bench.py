@@ -383,8 +383,20 @@ def full_step_run(args):
         q = rnd(cfg.n_seq, cfg.l_d, cfg.h_q, cfg.d)
         k_resp = rnd(cfg.n_seq, cfg.l_d, cfg.h_kv, cfg.d)
         v_resp = rnd(cfg.n_seq, cfg.l_d, cfg.h_kv, cfg.d)
+        # the selection is static over the denoising steps of a prompt: each
+        # layer's attended rows are resolved once (pdllm_resolve_rows), outside
+        # the per-step graph; that cost is timed below and amortised over the
+        # steps in the reported figure
         calls.append(L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp,
-                              cfg.scale, merge=args.decode_merge))
+                              cfg.scale, merge=args.decode_merge, resolve=True))
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for c in calls:
+        c.resolve()
+    r1.record()
+    torch.cuda.synchronize()
+    resolve_us = r0.elapsed_time(r1) * 1e3        # all layers, once per prompt
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
@@ -404,14 +416,17 @@ def full_step_run(args):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / cfg.steps
+    t_graph = e0.elapsed_time(e1) * 1e-3 / cfg.steps
+    t = t_graph + resolve_us * 1e-6 / cfg.steps   # the once-per-prompt resolve, amortised
     flops, _ = workload_counts(cfg)
     step_flops = flops["decode"] * cfg.layers
     del graph, calls
     torch.cuda.empty_cache()
     return {"diagnostic": f"decode side of one denoising step: {cfg.layers} layers x one decode call "
                           f"(32K prefix, K=16, B=128, L_d=256), one HIP graph per step, "
-                          f"{cfg.steps} steps replayed", "us_per_step": t * 1e6,
+                          f"{cfg.steps} steps replayed; each layer's attended rows resolved once per prompt "
+                          f"(pdllm_resolve_rows), that time amortised over the steps", "us_per_step": t * 1e6,
+            "us_per_step_graph": t_graph * 1e6, "resolve_us_all_layers": resolve_us,
             "us_per_layer": t * 1e6 / cfg.layers, "tflops": step_flops / t / 1e12,
             "mfma_frac": step_flops / t / 1e12 / BF16_PEAK_TFLOPS, "target_us_per_step": 190.7,
             "us_per_run": t * 1e6 * cfg.steps, "algorithmic_flops_per_step": step_flops}
@@ -1018,6 +1033,7 @@ def main():
             "kernel": STAGE_KERNELS["decode"], "bound": "mfma", "unit": "TFLOP/s", "achieved": fs["tflops"],
             "peak": BF16_PEAK_TFLOPS, "frac": fs["mfma_frac"], "us_per_step": fs["us_per_step"],
             "us_per_layer": fs["us_per_layer"], "target_us_per_step": fs["target_us_per_step"],
+            "us_per_step_graph": fs["us_per_step_graph"], "resolve_us_all_layers": fs["resolve_us_all_layers"],
             "workload": fs["diagnostic"], "traffic": None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)

@@ -33,7 +33,7 @@ class PageTable(ctypes.Structure):
     _fields_ = [("chunk_slot", ctypes.c_void_p), ("sel_chunk", ctypes.c_void_p),
                 ("keep_rows", ctypes.c_void_p), ("k_per_seq", ctypes.c_void_p),
                 ("n_chunks_per_seq", ctypes.c_int32), ("k_max", ctypes.c_int32),
-                ("b", ctypes.c_int32), ("rows_compacted", ctypes.c_int32)]
+                ("b", ctypes.c_int32), ("rows_compacted", ctypes.c_int32), ("rows", ctypes.c_void_p)]
 
 
 class DecodeOpts(ctypes.Structure):
@@ -46,7 +46,7 @@ EXPORTS = ("pdllm_prefill_score_workspace", "pdllm_chunk_prefill_score", "pdllm_
            "pdllm_split_attn_decode", "pdllm_last_error", "pdllm_abi_version",
            "pdllm_chunk_score_workspace", "pdllm_chunk_score", "pdllm_compact_kept_rows",
            "pdllm_prefill_select", "pdllm_split_attn_decode_ex_workspace", "pdllm_split_attn_decode_ex",
-           "pdllm_split_attn_decode_noalloc", "pdllm_gather_kept_kv")
+           "pdllm_split_attn_decode_noalloc", "pdllm_gather_kept_kv", "pdllm_resolve_rows")
 
 
 def _load() -> ctypes.CDLL:
@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
     lib.pdllm_split_attn_decode.restype = ctypes.c_int
     lib.pdllm_split_attn_decode.argtypes = [P(Pool), P(PageTable), vp, vp, vp, i32, i32, i32, f32,
                                             i32, vp, vp, vp, sz, vp]
+    lib.pdllm_resolve_rows.restype = ctypes.c_int
+    lib.pdllm_resolve_rows.argtypes = [P(Pool), P(PageTable), i32, vp, sz, vp]
     lib.pdllm_split_attn_decode_ex_workspace.restype = sz
     lib.pdllm_split_attn_decode_ex_workspace.argtypes = [P(Pool), P(PageTable), i32, i32, i32, P(DecodeOpts)]
     lib.pdllm_split_attn_decode_ex.restype = ctypes.c_int
@@ -371,12 +373,15 @@ class Decode:
     whose kept rows are rows 1..b, pass ``compacted=True`` with ``keep_rows``
     (read only for its -1 entries) or with keep_rows=None and ``b``.
     ``q_rows_per_wg`` forces the workgroup shape and ``merge`` the merge
-    (pdllm_decode_opts; 0 = the library's choice).  The workspace is
+    (pdllm_decode_opts; 0 = the library's choice).  With ``resolve`` the
+    attended pool rows are resolved once here (pdllm_resolve_rows, into
+    ``self.rows``) and every call reads them instead of the index tables;
+    call ``resolve()`` again after the tables change.  The workspace is
     zero-filled once, as the in-kernel merge requires."""
 
     def __init__(self, pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
                  v_resp, scale, num_splits=0, want_lse=True, out=None, b=None, compacted=False,
-                 q_rows_per_wg=0, merge=0):
+                 q_rows_per_wg=0, merge=0, resolve=False):
         self.pool = make_pool(pool_k, pool_v)
         compacted = compacted or keep_rows is None
         no_table = keep_rows is None
@@ -413,6 +418,19 @@ class Decode:
         need = lib.pdllm_split_attn_decode_ex_workspace(ctypes.byref(self.pool), ctypes.byref(self.pt),
                                                         n_seq, l_d, h_q, ctypes.byref(self.opts))
         self.workspace = torch.zeros(max(int(need), 256), dtype=torch.uint8, device=dev)
+        self.rows = None
+        if resolve:
+            self.rows = torch.empty(max(n_seq * self.pt.k_max * (self.pt.b + 1), 1), dtype=torch.int32, device=dev)
+            self.resolve()
+
+    def resolve(self, stream: Optional[int] = None):
+        """pdllm_resolve_rows into ``self.rows`` (from the index tables), then
+        point the page table at it."""
+        self.pt.rows = None
+        _check(lib.pdllm_resolve_rows(ctypes.byref(self.pool), ctypes.byref(self.pt), self.n_seq,
+                                      self.rows.data_ptr(), self.rows.numel(),
+                                      _stream(self.device) if stream is None else stream), "pdllm_resolve_rows")
+        self.pt.rows = self.rows.data_ptr()
 
     def __call__(self, stream: Optional[int] = None):
         st = lib.pdllm_split_attn_decode_ex(
@@ -426,9 +444,9 @@ class Decode:
 
 def split_attn_decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp,
                       v_resp, scale, num_splits=0, want_lse=True, b=None, compacted=False, q_rows_per_wg=0,
-                      merge=0):
+                      merge=0, resolve=False):
     """pdllm_split_attn_decode; returns (o [n_seq][L_d][h_q][d], lse [n_seq][h_q][L_d] or None).
     compacted=True (or keep_rows=None with ``b``) decodes over a pool of compacted slots."""
     return Decode(pool_k, pool_v, chunk_slot, sel_chunk, keep_rows, k_per_seq, q, k_resp, v_resp,
                   scale, num_splits, want_lse, b=b, compacted=compacted, q_rows_per_wg=q_rows_per_wg,
-                  merge=merge)()
+                  merge=merge, resolve=resolve)()

@@ -87,6 +87,11 @@ __device__ __forceinline__ int64_t resolve_row(const DecodeArgs& a, int s, int g
                                                int v, bool& absent) {
   const int per = a.b + 1;
   absent = false;
+  if (v < k_s * per && a.rows != nullptr) {   // resolved once (pdllm_resolve_rows)
+    const int e = a.rows[(int64_t)s * a.rows_stride + v];
+    absent = e < 0;
+    return ((int64_t)(uint32_t)(e & 0x7fffffff) << 3) + (int64_t)g * a.ps_head;
+  }
   if (v < k_s * per) {
     const int k = v / per;
     const int r = v - k * per;
@@ -397,6 +402,32 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void decode_bf16_ke
     // a sequence with no selected chunk reads only idx_dummy (valid device
     // memory): its chunk_slot / sel_chunk may be NULL
     const int32_t* dummy = a.idx_dummy;
+    const bool rmode = a.rows != nullptr;      // resolved rows: one load, no index chain
+    const int32_t* rt = rmode ? a.rows + (int64_t)s * a.rows_stride : dummy;
+    if (rmode) {
+      const bool pool = v < k_s * per;
+      const int e_ld = *(gptr32)(pool ? rt + v : dummy);
+      // any absent row among the split's pool rows (one row a thread per
+      // 512 rows of the split)
+      bool any = false;
+      for (int vv = t_begin * kTile + tid; vv < min(t_end * kTile, k_s * per); vv += kThreads)
+        any = any || *(gptr32)(rt + vv) < 0;
+      __builtin_amdgcn_sched_barrier(0);   // the row loads go out before the queries
+      {
+        const int qr = min(qrow, rows_total - 1);
+        const int i = qr / G, h = g * G + (qr - i * G);
+        load_q<DC, 16>(qf, static_cast<const uint16_t*>(a.q) + (((int64_t)s * a.l_d + i) * a.h_q + h) * D + 8 * lj);
+      }
+      const bool absent = pool && e_ld < 0;
+      const int64_t e = pool ? ((int64_t)(uint32_t)(e_ld & 0x7fffffff) << 3) + (int64_t)g * a.ps_head
+                             : (((int64_t)s * a.l_d + (v - k_s * per)) * a.h_kv + g) * D;
+      sm.kptr[tid] = (gptr16)((pool ? pk : rk) + e);
+      sm.vptr[tid] = (gptr16)((pool ? pv : rv) + e);
+      const uint64_t m = __ballot(absent && tid < nrow);
+      if (lane == 0) sm.absent[wave] = m;
+      const uint64_t fw = __ballot(any);
+      if (lane == 0) sm.flag[wave] = fw != 0;
+    } else {
     const int c0 = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kk : dummy);
     const int cx = *(gptr32)(k_s > 0 ? a.sel_chunk + (int64_t)s * a.k_max + kx : dummy);
     const int cg = s * a.n_chunks_per_seq + min(max(c0, 0), a.n_chunks_per_seq - 1);
@@ -430,6 +461,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void decode_bf16_ke
     const bool flag = tbl && k_s > 0 && t_begin * kTile < k_s * per && (klast < 0 || k_hi - k_lo >= kThreads);
     const uint64_t fw = __ballot(flag);
     if (lane == 0) sm.flag[wave] = fw != 0;
+    }
   }
 
   Attn at;

@@ -186,7 +186,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ws_kernel(const DecodeArgs
 
   // ---- the row table of the pool rows (thread tid: rows tid + 512 i); every
   // load of a batch is issued before the first use
-  if (n_pool > 0) {
+  if (n_pool > 0 && a.rows != nullptr) {    // resolved once (pdllm_resolve_rows): one load a row
+    const int32_t* rt = a.rows + (int64_t)s * a.rows_stride;
+    const uint32_t head8 = (uint32_t)(((int64_t)g * a.ps_head) >> 3);
+    int e[kFillPerThread];
+#pragma unroll
+    for (int i = 0; i < kFillPerThread; ++i)
+      e[i] = *(const __attribute__((address_space(1))) int32_t*)(rt + min(tid + kThreads * i, n_pool - 1));
+#pragma unroll
+    for (int i = 0; i < kFillPerThread; ++i) {
+      const int v = tid + kThreads * i;
+      if (v < n_pool) sm.rows[row_pos<D>(v)] = (int32_t)(((uint32_t)e[i] & 0x7fffffffu) + head8);
+      const uint64_t m = __ballot(v < n_pool && e[i] < 0);
+      if (lane == 0) {
+        sm.amask[(v - lane) / kT] = (uint32_t)m;
+        sm.amask[(v - lane) / kT + 1] = (uint32_t)(m >> 32);
+      }
+    }
+  } else if (n_pool > 0) {
     const int32_t* sel = a.sel_chunk + (int64_t)s * a.k_max;
     int vv[kFillPerThread], cg[kFillPerThread], rr[kFillPerThread];
 #pragma unroll

@@ -100,6 +100,13 @@ pdllm_status check_tensor(const void* p, const char* name) {
   return PDLLM_OK;
 }
 
+// Whether resolved rows (element offsets / 8 in 31 bits) can address the pool.
+bool rows_addressable(const pdllm_pool* pool) {
+  const int64_t pool_elems = (int64_t)(pool->n_slots - 1) * pool->stride_slot +
+                             (int64_t)(pool->slot_rows - 1) * pool->stride_row;
+  return (pool_elems >> 3) <= (int64_t)INT32_MAX;
+}
+
 pdllm::DecodeArgs base_decode_args(const pdllm_pool* pool, const pdllm_page_table* pt,
                                    const void* q, const void* k_resp, const void* v_resp,
                                    int l_d, int h_q, float scale, void* o, float* lse) {
@@ -113,6 +120,8 @@ pdllm::DecodeArgs base_decode_args(const pdllm_pool* pool, const pdllm_page_tabl
   a.sel_chunk = pt->sel_chunk;
   a.keep_rows = pt->keep_rows;
   a.idx_dummy = static_cast<const int32_t*>(q);   // any valid device memory of >= 16 bytes
+  a.rows = pt->rows;
+  a.rows_stride = (int64_t)pt->k_max * (pt->b + 1);
   a.q = q;
   a.k_resp = k_resp;
   a.v_resp = v_resp;
@@ -156,14 +165,68 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
       return fail(PDLLM_ERR_INVALID_ARG, "k_per_seq[%d] = %d outside [0, k_max %d]", s, ks, pt->k_max);
     any_chunk |= ks > 0;
   }
-  if (any_chunk) {
+  // resolved rows (pdllm_resolve_rows) replace the index tables
+  if (any_chunk && pt->rows == nullptr) {
     if (pt->chunk_slot == nullptr || pt->sel_chunk == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot / sel_chunk is NULL");
     if (pt->b > 0 && !pt->rows_compacted && pt->keep_rows == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
   }
+  if (pt->rows != nullptr) {
+    if (reinterpret_cast<uintptr_t>(pt->rows) % 4 != 0)
+      return fail(PDLLM_ERR_INVALID_ARG, "rows must be 4-byte aligned");
+    if (!rows_addressable(pool))
+      return fail(PDLLM_ERR_UNSUPPORTED, "resolved rows: the pool spans 2^34 elements or more");
+  }
   return PDLLM_OK;
 }
+
+}  // namespace
+
+pdllm_status pdllm_resolve_rows(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq,
+                                int32_t* rows, size_t rows_elems, void* stream) {
+  pdllm_status st = check_pool(pool);
+  if (st != PDLLM_OK) return st;
+  if (pt == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "page table is NULL");
+  if (n_seq < 1) return fail(PDLLM_ERR_INVALID_ARG, "n_seq must be >= 1 (got %d)", n_seq);
+  if (pt->n_chunks_per_seq < 1) return fail(PDLLM_ERR_INVALID_ARG, "n_chunks_per_seq must be >= 1");
+  if (pt->k_max < 0 || pt->k_max > pt->n_chunks_per_seq)
+    return fail(PDLLM_ERR_INVALID_ARG, "k_max %d outside [0, n_chunks_per_seq %d]", pt->k_max,
+                pt->n_chunks_per_seq);
+  if (pt->b < 0 || pt->b > pool->slot_rows - 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "b %d outside [0, slot_rows - 1 = %d]", pt->b, pool->slot_rows - 1);
+  if (pt->rows_compacted != 0 && pt->rows_compacted != 1)
+    return fail(PDLLM_ERR_INVALID_ARG, "rows_compacted must be 0 or 1 (got %d)", pt->rows_compacted);
+  const int64_t need = (int64_t)n_seq * pt->k_max * (pt->b + 1);
+  if (need > 0) {
+    if (pt->chunk_slot == nullptr || pt->sel_chunk == nullptr)
+      return fail(PDLLM_ERR_INVALID_ARG, "chunk_slot / sel_chunk is NULL");
+    if (pt->b > 0 && !pt->rows_compacted && pt->keep_rows == nullptr)
+      return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
+  }
+  if (rows == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "rows is NULL");
+  if (reinterpret_cast<uintptr_t>(rows) % 4 != 0) return fail(PDLLM_ERR_INVALID_ARG, "rows must be 4-byte aligned");
+  if ((int64_t)rows_elems < need)
+    return fail(PDLLM_ERR_INVALID_ARG, "rows holds %zu entries, %lld needed", rows_elems, (long long)need);
+  if (!rows_addressable(pool))
+    return fail(PDLLM_ERR_UNSUPPORTED, "resolved rows: the pool spans 2^34 elements or more");
+  pdllm::ResolveArgs a{};
+  a.chunk_slot = pt->chunk_slot;
+  a.sel_chunk = pt->sel_chunk;
+  a.keep_rows = pt->keep_rows;
+  a.rows = rows;
+  a.ps_slot = pool->stride_slot;
+  a.ps_row = pool->stride_row;
+  a.n_seq = n_seq;
+  a.n_chunks_per_seq = pt->n_chunks_per_seq;
+  a.k_max = pt->k_max;
+  a.b = pt->b;
+  a.compact = pt->rows_compacted ? 1 : 0;
+  if ((st = hip_status(pdllm::launch_resolve_rows(a, stream), "resolve launch")) != PDLLM_OK) return st;
+  return ok();
+}
+
+namespace {
 
 // Validation of a decode call's scale and tensor pointers.
 pdllm_status check_decode_io(float scale, const void* q, const void* k_resp, const void* v_resp, const void* o,
@@ -460,7 +523,11 @@ pdllm_status pdllm_compact_kept_rows(const pdllm_pool* src, const int32_t* chunk
 pdllm_status pdllm_gather_kept_kv(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq, void* dst_k,
                                   void* dst_v, int64_t dst_stride_slot, int64_t dst_stride_row,
                                   int64_t dst_stride_head, void* stream) {
-  pdllm_status st = check_decode(pool, pt, n_seq, 1, pool != nullptr ? pool->h_kv : 1, 0);
+  if (pt == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "page table is NULL");
+  // the gather reads the index tables themselves (pt->rows is not used)
+  pdllm_page_table tables = *pt;
+  tables.rows = nullptr;
+  pdllm_status st = check_decode(pool, &tables, n_seq, 1, pool != nullptr ? pool->h_kv : 1, 0);
   if (st != PDLLM_OK) return st;
   if (pt->rows_compacted) return fail(PDLLM_ERR_UNSUPPORTED, "gather: the pool must hold whole chunks");
   if (n_seq > pdllm::kMaxGatherSeq)

@@ -96,6 +96,8 @@ struct DecodeArgs {
   const int32_t* sel_chunk;
   const int32_t* keep_rows;
   const int32_t* idx_dummy;  // valid device memory read in place of absent index tables
+  const int32_t* rows;       // nullable: the resolved pool rows (pdllm_resolve_rows), [n_seq][rows_stride]
+  int64_t rows_stride;       // k_max (b + 1)
   const void* q;
   const void* k_resp;
   const void* v_resp;
@@ -124,6 +126,16 @@ struct DecodeArgs {
 int launch_decode_bf16(const DecodeArgs& a, int d, int q_rows_per_wg, void* stream);
 int launch_decode_f32(const DecodeArgs& a, int d, void* stream);
 int launch_decode_ws(const DecodeArgs& a, int d, void* stream);
+// pdllm_resolve_rows (resolve_rows.hip)
+struct ResolveArgs {
+  const int32_t* chunk_slot;
+  const int32_t* sel_chunk;
+  const int32_t* keep_rows;  // nullable (b = 0, or compacted slots without absent rows)
+  int32_t* rows;
+  int64_t ps_slot, ps_row;
+  int32_t n_seq, n_chunks_per_seq, k_max, b, compact;
+};
+int launch_resolve_rows(const ResolveArgs& a, void* stream);
 // bf16_part: the partials are bf16 (else float32); bf16_out: so is o.
 int launch_lse_merge(const DecodeArgs& a, int d, bool bf16_part, bool bf16_out, void* stream);
 

@@ -47,7 +47,9 @@
 extern "C" {
 #endif
 
-#define PDLLM_ABI_VERSION 11   /* 11: pdllm_decode_opts.q_rows_per_wg = 32, the decode without kv splits */
+/* 11: pdllm_decode_opts.q_rows_per_wg = 32 (the decode without kv splits);
+ *     pdllm_page_table.rows and pdllm_resolve_rows */
+#define PDLLM_ABI_VERSION 11
 
 typedef enum {
   PDLLM_OK = 0,
@@ -105,6 +107,13 @@ typedef struct {
  *                      rows are rows 1..b in order -- keep_rows is then read
  *                      only for its absent (-1) entries, and may be NULL when
  *                      there are none
+ *   rows        device [n_seq][k_max (b + 1)] or NULL: the same attended pool
+ *                      rows resolved once by pdllm_resolve_rows for this pool
+ *                      and page table.  The selection is static over the
+ *                      denoising steps of a prompt (Methodology 3), so a
+ *                      caller resolves it once and every decode call reads one
+ *                      entry per row instead of the chunk_slot / sel_chunk /
+ *                      keep_rows chain (which may then be NULL)
  * A selected chunk contributes its BOS row and its b kept rows (less the
  * absent ones), in that order; chunks are visited in sel_chunk order.
  */
@@ -117,6 +126,7 @@ typedef struct {
   int32_t k_max;
   int32_t b;
   int32_t rows_compacted;
+  const int32_t* rows;
 } pdllm_page_table;
 
 /* ------------------------------------------------------------------------ *
@@ -317,6 +327,27 @@ pdllm_status pdllm_chunk_score(const void* logits, int32_t dtype, int64_t row_st
 /* ------------------------------------------------------------------------ *
  * Decode side                                                               *
  * ------------------------------------------------------------------------ */
+
+/*
+ * The attended pool rows of a page table, resolved once (Methodology 2 and
+ * 3: the top-K chunks and their top-B rows stay fixed over the denoising
+ * steps of a prompt).  Entry rows[s * k_max (b + 1) + k (b + 1) + r] is the
+ * element offset / 8 of row r (0 = BOS, then the kept rows) of the k-th
+ * selected chunk of sequence s in the pool -- slot * stride_slot +
+ * row * stride_row, without the kv head's offset -- with bit 31 set for an
+ * absent kept row (which points at the BOS row); entries of chunks k >= K_s
+ * are written from the clamped sel_chunk entries and never read.  Pass the
+ * array as pdllm_page_table.rows to the decode calls over the same pool and
+ * page table.
+ *   pool, pt       as for pdllm_split_attn_decode (pt->rows is ignored)
+ *   rows           device [n_seq][k_max (b + 1)] int32 out, 4-byte aligned;
+ *                  rows_elems its length in elements
+ * Errors: PDLLM_ERR_INVALID_ARG for what pdllm_split_attn_decode rejects in
+ * the pool and page table, a NULL or short rows; PDLLM_ERR_UNSUPPORTED for a
+ * pool of 2^34 elements or more.  Nothing is enqueued on error.
+ */
+pdllm_status pdllm_resolve_rows(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq,
+                                int32_t* rows, size_t rows_elems, void* stream);
 
 /*
  * The split plan of a decode call (host only, deterministic).  The attended

@@ -9,6 +9,7 @@ int g_launches = 0;
 int launch_decode_bf16(const DecodeArgs&, int, int, void*) { return ++g_launches, 0; }
 int launch_decode_f32(const DecodeArgs&, int, void*) { return ++g_launches, 0; }
 int launch_decode_ws(const DecodeArgs&, int, void*) { return ++g_launches, 0; }
+int launch_resolve_rows(const ResolveArgs&, void*) { return ++g_launches, 0; }
 int launch_lse_merge(const DecodeArgs&, int, bool, bool, void*) { return ++g_launches, 0; }
 int launch_prefill_bf16(const PrefillArgs&, int, void*) { return ++g_launches, 0; }
 int launch_prefill_f32(const PrefillArgs&, int, void*) { return ++g_launches, 0; }

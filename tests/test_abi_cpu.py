@@ -393,3 +393,27 @@ def test_planner_takes_the_no_split_decode_where_it_measured_faster():
     c = synth.config("s8")
     assert L.decode_plan(c.k_per_seq, c.b, c.l_d, c.h_q, c.h_kv, c.d, 1, num_splits=3, with_rows=True)[3] == 256
     assert L.decode_plan(c.k_per_seq, c.b, c.l_d, c.h_q, c.h_kv, c.d, 0, with_rows=True)[3] == 64
+
+
+def test_resolve_rows_validation():
+    """pdllm_resolve_rows checks the pool, the page table and the output
+    before anything is enqueued; a decode given resolved rows accepts NULL
+    index tables and rejects a misaligned rows pointer."""
+    f = L.lib.pdllm_resolve_rows
+    pool = _pool()
+    pt, _keep = _pt([16])
+    need = 1 * 16 * 257
+    assert f(ctypes.byref(pool), ctypes.byref(pt), 1, None, need, None) == INVALID and "rows is NULL" in _err()
+    assert f(ctypes.byref(pool), ctypes.byref(pt), 1, 0xA0000, need - 1, None) == INVALID and "needed" in _err()
+    assert f(ctypes.byref(pool), ctypes.byref(pt), 0, 0xA0000, need, None) == INVALID
+    assert f(ctypes.byref(pool), None, 1, 0xA0000, need, None) == INVALID
+    bad, _k = _pt([16], sel_chunk=None)
+    assert f(ctypes.byref(pool), ctypes.byref(bad), 1, 0xA0000, need, None) == INVALID and "sel_chunk" in _err()
+    huge = _pool(n_slots=1 << 20, stride_slot=1 << 20)
+    assert f(ctypes.byref(huge), ctypes.byref(pt), 1, 0xA0000, need, None) == UNSUPPORTED
+    # a decode over resolved rows: NULL tables accepted (validation runs to the workspace check)
+    rpt, _k2 = _pt([16], chunk_slot=None, sel_chunk=None, keep_rows=None)
+    rpt.rows = 0xA0000
+    assert _decode(pool, rpt, splits=2) == WS_SMALL, _err()
+    rpt.rows = 0xA0002
+    assert _decode(pool, rpt, splits=2) == INVALID and "aligned" in _err()
