@@ -80,15 +80,15 @@ STAGE_KERNELS = {
 # profiles/step_32k_prefix_hbm_counters.md.
 COUNTERS = {
     "prefill_select": {
-        "sources": PREFILL_SOURCES, "sources_sha": "33aafd047319149b",
+        "sources": PREFILL_SOURCES, "sources_sha": "939caab1116e6daf",
         # the default step (only the kept chunks scored); other forms get no traffic figure
-        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149409.78, "write_kib": 231221.39},
-                    "finalize_select_kernel": {"fetch_kib": 319.81, "write_kib": 32.56}},
+        "kernels": {"prefill_bf16_kernel<128, 18, true>": {"fetch_kib": 149462.97, "write_kib": 231209.27},
+                    "finalize_select_kernel": {"fetch_kib": 319.83, "write_kib": 32.56}},
     },
     "decode": {
-        "sources": DECODE_SOURCES, "sources_sha": "84467a10f4dda044",
-        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7390.50, "write_kib": 16662.60},
-                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8350.50, "write_kib": 1992.00}},
+        "sources": DECODE_SOURCES, "sources_sha": "368b144dbb70e728",
+        "kernels": {"decode_bf16_kernel<128, 8, 0>": {"fetch_kib": 7395.25, "write_kib": 16664.37},
+                    "lse_merge_kernel<128, true, true, 12>": {"fetch_kib": 8344.50, "write_kib": 1992.00}},
     },
 }
 COPY_COUNTERS = {"copy_fetch_kib": 524301.25,      # __amd_rocclr_copyBuffer of COPY_BYTES
