@@ -18,8 +18,11 @@
 //   which need no index lookup, come first).
 // * A workgroup reads its kv head's rows once; the workgroups of one
 //   (sequence, kv head) sit on one XCD and hit its L2.  At 32 query rows per
-//   workgroup the loop streams about 2 KB of K/V per query row: bound by the
-//   L2-to-CU rate (about 0.1 TB/s per CU), not by the MFMAs.
+//   workgroup every CU streams the whole kv head (about 2 KB of K/V per
+//   query row), at about 70 GB/s per CU: bound by the wavefronts' own
+//   instruction streams (each tile is stored to and read from LDS by one
+//   wavefront), near the CU's load rate for gathered rows (75-94 GB/s),
+//   not by the MFMAs.
 // * Each wavefront gathers its tiles with coalesced 16-byte loads (four
 //   256-byte rows per instruction; the MFMA fragment layout would read 32-byte
 //   pieces of 32 rows per instruction, which a CU streams at a third of the
@@ -27,7 +30,9 @@
 //   LDS tile: no workgroup barrier in the loop.  S^T = K Q^T and
 //   O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 (attn_tile.h).
 // * The pool rows' addresses come from a row table built once per workgroup
-//   in LDS (element offsets / 8, and per-tile masks of absent kept rows).
+//   in LDS (element offsets / 8, and per-tile masks of absent kept rows),
+//   from the index tables or from rows resolved once per prompt
+//   (pdllm_resolve_rows).
 //   Loads take a scalar base and a 32-bit byte offset, so the pool and the
 //   response rows must each span under 4 GiB (the library checks).
 // * At the end the 8 online-softmax states are merged in LDS: reference max
