@@ -173,6 +173,7 @@ pdllm_status check_decode(const pdllm_pool* pool, const pdllm_page_table* pt, in
       return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
   }
   if (pt->rows != nullptr) {
+    if (pool->dtype != PDLLM_BF16) return fail(PDLLM_ERR_UNSUPPORTED, "resolved rows: bf16 pools only");
     if (reinterpret_cast<uintptr_t>(pt->rows) % 4 != 0)
       return fail(PDLLM_ERR_INVALID_ARG, "rows must be 4-byte aligned");
     if (!rows_addressable(pool))
@@ -204,6 +205,7 @@ pdllm_status pdllm_resolve_rows(const pdllm_pool* pool, const pdllm_page_table* 
     if (pt->b > 0 && !pt->rows_compacted && pt->keep_rows == nullptr)
       return fail(PDLLM_ERR_INVALID_ARG, "keep_rows is NULL");
   }
+  if (pool->dtype != PDLLM_BF16) return fail(PDLLM_ERR_UNSUPPORTED, "resolved rows: bf16 pools only");
   if (rows == nullptr) return fail(PDLLM_ERR_INVALID_ARG, "rows is NULL");
   if (reinterpret_cast<uintptr_t>(rows) % 4 != 0) return fail(PDLLM_ERR_INVALID_ARG, "rows must be 4-byte aligned");
   if ((int64_t)rows_elems < need)

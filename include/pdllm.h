@@ -109,7 +109,7 @@ typedef struct {
  *                      there are none
  *   rows        device [n_seq][k_max (b + 1)] or NULL: the same attended pool
  *                      rows resolved once by pdllm_resolve_rows for this pool
- *                      and page table.  The selection is static over the
+ *                      and page table (bf16 pools only).  The selection is static over the
  *                      denoising steps of a prompt (Methodology 3), so a
  *                      caller resolves it once and every decode call reads one
  *                      entry per row instead of the chunk_slot / sel_chunk /
@@ -344,7 +344,9 @@ pdllm_status pdllm_chunk_score(const void* logits, int32_t dtype, int64_t row_st
  *                  rows_elems its length in elements
  * Errors: PDLLM_ERR_INVALID_ARG for what pdllm_split_attn_decode rejects in
  * the pool and page table, a NULL or short rows; PDLLM_ERR_UNSUPPORTED for a
- * pool of 2^34 elements or more.  Nothing is enqueued on error.
+ * float32 pool or a pool of 2^34 elements or more (bf16 strides are
+ * multiples of 8 elements, so offset / 8 is exact).  Nothing is enqueued on
+ * error.
  */
 pdllm_status pdllm_resolve_rows(const pdllm_pool* pool, const pdllm_page_table* pt, int32_t n_seq,
                                 int32_t* rows, size_t rows_elems, void* stream);

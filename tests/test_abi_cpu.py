@@ -409,6 +409,7 @@ def test_resolve_rows_validation():
     assert f(ctypes.byref(pool), None, 1, 0xA0000, need, None) == INVALID
     bad, _k = _pt([16], sel_chunk=None)
     assert f(ctypes.byref(pool), ctypes.byref(bad), 1, 0xA0000, need, None) == INVALID and "sel_chunk" in _err()
+    assert f(ctypes.byref(_pool(dtype=0)), ctypes.byref(pt), 1, 0xA0000, need, None) == UNSUPPORTED
     huge = _pool(n_slots=1 << 20, stride_slot=1 << 20)
     assert f(ctypes.byref(huge), ctypes.byref(pt), 1, 0xA0000, need, None) == UNSUPPORTED
     # a decode over resolved rows: NULL tables accepted (validation runs to the workspace check)
@@ -417,3 +418,5 @@ def test_resolve_rows_validation():
     assert _decode(pool, rpt, splits=2) == WS_SMALL, _err()
     rpt.rows = 0xA0002
     assert _decode(pool, rpt, splits=2) == INVALID and "aligned" in _err()
+    rpt.rows = 0xA0000
+    assert _decode(_pool(dtype=0), rpt, splits=2) == UNSUPPORTED and "bf16" in _err()
