@@ -137,7 +137,8 @@ def parse():
                    help="diagnostic: time only decode calls of this configuration (seeded page table), "
                         "with the planner's plan (or --rows), eager launches between HIP events")
     p.add_argument("--rows", type=int, default=0,
-                   help="with --decode-config: force the workgroup shape (pdllm_decode_opts.q_rows_per_wg)")
+                   help="with --decode-config or --full-step: force the decode's workgroup shape "
+                        "(pdllm_decode_opts.q_rows_per_wg)")
     p.add_argument("--chunk", type=int, default=0,
                    help="diagnostic: time only the prefill side (chunk attention + scoring) of a "
                         "32K prefix cut into chunks of this size (256 .. 4096); not the headline step")
@@ -388,7 +389,8 @@ def full_step_run(args):
         # the per-step graph; that cost is timed below and amortised over the
         # steps in the reported figure
         calls.append(L.Decode(pool_k, pool_v, chunk_slot, sel, keep, cfg.k_per_seq, q, k_resp, v_resp,
-                              cfg.scale, merge=args.decode_merge, resolve=True))
+                              cfg.scale, merge=args.decode_merge, resolve=True,
+                              q_rows_per_wg=args.rows))
     torch.cuda.synchronize()
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     r0.record()
@@ -426,7 +428,7 @@ def full_step_run(args):
                           f"(32K prefix, K=16, B=128, L_d=256), one HIP graph per step, "
                           f"{cfg.steps} steps replayed; each layer's attended rows resolved once per prompt "
                           f"(pdllm_resolve_rows), that time amortised over the steps", "us_per_step": t * 1e6,
-            "us_per_step_graph": t_graph * 1e6, "resolve_us_all_layers": resolve_us,
+            "us_per_step_graph": t_graph * 1e6, "resolve_us_all_layers": resolve_us, "q_rows_per_wg_forced": args.rows or None,
             "us_per_layer": t * 1e6 / cfg.layers, "tflops": step_flops / t / 1e12,
             "mfma_frac": step_flops / t / 1e12 / BF16_PEAK_TFLOPS, "target_us_per_step": 190.7,
             "us_per_run": t * 1e6 * cfg.steps, "algorithmic_flops_per_step": step_flops}
